@@ -1,0 +1,237 @@
+/*
+ * maskattn — masked flash-attention prefill and speculative tree verify over
+ * ragged sequences with paged K/V, for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libmaskattn.so.  Plain pointers and sizes only.  "host" and
+ * "device" below say where a pointer must point.  Streams are hipStream_t
+ * passed as void* (NULL = the default stream).
+ *
+ * Sources of the operations (web pages; sections named, not quoted):
+ *  - sglang-jax pull request 20, "feat: support custom mask for flash
+ *    attention": ragged paged attention with a `causal` flag or a flattened
+ *    custom mask; the reference implementation rejects a custom mask together
+ *    with causal; the custom mask must be at least as large as the sequences
+ *    it covers; a sliding window only makes sense with causal masking
+ *    (review comments).
+ *  - aphrodite-engine issue 1526, "[Attention] feat: support PrefixLM":
+ *    prefixlm_mask_mod, bidirectional inside a per-sequence prefix, causal
+ *    after it (highlights).
+ *  - flashinfer issue 724, "Custom mask slows down attention.": a float mask
+ *    bit-packed before the kernel, the block-sparse alternative, tree
+ *    attention for speculative decoding as a custom mask.
+ *  - MagiAttention issue 316, "Feature request: chunk-causal mask type for
+ *    Flex Flash Attention": (q_range, k_range, attn_type) lists with types
+ *    FULL, CAUSAL, INV_CAUSAL, BI_CAUSAL and the proposed CHUNK_CAUSAL with a
+ *    per-range chunk size ("Proposed API", "Semantically equivalent to").
+ *  - mlxcel pull request 555, "feat: add Gemma2 sliding-window (local/global)
+ *    attention": the window ANDed into the causal mask.
+ *
+ * Semantics shared by every entry point
+ *  - Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and
+ *    keys 0 .. kv_len[b]-1.  Query row t of the sequence sits at key position
+ *    pos(t) = t + kv_len - q_len (the queries are the sequence's last q_len
+ *    tokens).
+ *  - Query head h reads K/V head h / (Hq / Hkv) (contiguous GQA groups).
+ *  - O[t] = sum_j P[t,j] V[j] with P = softmax over the visible keys of
+ *    scale * Q[t].K[j]; a row with no visible key gives O = 0 and
+ *    LSE = -inf.  LSE is the natural-log sum of exp over visible keys of the
+ *    scaled scores.
+ *  - Mask kinds:
+ *      CAUSAL          j <= pos(t)
+ *      SLIDING_WINDOW  pos(t) - window < j <= pos(t)
+ *      PREFIX_LM       j <= pos(t) or j < prefix_len[b]
+ *      RANGES          union of the sequence's range descriptors (below)
+ *      DENSE_BOOL      uint8 per (t, j), nonzero = visible; per sequence a
+ *                      row-major q_len x kv_len block, sequences concatenated
+ *      PACKED_U64      per query row ceil(kv_len/64) uint64 words; key j is
+ *                      bit (j % 64) of word j / 64; rows concatenated over
+ *                      sequences; bits past kv_len are ignored
+ *  - Range descriptors are in per-sequence local coordinates (query rows and
+ *    keys of that sequence).  Inside a range, i = t - q_start,
+ *    jj = j - k_start, Lq = q_end - q_start, Lk = k_end - k_start:
+ *      FULL          every (i, jj)
+ *      CAUSAL        jj <= i + Lk - Lq            (bottom-right aligned)
+ *      INV_CAUSAL    jj >= i
+ *      BI_CAUSAL     i <= jj <= i + Lk - Lq
+ *      CHUNK_CAUSAL  jj < Lk - (Lq - min(Lq, (i / cs + 1) * cs)), cs = chunk_size
+ *
+ * Errors: every function returns a status; nothing else crosses the ABI.
+ * Arguments are validated on the host before any HIP call.  ma_last_error()
+ * returns a thread-local message describing the last failure.
+ */
+#ifndef MASKATTN_H
+#define MASKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MA_OK = 0,
+  MA_ERR_INVALID = -1,       /* a bad argument (null pointer, bad size, range outside the sequence) */
+  MA_ERR_CONFLICT = -2,      /* arguments that cannot be used together */
+  MA_ERR_SIZE = -3,          /* a mask buffer smaller than its sequences need, or a short workspace */
+  MA_ERR_UNSUPPORTED = -4,   /* a head_dim, dtype, tile shape or page size with no kernel */
+  MA_ERR_PLAN_MISMATCH = -5, /* plan built for other lengths / tile shape than the call */
+  MA_ERR_HIP = -6,           /* a HIP runtime call failed (message has the HIP error) */
+  MA_ERR_NOMEM = -7          /* host or device allocation failed */
+} ma_status;
+
+/* Range types; 0..3 keep the numbering of MagiAttention's attn_type_map. */
+typedef enum {
+  MA_RANGE_FULL = 0,
+  MA_RANGE_CAUSAL = 1,
+  MA_RANGE_INV_CAUSAL = 2,
+  MA_RANGE_BI_CAUSAL = 3,
+  MA_RANGE_CHUNK_CAUSAL = 4
+} ma_range_type;
+
+typedef enum {
+  MA_KIND_CAUSAL = 0,
+  MA_KIND_SLIDING_WINDOW = 1,
+  MA_KIND_PREFIX_LM = 2,
+  MA_KIND_RANGES = 3,
+  MA_KIND_DENSE_BOOL = 4,
+  MA_KIND_PACKED_U64 = 5
+} ma_mask_kind;
+
+typedef enum { MA_F32 = 0, MA_BF16 = 1 } ma_dtype;
+
+/* Tile classes stored in a plan. */
+typedef enum { MA_TILE_SKIP = 0, MA_TILE_FULL = 1, MA_TILE_PARTIAL = 2 } ma_tile_class;
+
+typedef struct {
+  int32_t q_start, q_end; /* query rows [q_start, q_end) of the sequence */
+  int32_t k_start, k_end; /* keys [k_start, k_end) */
+  int32_t type;           /* ma_range_type */
+  int32_t chunk_size;     /* CHUNK_CAUSAL only, >= 1 */
+} ma_range;
+
+/* A mask description for mask_compile.  All arrays not marked otherwise are
+ * host memory and are only read during the call. */
+typedef struct {
+  int32_t kind;                 /* ma_mask_kind */
+  int32_t batch;                /* number of sequences, >= 1 */
+  const int32_t *cu_seqlens_q;  /* host [batch+1], nondecreasing, starts at 0 */
+  const int32_t *kv_lens;       /* host [batch], kv_len >= q_len of the sequence */
+  int32_t window;               /* SLIDING_WINDOW: >= 1 (other kinds: must be 0) */
+  const int32_t *prefix_len;    /* PREFIX_LM: host [batch], 0 <= prefix_len <= kv_len */
+  const ma_range *ranges;       /* RANGES: host, range_indptr[batch] descriptors */
+  const int32_t *range_indptr;  /* RANGES: host [batch+1] CSR offsets into ranges */
+  const void *mask;             /* DENSE_BOOL (uint8) or PACKED_U64 (uint64) */
+  int64_t mask_numel;           /* elements in `mask`; must cover every sequence exactly or more */
+  int32_t mask_on_device;       /* 1: `mask` is device memory (classified on the GPU, stream-ordered) */
+  int32_t tile_q;               /* 64 or 128: query rows per tile */
+  int32_t tile_k;               /* 64: keys per tile */
+} ma_mask_desc;
+
+/* A compiled plan: per (sequence, q-tile, k-tile) FULL/SKIP/PARTIAL, the
+ * packed words of PARTIAL tiles, and the q-tiles in execution order (most
+ * non-SKIP tiles first).  Opaque; owned by the library. */
+typedef struct ma_plan ma_plan;
+
+typedef struct {
+  int32_t batch, tile_q, tile_k;
+  int32_t num_qtiles;      /* q-tile rows over all sequences */
+  int64_t num_tiles;       /* sum over sequences of q-tiles x k-tiles */
+  int64_t num_entries;     /* non-SKIP tiles (an upper bound for device-built plans) */
+  int64_t num_word_blocks; /* PARTIAL word blocks held (tile_q rows each) */
+  int64_t total_q;         /* cu_seqlens_q[batch] */
+  int64_t device_bytes;    /* size of the plan's device buffer (0 before upload) */
+  int32_t on_device;       /* 1 when the device buffer is populated */
+  int32_t host_valid;      /* 1 when a host copy exists (host-compiled plans) */
+} ma_plan_info;
+
+/* Compile a mask into a plan and make it resident on the device (one
+ * stream-ordered upload, or a device classification pass for a device-resident
+ * DENSE_BOOL / PACKED_U64 mask).  The plan depends on the mask only: equal
+ * masks give byte-identical plans whatever descriptors described them.
+ * Errors: INVALID / CONFLICT (window given with another kind; a custom mask
+ * combined with causal is expressed by choosing one kind) / SIZE (mask_numel
+ * short of sum q_len*kv_len, or of sum q_len*ceil(kv_len/64) words) /
+ * UNSUPPORTED (tile shape) / HIP / NOMEM.  *out is set only on MA_OK. */
+ma_status mask_compile(const ma_mask_desc *desc, void *stream, ma_plan **out);
+
+/* Host-only compile (no HIP call): descriptors or a host-resident mask.
+ * Used to inspect plans without a GPU; attn_prefill_masked uploads such a
+ * plan on first use. */
+ma_status mask_compile_host(const ma_mask_desc *desc, ma_plan **out);
+
+/* Upload a host-compiled plan (no-op when already on the device). */
+ma_status mask_plan_upload(ma_plan *plan, void *stream);
+
+ma_status mask_plan_destroy(ma_plan *plan);
+
+ma_status mask_plan_info_get(const ma_plan *plan, ma_plan_info *out);
+
+/* Dense export for tests: classes[num_tiles] (ma_tile_class, tiles of
+ * sequence 0 first, q-tile major, k-tile minor) and, if words != NULL,
+ * words[num_tiles * tile_q * tile_k/64] holding each PARTIAL tile's rows
+ * (zero for other tiles).  Reads the device copy when there is no host copy
+ * (synchronises the device). */
+ma_status mask_plan_export(const ma_plan *plan, uint8_t *classes, uint64_t *words);
+
+/* Canonical serialisation of the plan (execution order, tile lists and
+ * words), for byte-identity checks.  Call with dst = NULL to get *bytes. */
+ma_status mask_plan_serialize(const ma_plan *plan, void *dst, size_t *bytes);
+
+/* Masked prefill over a compiled plan.
+ *  q        device [total_q, Hq, d], in_dtype, contiguous
+ *  k_cache, v_cache  device paged caches of in_dtype; element (page, slot,
+ *           head, x) at page*kv_strides[0] + slot*kv_strides[1] +
+ *           head*kv_strides[2] + x (strides in elements, x contiguous)
+ *  page_table device int32 [batch, max_pages]; entry (b, i) is the physical
+ *           page of keys i*page_size .. (i+1)*page_size-1 of sequence b.  Only
+ *           entries for keys < kv_len are read.
+ *  page_size power of two >= 1
+ *  out      device [total_q, Hq, d] of out_dtype; lse device fp32 [total_q,
+ *           Hq] or NULL
+ *  scale    positive, finite (the softmax temperature, usually 1/sqrt(d))
+ * Supported: in_dtype BF16 with d in {64, 128, 256} and out_dtype BF16 or F32;
+ * in_dtype F32 with d in {64, 128} and out_dtype F32.  Arithmetic: fp32
+ * accumulation; bf16 inputs use bf16 matrix products, fp32 inputs fp32 ones.
+ * Launches are stream-ordered; the call does not synchronise.  Results are
+ * deterministic (no atomics touch accumulators). */
+ma_status attn_prefill_masked(const ma_plan *plan, const void *q, int64_t total_q, int32_t hq,
+                              const void *k_cache, const void *v_cache, int32_t hkv, int32_t d,
+                              int32_t page_size, const int64_t kv_strides[3],
+                              const int32_t *page_table, int32_t max_pages, int32_t in_dtype,
+                              int32_t out_dtype, float scale, void *out, float *lse, void *stream);
+
+/* Workspace bytes attn_verify_tree needs for these bounds. */
+size_t attn_verify_tree_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq,
+                                  int32_t hkv, int32_t d);
+
+/* Speculative tree verify: every sequence's draft-tree queries (q_len <= 64
+ * per sequence) against its cached context plus the draft tokens, under a
+ * full-row custom mask (DENSE_BOOL or PACKED_U64, device memory, rows over
+ * all kv_len keys).  Lengths stay on the device (no host round trip):
+ *  cu_seqlens_q device int32 [batch+1], kv_lens device int32 [batch];
+ *  max_q >= every q_len (<= 64), max_kv >= every kv_len (host bounds used for
+ *  the launch shape and the workspace).
+ * The GQA group of a K/V head is processed together (the group's query heads
+ * share each K/V tile) and long contexts are split over several workgroups
+ * whose partial results are merged in a fixed order.  Requires in_dtype BF16
+ * and d in {64, 128, 256}.  workspace: device, at least
+ * attn_verify_tree_workspace(...) bytes (NULL allowed
+ * when that is 0), owned by the caller; its contents need no initialisation. */
+ma_status attn_verify_tree(const void *q, int64_t total_q, int32_t hq, const void *k_cache,
+                           const void *v_cache, int32_t hkv, int32_t d, int32_t page_size,
+                           const int64_t kv_strides[3], const int32_t *page_table,
+                           int32_t max_pages, const int32_t *cu_seqlens_q, const int32_t *kv_lens,
+                           int32_t batch, int32_t max_q, int32_t max_kv, int32_t mask_kind,
+                           const void *mask, int64_t mask_numel, int32_t in_dtype,
+                           int32_t out_dtype, float scale, void *workspace, size_t ws_bytes,
+                           void *out, float *lse, void *stream);
+
+const char *ma_status_string(int32_t status);
+const char *ma_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MASKATTN_H */

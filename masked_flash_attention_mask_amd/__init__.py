@@ -1,0 +1,14 @@
+"""masked_flash_attention_mask_amd — masked flash-attention prefill and
+speculative tree verify over ragged, paged K/V on MI355X (gfx950).
+
+The compute path is libmaskattn.so (hand-written HIP kernels behind a C ABI,
+declared in include/maskattn.h).  This package is its thin ctypes binding; it
+needs the library to be built and raises when it is not.
+"""
+
+from ._lib import (  # noqa: F401
+    BF16, F32, KIND, LIB, LIB_PATH, MaskAttnError, Plan, RANGE_BI_CAUSAL, RANGE_CAUSAL,
+    RANGE_CHUNK_CAUSAL, RANGE_FULL, RANGE_INV_CAUSAL, TILE_FULL, TILE_PARTIAL, TILE_SKIP,
+    attn_prefill_masked, attn_verify_tree, attn_verify_tree_workspace, mask_compile,
+    mask_compile_host,
+)

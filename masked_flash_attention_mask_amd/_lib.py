@@ -1,0 +1,274 @@
+"""ctypes binding of libmaskattn.so: argument marshalling only.
+
+Every function here converts Python / torch arguments into the C ABI's plain
+pointers and sizes and calls the library; none computes any part of the
+attention or the mask.  The library must have been built (see build.py); a
+missing library raises at import of this module, there is no fallback.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmaskattn.so")
+
+MA_OK, MA_ERR_INVALID, MA_ERR_CONFLICT, MA_ERR_SIZE = 0, -1, -2, -3
+MA_ERR_UNSUPPORTED, MA_ERR_PLAN_MISMATCH, MA_ERR_HIP, MA_ERR_NOMEM = -4, -5, -6, -7
+RANGE_FULL, RANGE_CAUSAL, RANGE_INV_CAUSAL, RANGE_BI_CAUSAL, RANGE_CHUNK_CAUSAL = 0, 1, 2, 3, 4
+KIND = {"causal": 0, "window": 1, "prefix_lm": 2, "ranges": 3, "dense": 4, "packed": 5}
+F32, BF16 = 0, 1
+TILE_SKIP, TILE_FULL, TILE_PARTIAL = 0, 1, 2
+
+EXPORTS = ["mask_compile", "mask_compile_host", "mask_plan_upload", "mask_plan_destroy",
+           "mask_plan_info_get", "mask_plan_export", "mask_plan_serialize", "attn_prefill_masked",
+           "attn_verify_tree_workspace", "attn_verify_tree", "ma_status_string", "ma_last_error"]
+
+
+class MaRange(ctypes.Structure):
+    _fields_ = [("q_start", ctypes.c_int32), ("q_end", ctypes.c_int32), ("k_start", ctypes.c_int32),
+                ("k_end", ctypes.c_int32), ("type", ctypes.c_int32), ("chunk_size", ctypes.c_int32)]
+
+
+class MaMaskDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("cu_seqlens_q", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p),
+                ("window", ctypes.c_int32), ("prefix_len", ctypes.c_void_p),
+                ("ranges", ctypes.c_void_p), ("range_indptr", ctypes.c_void_p),
+                ("mask", ctypes.c_void_p), ("mask_numel", ctypes.c_int64),
+                ("mask_on_device", ctypes.c_int32), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32)]
+
+
+class MaPlanInfo(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
+                ("num_qtiles", ctypes.c_int32), ("num_tiles", ctypes.c_int64),
+                ("num_entries", ctypes.c_int64), ("num_word_blocks", ctypes.c_int64),
+                ("total_q", ctypes.c_int64), ("device_bytes", ctypes.c_int64),
+                ("on_device", ctypes.c_int32), ("host_valid", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with masked_flash_attention_mask_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "mask_compile": (i32, [vp, vp, pp]),
+        "mask_compile_host": (i32, [vp, pp]),
+        "mask_plan_upload": (i32, [vp, vp]),
+        "mask_plan_destroy": (i32, [vp]),
+        "mask_plan_info_get": (i32, [vp, vp]),
+        "mask_plan_export": (i32, [vp, vp, vp]),
+        "mask_plan_serialize": (i32, [vp, vp, ctypes.POINTER(sz)]),
+        "attn_prefill_masked": (i32, [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, i32, i32, f32,
+                                      vp, vp, vp]),
+        "attn_verify_tree_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
+        "attn_verify_tree": (i32, [vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp, i32, i32, i32,
+                                   i32, vp, i64, i32, i32, f32, vp, sz, vp, vp, vp]),
+        "ma_status_string": (ctypes.c_char_p, [i32]),
+        "ma_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+class MaskAttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = LIB.ma_last_error().decode() or LIB.ma_status_string(status).decode()
+        super().__init__(f"{where}: {LIB.ma_status_string(status).decode()} ({status}): {msg}")
+
+
+def check(status, where):
+    if status != MA_OK:
+        raise MaskAttnError(status, where)
+
+
+def _i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(arr):
+    return None if arr is None else arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Plan:
+    """Owns one ma_plan handle."""
+
+    def __init__(self, handle, keep):
+        self.handle = handle
+        self._keep = keep   # the host arrays the description pointed at
+
+    def __del__(self):
+        h, self.handle = getattr(self, "handle", None), None
+        if h:
+            LIB.mask_plan_destroy(h)
+
+    def info(self):
+        out = MaPlanInfo()
+        check(LIB.mask_plan_info_get(self.handle, ctypes.byref(out)), "mask_plan_info_get")
+        return out
+
+    def export(self, words=True):
+        """(classes uint8 [num_tiles], words uint64 [num_tiles, tile_q] or None)."""
+        inf = self.info()
+        cls = np.zeros(inf.num_tiles, dtype=np.uint8)
+        w = np.zeros((inf.num_tiles, inf.tile_q * inf.tile_k // 64), dtype=np.uint64) if words else None
+        check(LIB.mask_plan_export(self.handle, _ptr(cls), _ptr(w)), "mask_plan_export")
+        return cls, w
+
+    def serialize(self):
+        n = ctypes.c_size_t(0)
+        check(LIB.mask_plan_serialize(self.handle, None, ctypes.byref(n)), "mask_plan_serialize")
+        buf = np.zeros(n.value, dtype=np.uint8)
+        check(LIB.mask_plan_serialize(self.handle, _ptr(buf), ctypes.byref(n)), "mask_plan_serialize")
+        return buf.tobytes()
+
+    def upload(self, stream=None):
+        check(LIB.mask_plan_upload(self.handle, _stream(stream)), "mask_plan_upload")
+
+
+def make_desc(kind, cu_seqlens_q, kv_lens, window=0, prefix_len=None, ranges=None, mask=None,
+              tile_q=128, tile_k=64):
+    """Builds the C mask description; returns (desc, arrays to keep alive)."""
+    cu = _i32(cu_seqlens_q)
+    kv = _i32(kv_lens)
+    keep = [cu, kv]
+    d = MaMaskDesc()
+    d.kind = KIND[kind] if isinstance(kind, str) else int(kind)
+    d.batch = len(kv)
+    d.cu_seqlens_q = _ptr(cu)
+    d.kv_lens = _ptr(kv)
+    d.window = int(window)
+    d.tile_q = tile_q
+    d.tile_k = tile_k
+    if prefix_len is not None:
+        pl = _i32(prefix_len)
+        keep.append(pl)
+        d.prefix_len = _ptr(pl)
+    if ranges is not None:
+        flat = [r for seq in ranges for r in seq]
+        indptr = _i32(np.concatenate([[0], np.cumsum([len(s) for s in ranges])]))
+        arr = (MaRange * max(1, len(flat)))(*[MaRange(*map(int, r)) for r in flat])
+        keep += [indptr, arr]
+        d.ranges = ctypes.cast(arr, ctypes.c_void_p)
+        d.range_indptr = _ptr(indptr)
+    if mask is not None:
+        if hasattr(mask, "is_cuda"):
+            d.mask = ctypes.c_void_p(mask.data_ptr())
+            d.mask_numel = mask.numel()
+            d.mask_on_device = 1 if mask.is_cuda else 0
+            keep.append(mask)
+        else:
+            m = np.ascontiguousarray(mask)
+            keep.append(m)
+            d.mask = _ptr(m)
+            d.mask_numel = m.size
+            d.mask_on_device = 0
+    return d, keep
+
+
+def mask_compile_host(kind, cu_seqlens_q, kv_lens, **kw):
+    desc, keep = make_desc(kind, cu_seqlens_q, kv_lens, **kw)
+    h = ctypes.c_void_p()
+    check(LIB.mask_compile_host(ctypes.byref(desc), ctypes.byref(h)), "mask_compile_host")
+    return Plan(h.value, keep)
+
+
+def mask_compile(kind, cu_seqlens_q, kv_lens, stream=None, **kw):
+    desc, keep = make_desc(kind, cu_seqlens_q, kv_lens, **kw)
+    h = ctypes.c_void_p()
+    check(LIB.mask_compile(ctypes.byref(desc), _stream(stream), ctypes.byref(h)), "mask_compile")
+    return Plan(h.value, keep)
+
+
+def _dtype_code(t):
+    import torch
+    if t == torch.bfloat16:
+        return BF16
+    if t == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _cache_args(k_cache, v_cache):
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ValueError("k_cache and v_cache must share shape [pages, page_size, Hkv, d] and strides")
+    if k_cache.stride(3) != 1:
+        raise ValueError("the head dimension of the caches must be contiguous")
+    strides = (ctypes.c_int64 * 3)(k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
+    return strides
+
+
+def attn_prefill_masked(plan, q, k_cache, v_cache, page_table, scale, out=None, lse=None,
+                        out_dtype=None, stream=None):
+    """q [total_q, Hq, d]; caches [pages, page_size, Hkv, d]; page_table int32
+    [batch, max_pages].  Returns (out, lse)."""
+    import torch
+    if not q.is_contiguous() or not page_table.is_contiguous() or page_table.dtype != torch.int32:
+        raise ValueError("q must be contiguous and page_table a contiguous int32 tensor")
+    total_q, hq, d = q.shape
+    hkv, page_size = k_cache.shape[2], k_cache.shape[1]
+    strides = _cache_args(k_cache, v_cache)
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((total_q, hq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device)
+    st = LIB.attn_prefill_masked(
+        plan.handle, q.data_ptr(), total_q, hq, k_cache.data_ptr(), v_cache.data_ptr(), hkv, d, page_size,
+        strides, page_table.data_ptr(), page_table.shape[1], _dtype_code(q.dtype), _dtype_code(out.dtype),
+        float(scale), out.data_ptr(), lse.data_ptr() if lse is not False else None, _stream(stream))
+    check(st, "attn_prefill_masked")
+    return out, lse
+
+
+def attn_verify_tree_workspace(batch, max_q, max_kv, hq, hkv, d):
+    return int(LIB.attn_verify_tree_workspace(batch, max_q, max_kv, hq, hkv, d))
+
+
+def attn_verify_tree(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, mask, mask_kind, max_q, max_kv,
+                     scale, workspace=None, out=None, lse=None, out_dtype=None, stream=None):
+    """Tree verify with lengths and mask on the device.  mask_kind: 'dense'
+    (uint8 rows) or 'packed' (int64/uint64 words)."""
+    import torch
+    total_q, hq, d = q.shape
+    hkv, page_size = k_cache.shape[2], k_cache.shape[1]
+    batch = kv_lens.shape[0]
+    strides = _cache_args(k_cache, v_cache)
+    for t in (q, page_table, cu_seqlens_q, kv_lens, mask):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("verify tensors must be contiguous device tensors")
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((total_q, hq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device)
+    need = attn_verify_tree_workspace(batch, max_q, max_kv, hq, hkv, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = LIB.attn_verify_tree(
+        q.data_ptr(), total_q, hq, k_cache.data_ptr(), v_cache.data_ptr(), hkv, d, page_size, strides,
+        page_table.data_ptr(), page_table.shape[1], cu_seqlens_q.data_ptr(), kv_lens.data_ptr(), batch,
+        int(max_q), int(max_kv), KIND[mask_kind], mask.data_ptr(), mask.numel(), _dtype_code(q.dtype),
+        _dtype_code(out.dtype), float(scale), ws_ptr, ws_bytes, out.data_ptr(),
+        lse.data_ptr() if lse is not False else None, _stream(stream))
+    check(st, "attn_verify_tree")
+    return out, lse

@@ -1,0 +1,330 @@
+// Masked flash-attention prefill over a compiled plan (gfx950).
+//
+// One workgroup per (q-tile, query head).  The plan lists, per q-tile, the
+// k-tiles that are not SKIP in ascending key order, each FULL or PARTIAL;
+// SKIP tiles cost nothing (the block-sparse form flashinfer issue 724
+// recommends).  A PARTIAL tile carries one 64-bit word per query row; each
+// lane fetches its own row's word with one coalesced 8-byte load, prefetched
+// one tile ahead, and masks its scores with shifts of that word.  The mask
+// is thus never read per element from memory (the non-coalesced pattern the
+// same issue blames for a custom mask running about twice as slow as
+// causal).
+//
+// Per tile (64 keys), every wave owns 32 query rows:
+//   paged K/V gather -> registers (one tile ahead) -> LDS (K row-major, V
+//   transposed), S^T = K Q^T on bf16 matrix cores, mask, online softmax in
+//   fp32 with exp2, O^T += V^T P^T on bf16 matrix cores.
+// Two LDS stages, one barrier per tile.  The fp32 variant (fp32 inputs, fp32
+// matrix cores, no bf16 rounding anywhere) keeps the same walk with a single
+// stage.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+#include "kernels_common.h"
+#include "tile_bf16.h"
+
+namespace maskattn {
+using namespace dev;
+
+namespace {
+
+struct PrefillParams {
+  const SeqInfo *seqs;
+  const Item *items;
+  const Entry *entries;
+  const uint64_t *words;
+  const void *q;
+  const void *k;
+  const void *v;
+  const int32_t *page_table;
+  void *out;
+  float *lse;
+  int64_t s_page, s_slot, s_head;
+  int32_t max_pages, page_shift;
+  int32_t hq, group;
+  int32_t num_items;
+  float scale;
+  float scale_log2;
+};
+
+// Workgroup -> (work item, query head).  Workgroups are dispatched to the 8
+// XCDs round-robin; when Hq is a multiple of 8, each XCD gets a contiguous
+// block of Hq/8 query heads (so its L2 serves the K/V of few K/V heads) and
+// walks the work items in plan order (most work first).
+__device__ __forceinline__ void map_block(int b, int num_items, int hq, int &item, int &h) {
+  if ((hq & 7) == 0) {
+    const int m = hq >> 3, x = b & 7, slot = b >> 3;
+    item = slot / m;
+    h = x * m + slot % m;
+  } else {
+    item = b / hq;
+    h = b - item * hq;
+  }
+}
+
+template <int D, typename OutT>
+__device__ __forceinline__ void epilogue(const PrefillParams &p, const f32x16 (&o)[D / 32], float m_run,
+                                         float l_run, int64_t tok, int h, bool row_ok, int hi) {
+  const float lt = l_run + lane_swap32(l_run);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (!row_ok) return;
+  store_row<D, OutT>((OutT *)p.out + (tok * p.hq + h) * D, o, inv, hi);
+  if (p.lse && hi == 0) p.lse[tok * p.hq + h] = lt > 0.f ? m_run * p.scale + __logf(lt) : neg_inf();
+}
+
+// ---------------------------------------------------------------------------
+// bf16 inputs, bf16 matrix cores
+// ---------------------------------------------------------------------------
+template <int D, int BQ>
+struct Bf16Cfg {
+  static constexpr int NW = BQ / 32;
+  static constexpr int NT = NW * 64;
+  static constexpr size_t LDS_BYTES = 2 * Stage<D>::BYTES;
+};
+
+template <int D, int BQ, typename OutT>
+__global__ __launch_bounds__(BQ * 2, (D == 256 ? 1 : 2)) void prefill_bf16_kernel(PrefillParams p) {
+  using C = Bf16Cfg<D, BQ>;
+  extern __shared__ __align__(16) uint16_t lds[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  int item_idx, h;
+  map_block(blockIdx.x, p.num_items, p.hq, item_idx, h);
+  const Item it = p.items[item_idx];
+  const SeqInfo sq = p.seqs[it.seq];
+  const int g = h / p.group;
+  const int wrow = wave * 32 + l32;  // row inside the q-tile
+  const int row_local = it.qt * BQ + wrow;
+  const bool row_ok = row_local < sq.q_len;
+  const int64_t tok = (int64_t)sq.q_start + row_local;
+  const int kv_len = sq.kv_len;
+
+  bf16x8 qf[D / 16];
+  load_q<D>(qf, (const uint16_t *)p.q + (tok * p.hq + h) * D, row_ok, hi);
+
+  const uint16_t *kbase = (const uint16_t *)p.k + (int64_t)g * p.s_head;
+  const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)g * p.s_head;
+  const int32_t *pt = p.page_table + (int64_t)it.seq * p.max_pages;
+  KvTile<D, C::NT> kv;
+
+  auto load_word = [&](Entry e) -> uint64_t {
+    if (entry_cls(e.kt_cls) != MA_TILE_PARTIAL) return 0ull;
+    return p.words[(int64_t)e.wblk * BQ + wrow];
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
+  float m_run = neg_inf(), l_run = 0.f;
+  const float c = p.scale_log2;
+
+  const int eb = it.ent_begin, ee = it.ent_end;
+  uint64_t word_nxt = 0;
+  if (eb < ee) {
+    const Entry e0 = p.entries[eb];
+    kv.load(kbase, vbase, pt, p.page_shift, p.s_page, p.s_slot, entry_kt(e0.kt_cls), kv_len, tid);
+    word_nxt = load_word(e0);
+    kv.store(lds, tid);
+    __syncthreads();
+  }
+  for (int e = eb; e < ee; ++e) {
+    const int cur = (e - eb) & 1;
+    const Entry ec = p.entries[e];
+    const uint64_t wcur = word_nxt;
+    const bool has_next = e + 1 < ee;
+    if (has_next) {
+      const Entry en = p.entries[e + 1];
+      kv.load(kbase, vbase, pt, p.page_shift, p.s_page, p.s_slot, entry_kt(en.kt_cls), kv_len, tid);
+      word_nxt = load_word(en);
+    }
+    const uint16_t *stage = lds + cur * Stage<D>::ELEMS;
+    f32x16 sacc[2];
+    qk_tile<D>(stage, qf, sacc, l32, hi);
+
+    const int kt = entry_kt(ec.kt_cls);
+    const int cls = entry_cls(ec.kt_cls);
+    const int kin = kv_len - kt * 64;
+    if (cls == MA_TILE_PARTIAL || kin < 64)
+      apply_word(sacc, (cls == MA_TILE_PARTIAL ? wcur : ~0ull) & low_bits(kin), hi);
+
+    const float alpha = softmax_tile(sacc, m_run, l_run, c);
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+    pv_tile<D>(stage, sacc, oacc, l32, hi);
+    if (has_next) kv.store(lds + (cur ^ 1) * Stage<D>::ELEMS, tid);
+    __syncthreads();
+  }
+  epilogue<D, OutT>(p, oacc, m_run, l_run, tok, h, row_ok, hi);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs, fp32 matrix cores (v_mfma_f32_32x32x2_f32)
+// ---------------------------------------------------------------------------
+template <int D, int BQ>
+struct F32Cfg {
+  static constexpr int NW = BQ / 32;
+  static constexpr int NT = NW * 64;
+  static constexpr int KS = D + 1;   // odd stride: column reads are conflict-free
+  static constexpr int VS = D + 4;
+  static constexpr int CH = D / 4;   // 16-byte chunks per key row
+  static constexpr int CHUNKS = 64 * CH;
+  static constexpr size_t LDS_BYTES = (64 * KS + 64 * VS) * sizeof(float);
+};
+
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 2, 1) void prefill_f32_kernel(PrefillParams p) {
+  using C = F32Cfg<D, BQ>;
+  extern __shared__ __align__(16) float ldsf[];
+  float *Ks = ldsf;
+  float *Vs = ldsf + 64 * C::KS;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  int item_idx, h;
+  map_block(blockIdx.x, p.num_items, p.hq, item_idx, h);
+  const Item it = p.items[item_idx];
+  const SeqInfo sq = p.seqs[it.seq];
+  const int g = h / p.group;
+  const int row_local = it.qt * BQ + wave * 32 + l32;
+  const bool row_ok = row_local < sq.q_len;
+  const int64_t tok = (int64_t)sq.q_start + row_local;
+  const int kv_len = sq.kv_len;
+
+  float qf[D / 2];
+  {
+    const float *qb = (const float *)p.q + (tok * p.hq + h) * D + hi;
+#pragma unroll
+    for (int s = 0; s < D / 2; ++s) qf[s] = row_ok ? qb[2 * s] : 0.f;
+  }
+  const float *kbase = (const float *)p.k + (int64_t)g * p.s_head;
+  const float *vbase = (const float *)p.v + (int64_t)g * p.s_head;
+  const int32_t *pt = p.page_table + (int64_t)it.seq * p.max_pages;
+  const int pmask = (1 << p.page_shift) - 1;
+  const int wrow = wave * 32 + l32;
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
+  float m_run = neg_inf(), l_run = 0.f;
+  const float c = p.scale_log2;
+
+  for (int e = it.ent_begin; e < it.ent_end; ++e) {
+    const Entry ec = p.entries[e];
+    const int kt = entry_kt(ec.kt_cls);
+    const int cls = entry_cls(ec.kt_cls);
+    __syncthreads();  // previous tile fully consumed
+    for (int idx = tid; idx < C::CHUNKS; idx += C::NT) {
+      const int key = idx / C::CH, ch = idx % C::CH;
+      const int kk = kt * 64 + key;
+      f32x4 kv4 = {0.f, 0.f, 0.f, 0.f}, vv4 = {0.f, 0.f, 0.f, 0.f};
+      if (kk < kv_len) {
+        const int32_t page = pt[kk >> p.page_shift];
+        const int64_t off = (int64_t)page * p.s_page + (int64_t)(kk & pmask) * p.s_slot + 4 * ch;
+        kv4 = *(const f32x4 *)(kbase + off);
+        vv4 = *(const f32x4 *)(vbase + off);
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) Ks[key * C::KS + 4 * ch + x] = kv4[x];
+      *(f32x4 *)(Vs + key * C::VS + 4 * ch) = vv4;
+    }
+    const uint64_t word = cls == MA_TILE_PARTIAL ? p.words[(int64_t)ec.wblk * BQ + wrow] : ~0ull;
+    __syncthreads();
+
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < D / 2; ++s)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[(32 * kb + l32) * C::KS + 2 * s + hi], qf[s],
+                                                       sacc[kb], 0, 0, 0);
+    const int kin = kv_len - kt * 64;
+    if (cls == MA_TILE_PARTIAL || kin < 64) apply_word(sacc, word & low_bits(kin), hi);
+    const float alpha = softmax_tile(sacc, m_run, l_run, c);
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n)
+          oacc[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * C::VS + 32 * n + l32], sacc[kb][r], oacc[n],
+                                                         0, 0, 0);
+      }
+  }
+  epilogue<D, float>(p, oacc, m_run, l_run, tok, h, row_ok, hi);
+}
+
+template <typename K>
+ma_status launch_kernel(K kernel, int grid, int block, size_t lds, const PrefillParams &prm, void *stream) {
+  hipError_t e = hipSuccess;
+  if (lds > 64 * 1024) e = hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), lds, (hipStream_t)stream, prm);
+  e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return MA_OK;
+}
+
+template <int D, int BQ>
+ma_status dispatch_bf16(const PrefillArgs &a, const PrefillParams &prm, int grid) {
+  using C = Bf16Cfg<D, BQ>;
+  if (a.out_dtype == MA_F32)
+    return launch_kernel(prefill_bf16_kernel<D, BQ, float>, grid, C::NT, C::LDS_BYTES, prm, a.stream);
+  return launch_kernel(prefill_bf16_kernel<D, BQ, uint16_t>, grid, C::NT, C::LDS_BYTES, prm, a.stream);
+}
+
+template <int D, int BQ>
+ma_status dispatch_f32(const PrefillArgs &a, const PrefillParams &prm, int grid) {
+  using C = F32Cfg<D, BQ>;
+  return launch_kernel(prefill_f32_kernel<D, BQ>, grid, C::NT, C::LDS_BYTES, prm, a.stream);
+}
+
+}  // namespace
+
+ma_status launch_prefill(const PrefillArgs &a) {
+  const ma_plan *pl = a.plan;
+  PrefillParams prm{};
+  const char *base = (const char *)pl->dbuf;
+  prm.seqs = (const SeqInfo *)(base + pl->off_seqs);
+  prm.items = (const Item *)(base + pl->off_items);
+  prm.entries = (const Entry *)(base + pl->off_entries);
+  prm.words = (const uint64_t *)(base + pl->off_words);
+  prm.q = a.q;
+  prm.k = a.k;
+  prm.v = a.v;
+  prm.page_table = a.page_table;
+  prm.out = a.out;
+  prm.lse = a.lse;
+  prm.s_page = a.s_page;
+  prm.s_slot = a.s_slot;
+  prm.s_head = a.s_head;
+  prm.max_pages = a.max_pages;
+  prm.page_shift = a.page_shift;
+  prm.hq = a.hq;
+  prm.group = a.hq / a.hkv;
+  prm.num_items = pl->num_rows;
+  prm.scale = a.scale;
+  prm.scale_log2 = a.scale * kLog2e;
+  const int64_t grid64 = (int64_t)pl->num_rows * a.hq;
+  if (grid64 > INT32_MAX) return set_error(MA_ERR_UNSUPPORTED, "grid too large");
+  const int grid = (int)grid64;
+  const bool bq128 = pl->tile_q == 128;
+  if (a.in_dtype == MA_BF16) {
+    switch (a.d) {
+      case 64: return bq128 ? dispatch_bf16<64, 128>(a, prm, grid) : dispatch_bf16<64, 64>(a, prm, grid);
+      case 128: return bq128 ? dispatch_bf16<128, 128>(a, prm, grid) : dispatch_bf16<128, 64>(a, prm, grid);
+      case 256: return bq128 ? dispatch_bf16<256, 128>(a, prm, grid) : dispatch_bf16<256, 64>(a, prm, grid);
+    }
+  } else {
+    switch (a.d) {
+      case 64: return bq128 ? dispatch_f32<64, 128>(a, prm, grid) : dispatch_f32<64, 64>(a, prm, grid);
+      case 128: return bq128 ? dispatch_f32<128, 128>(a, prm, grid) : dispatch_f32<128, 64>(a, prm, grid);
+    }
+  }
+  return set_error(MA_ERR_UNSUPPORTED, "no kernel for dtype %d, head_dim %d", a.in_dtype, a.d);
+}
+
+}  // namespace maskattn

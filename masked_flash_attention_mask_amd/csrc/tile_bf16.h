@@ -1,0 +1,226 @@
+// bf16 tile machinery shared by the prefill and tree-verify kernels: paged
+// K/V gather of one 64-key tile into registers, the LDS stage layout, and the
+// two matrix-core products of a wave's 32 query rows against a staged tile.
+#pragma once
+
+#include "internal.h"
+#include "kernels_common.h"
+
+namespace maskattn {
+namespace dev {
+
+// LDS stage of one 64-key tile: K row-major [64][D + 8] and V transposed
+// [D][64 + 4] (bf16 elements).  The pads spread the matrix-core operand reads
+// of 32 rows over all banks.
+template <int D>
+struct Stage {
+  static constexpr int KS = D + 8;
+  static constexpr int VS = 64 + 4;
+  static constexpr int ELEMS = 64 * KS + D * VS;
+  static constexpr size_t BYTES = ELEMS * sizeof(uint16_t);
+};
+
+// Per-thread share of a tile gather: (4-key group, 16-byte chunk) pairs.
+template <int D, int NT>
+struct KvTile {
+  static constexpr int CH = D / 8;
+  static constexpr int PAIRS = 16 * CH;
+  static constexpr int PPT = (PAIRS + NT - 1) / NT;
+  u32x4 kreg[PPT][4];
+  u32x4 vreg[PPT][4];
+
+  // Gathers keys [64*kt, 64*kt + 64) of one K/V head; keys >= kv_len read as
+  // zero and touch neither the page table nor the cache.
+  __device__ __forceinline__ void load(const uint16_t *kbase, const uint16_t *vbase, const int32_t *pt,
+                                       int page_shift, int64_t s_page, int64_t s_slot, int kt, int kv_len,
+                                       int tid) {
+    const int pmask = (1 << page_shift) - 1;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pair = tid + i * NT;
+      if (PAIRS % NT == 0 || pair < PAIRS) {
+        const int kg = pair / CH, c = pair % CH;
+        const int key0 = kt * 64 + 4 * kg;
+        if (page_shift >= 2) {  // the 4 keys share a page
+          const int32_t page = key0 < kv_len ? pt[key0 >> page_shift] : 0;
+          const int64_t base = (int64_t)page * s_page + (int64_t)(key0 & pmask) * s_slot + 8 * c;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (key0 + j < kv_len) {
+              kreg[i][j] = *(const u32x4 *)(kbase + base + j * s_slot);
+              vreg[i][j] = *(const u32x4 *)(vbase + base + j * s_slot);
+            } else {
+              kreg[i][j] = u32x4{0, 0, 0, 0};
+              vreg[i][j] = u32x4{0, 0, 0, 0};
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = key0 + j;
+            if (key < kv_len) {
+              const int32_t page = pt[key >> page_shift];
+              const int64_t off = (int64_t)page * s_page + (int64_t)(key & pmask) * s_slot + 8 * c;
+              kreg[i][j] = *(const u32x4 *)(kbase + off);
+              vreg[i][j] = *(const u32x4 *)(vbase + off);
+            } else {
+              kreg[i][j] = u32x4{0, 0, 0, 0};
+              vreg[i][j] = u32x4{0, 0, 0, 0};
+            }
+          }
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t *stage, int tid) const {
+    uint16_t *Ks = stage;
+    uint16_t *Vt = stage + 64 * Stage<D>::KS;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pair = tid + i * NT;
+      if (PAIRS % NT == 0 || pair < PAIRS) {
+        const int kg = pair / CH, c = pair % CH;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *(u32x4 *)(Ks + (4 * kg + j) * Stage<D>::KS + 8 * c) = kreg[i][j];
+        // V^T rows are head-dim indices; 4 consecutive keys per 8-byte store.
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t a0 = vreg[i][0][m], a1 = vreg[i][1][m], a2 = vreg[i][2][m], a3 = vreg[i][3][m];
+          const u32x2 lo = {perm_b32(a1, a0, 0x05040100u), perm_b32(a3, a2, 0x05040100u)};
+          const u32x2 hv = {perm_b32(a1, a0, 0x07060302u), perm_b32(a3, a2, 0x07060302u)};
+          *(u32x2 *)(Vt + (8 * c + 2 * m) * Stage<D>::VS + 4 * kg) = lo;
+          *(u32x2 *)(Vt + (8 * c + 2 * m + 1) * Stage<D>::VS + 4 * kg) = hv;
+        }
+      }
+    }
+  }
+};
+
+// Q rows as B operands: lane l holds Q[row][16 s + 8 (l / 32) .. + 7].
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 16], const uint16_t *qrow, bool ok, int hi) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const u32x4 raw = ok ? *(const u32x4 *)(qrow + 16 * s + 8 * hi) : u32x4{0, 0, 0, 0};
+    qf[s] = __builtin_bit_cast(bf16x8, raw);
+  }
+}
+
+// S^T for keys [0, 64) of the staged tile and the wave's 32 query rows.
+template <int D>
+__device__ __forceinline__ void qk_tile(const uint16_t *stage, const bf16x8 (&qf)[D / 16], f32x16 (&s)[2],
+                                        int l32, int hi) {
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+      const bf16x8 a = __builtin_bit_cast(
+          bf16x8, *(const u32x4 *)(stage + (32 * kb + l32) * Stage<D>::KS + 16 * k + 8 * hi));
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k], s[kb], 0, 0, 0);
+    }
+}
+
+// O^T += V^T P^T.  P leaves the S^T accumulator as the B operand: product u
+// takes registers 8 (u % 2) .. + 7 of score block u / 2, i.e. keys
+// 32 (u/2) + 16 (u%2) + 8 (e/4) + 4 (l/32) + e % 4 for element e; the V^T
+// operand reads the same keys (two 8-byte reads per lane).
+template <int D>
+__device__ __forceinline__ void pv_tile(const uint16_t *stage, const f32x16 (&p)[2], f32x16 (&o)[D / 32],
+                                        int l32, int hi) {
+  const uint16_t *Vt = stage + 64 * Stage<D>::KS;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int kb = u >> 1, hh = u & 1;
+    f32x8 pv;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) pv[x] = p[kb][8 * hh + x];
+    const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
+    const int koff = 32 * kb + 16 * hh + 4 * hi;
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) {
+      const uint16_t *vr = Vt + (32 * n + l32) * Stage<D>::VS + koff;
+      const u32x2 a0 = *(const u32x2 *)vr;
+      const u32x2 a1 = *(const u32x2 *)(vr + 8);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
+      o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[n], 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t low_bits(int n) {  // n in [0, 64]
+  return n >= 64 ? ~0ull : (n <= 0 ? 0ull : ((1ull << n) - 1ull));
+}
+
+// Masks the two 32-key score blocks of a lane with its row's tile word.
+// Score (kb, r) of lane l is key 32 kb + 8 (r / 4) + 4 (l / 32) + r % 4.
+__device__ __forceinline__ void apply_word(f32x16 (&s)[2], uint64_t word, int hi) {
+  const uint64_t ws = word >> (4 * hi);
+  const uint32_t w0 = (uint32_t)ws, w1 = (uint32_t)(ws >> 32);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int bit = 8 * (r >> 2) + (r & 3);
+    if (!((w0 >> bit) & 1u)) s[0][r] = neg_inf();
+    if (!((w1 >> bit) & 1u)) s[1][r] = neg_inf();
+  }
+}
+
+// Online-softmax update for one tile (scores -> probabilities).  Returns the
+// factor the O accumulator is rescaled by.  Rows with no visible key so far
+// keep m = -inf and produce zeros.
+__device__ __forceinline__ float softmax_tile(f32x16 (&s)[2], float &m_run, float &l_run, float c) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+  mx = fmaxf(mx, lane_swap32(mx));
+  const float m_new = fmaxf(m_run, mx);
+  const float m_use = m_new == neg_inf() ? 0.f : m_new;
+  const float alpha = fast_exp2((m_run - m_use) * c);
+  const float mc = m_use * c;
+  float psum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
+      s[kb][r] = pv;
+      psum += pv;
+    }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+  return alpha;
+}
+
+template <typename OutT>
+__device__ __forceinline__ void store4(OutT *dst, float a, float b, float c, float d);
+
+template <>
+__device__ __forceinline__ void store4<float>(float *dst, float a, float b, float c, float d) {
+  *(f32x4 *)dst = f32x4{a, b, c, d};
+}
+
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t *dst, float a, float b, float c, float d) {
+  *(u32x2 *)dst = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+
+// Writes a lane's normalised output row slice (O^T register layout: register
+// r of block n is head-dim 32 n + 8 (r / 4) + 4 (l / 32) + r % 4).
+template <int D, typename OutT>
+__device__ __forceinline__ void store_row(OutT *dst, const f32x16 (&o)[D / 32], float inv, int hi) {
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = 32 * n + 8 * r4 + 4 * hi;
+      store4<OutT>(dst + d0, o[n][4 * r4] * inv, o[n][4 * r4 + 1] * inv, o[n][4 * r4 + 2] * inv,
+                   o[n][4 * r4 + 3] * inv);
+    }
+}
+
+}  // namespace dev
+}  // namespace maskattn

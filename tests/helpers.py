@@ -1,0 +1,97 @@
+"""Shared plumbing for the GPU parity tests: device copies of a workload, the
+library calls, the oracle's masks for the same inputs, and error metrics."""
+
+import numpy as np
+import torch
+
+import masked_flash_attention_mask_amd as ma
+from oracle import attention as OA
+from oracle import masks as OM
+
+TOL_F32 = 1e-5      # fp32 inputs, fp32 accumulation
+TOL_BF16 = 1.5e-2   # bf16 inputs, fp32 accumulation, fp32 output
+
+
+def device_inputs(w, dev="cuda"):
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    return {
+        "q": torch.from_numpy(w.q).to(dev).to(dt).contiguous(),
+        "k": torch.from_numpy(w.k_cache).to(dev).to(dt).contiguous(),
+        "v": torch.from_numpy(w.v_cache).to(dev).to(dt).contiguous(),
+        "pt": torch.from_numpy(w.page_table).to(dev).contiguous(),
+        "cu": torch.from_numpy(w.cu_seqlens_q).to(dev).contiguous(),
+        "kv": torch.from_numpy(w.kv_lens).to(dev).contiguous(),
+    }
+
+
+def compile_plan(w, mask_name, tile_q=128, device_mask=True):
+    mi = w.masks[mask_name]
+    kw = {}
+    if mi.kind == "window":
+        kw["window"] = mi.window
+    elif mi.kind == "prefix_lm":
+        kw["prefix_len"] = mi.prefix_len
+    elif mi.kind == "ranges":
+        kw["ranges"] = mi.ranges
+    elif mi.kind in ("dense", "packed"):
+        data = mi.data if mi.kind == "dense" else mi.data.view(np.int64)
+        kw["mask"] = torch.from_numpy(np.ascontiguousarray(data)).cuda() if device_mask else mi.data
+    return ma.mask_compile(mi.kind, w.cu_seqlens_q, w.kv_lens, tile_q=tile_q, **kw)
+
+
+def run_prefill(w, dev_in, mask_name, tile_q=128, out_dtype=torch.float32, device_mask=True):
+    plan = compile_plan(w, mask_name, tile_q, device_mask)
+    out, lse = ma.attn_prefill_masked(plan, dev_in["q"], dev_in["k"], dev_in["v"], dev_in["pt"], w.scale,
+                                      out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, lse, plan
+
+
+def oracle_masks(w, mask_name):
+    mi = w.masks[mask_name]
+    ql, kl = w.q_lens, w.kv_lens
+    if mi.kind == "causal":
+        return lambda b: OM.causal(int(ql[b]), int(kl[b]))
+    if mi.kind == "window":
+        return lambda b: OM.sliding_window(int(ql[b]), int(kl[b]), mi.window)
+    if mi.kind == "prefix_lm":
+        return lambda b: OM.prefix_lm(int(ql[b]), int(kl[b]), int(mi.prefix_len[b]))
+    if mi.kind == "ranges":
+        return lambda b: OM.ranges(int(ql[b]), int(kl[b]), mi.ranges[b])
+    if mi.kind == "dense":
+        lst = OM.dense_from_flat(mi.data, ql, kl)
+        return lambda b: lst[b]
+    if mi.kind == "packed":
+        lst = OM.packed_from_flat(mi.data, ql, kl)
+        return lambda b: lst[b]
+    raise ValueError(mi.kind)
+
+
+def oracle(w, mask_name, heads=None, rows=None):
+    return OA.attention(w.q, w.k_cache, w.v_cache, w.page_table, w.cu_seqlens_q, w.kv_lens,
+                        oracle_masks(w, mask_name), w.scale, heads=heads, rows=rows)
+
+
+def max_abs_err(gpu, ref):
+    g = gpu.float().cpu().numpy().astype(np.float64)
+    sel = ~np.isnan(ref)
+    assert not np.isnan(g[sel]).any(), "GPU output has NaN where the oracle has a value"
+    return float(np.abs(g[sel] - ref[sel]).max()) if sel.any() else 0.0
+
+
+def lse_err(gpu_lse, ref_lse):
+    g = gpu_lse.cpu().numpy().astype(np.float64)
+    sel = ~np.isnan(ref_lse)
+    fin = sel & np.isfinite(ref_lse)
+    assert np.array_equal(np.isneginf(g[sel]), np.isneginf(ref_lse[sel])), "fully masked rows differ"
+    return float(np.abs(g[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
+
+
+def bf16_out_err(gpu_bf16, ref):
+    """Error of a bf16 output against the oracle, less one bf16 rounding step
+    of the reference value (the output rounding alone)."""
+    g = gpu_bf16.float().cpu().numpy().astype(np.float64)
+    sel = ~np.isnan(ref)
+    r = ref[sel]
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - 7)
+    return float((np.abs(g[sel] - r) - ulp).max())

