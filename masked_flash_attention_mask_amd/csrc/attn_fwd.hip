@@ -62,14 +62,15 @@ __device__ __forceinline__ void map_block(int b, int num_items, int hq, int &ite
   }
 }
 
+// m_ref is the softmax reference in log2 units (scale * log2 e applied).
 template <int D, typename OutT>
-__device__ __forceinline__ void epilogue(const PrefillParams &p, const f32x16 (&o)[D / 32], float m_run,
+__device__ __forceinline__ void epilogue(const PrefillParams &p, const f32x16 (&o)[D / 32], float m_ref,
                                          float l_run, int64_t tok, int h, bool row_ok, int hi) {
-  const float lt = l_run + lane_swap32(l_run);
+  const float lt = sum_halves(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (!row_ok) return;
   store_row<D, OutT>((OutT *)p.out + (tok * p.hq + h) * D, o, inv, hi);
-  if (p.lse && hi == 0) p.lse[tok * p.hq + h] = lt > 0.f ? m_run * p.scale + __logf(lt) : neg_inf();
+  if (p.lse && hi == 0) p.lse[tok * p.hq + h] = lt > 0.f ? (m_ref + __log2f(lt)) * kLn2 : neg_inf();
 }
 
 // ---------------------------------------------------------------------------
@@ -83,7 +84,7 @@ struct Bf16Cfg {
 };
 
 template <int D, int BQ, typename OutT>
-__global__ __launch_bounds__(BQ * 2, (D == 256 ? 1 : 2)) void prefill_bf16_kernel(PrefillParams p) {
+__global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefill_bf16_kernel(PrefillParams p) {
   using C = Bf16Cfg<D, BQ>;
   extern __shared__ __align__(16) uint16_t lds[];
 
@@ -106,7 +107,9 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 ? 1 : 2)) void prefill_bf16_kerne
   const uint16_t *kbase = (const uint16_t *)p.k + (int64_t)g * p.s_head;
   const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)g * p.s_head;
   const int32_t *pt = p.page_table + (int64_t)it.seq * p.max_pages;
-  KvTile<D, C::NT> kv;
+  using KV = KvTile<D, C::NT>;
+  KV kv;
+  typename KV::Pages pg_nxt;
 
   auto load_word = [&](Entry e) -> uint64_t {
     if (entry_cls(e.kt_cls) != MA_TILE_PARTIAL) return 0ull;
@@ -116,15 +119,18 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 ? 1 : 2)) void prefill_bf16_kerne
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
-  float m_run = neg_inf(), l_run = 0.f;
+  float m_ref = neg_inf(), l_run = 0.f;
   const float c = p.scale_log2;
 
   const int eb = it.ent_begin, ee = it.ent_end;
   uint64_t word_nxt = 0;
   if (eb < ee) {
     const Entry e0 = p.entries[eb];
-    kv.load(kbase, vbase, pt, p.page_shift, p.s_page, p.s_slot, entry_kt(e0.kt_cls), kv_len, tid);
+    const int kt0 = entry_kt(e0.kt_cls);
+    const typename KV::Pages pg0 = kv.pages(pt, p.page_shift, kt0, kv_len, tid);
+    kv.load(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv_len, tid);
     word_nxt = load_word(e0);
+    if (eb + 1 < ee) pg_nxt = kv.pages(pt, p.page_shift, entry_kt(p.entries[eb + 1].kt_cls), kv_len, tid);
     kv.store(lds, tid);
     __syncthreads();
   }
@@ -135,8 +141,9 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 ? 1 : 2)) void prefill_bf16_kerne
     const bool has_next = e + 1 < ee;
     if (has_next) {
       const Entry en = p.entries[e + 1];
-      kv.load(kbase, vbase, pt, p.page_shift, p.s_page, p.s_slot, entry_kt(en.kt_cls), kv_len, tid);
+      kv.load(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, entry_kt(en.kt_cls), kv_len, tid);
       word_nxt = load_word(en);
+      if (e + 2 < ee) pg_nxt = kv.pages(pt, p.page_shift, entry_kt(p.entries[e + 2].kt_cls), kv_len, tid);
     }
     const uint16_t *stage = lds + cur * Stage<D>::ELEMS;
     f32x16 sacc[2];
@@ -148,14 +155,16 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 ? 1 : 2)) void prefill_bf16_kerne
     if (cls == MA_TILE_PARTIAL || kin < 64)
       apply_word(sacc, (cls == MA_TILE_PARTIAL ? wcur : ~0ull) & low_bits(kin), hi);
 
-    const float alpha = softmax_tile(sacc, m_run, l_run, c);
+    float alpha;
+    if (softmax_tile(sacc, m_ref, l_run, c, alpha)) {
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+      for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+    }
     pv_tile<D>(stage, sacc, oacc, l32, hi);
     if (has_next) kv.store(lds + (cur ^ 1) * Stage<D>::ELEMS, tid);
     __syncthreads();
   }
-  epilogue<D, OutT>(p, oacc, m_run, l_run, tok, h, row_ok, hi);
+  epilogue<D, OutT>(p, oacc, m_ref, l_run, tok, h, row_ok, hi);
 }
 
 // ---------------------------------------------------------------------------
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(BQ * 2, 1) void prefill_f32_kernel(PrefillParams p)
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
-  float m_run = neg_inf(), l_run = 0.f;
+  float m_ref = neg_inf(), l_run = 0.f;
   const float c = p.scale_log2;
 
   for (int e = it.ent_begin; e < it.ent_end; ++e) {
@@ -240,9 +249,11 @@ __global__ __launch_bounds__(BQ * 2, 1) void prefill_f32_kernel(PrefillParams p)
                                                        sacc[kb], 0, 0, 0);
     const int kin = kv_len - kt * 64;
     if (cls == MA_TILE_PARTIAL || kin < 64) apply_word(sacc, word & low_bits(kin), hi);
-    const float alpha = softmax_tile(sacc, m_run, l_run, c);
+    float alpha;
+    if (softmax_tile(sacc, m_ref, l_run, c, alpha)) {
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+      for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(BQ * 2, 1) void prefill_f32_kernel(PrefillParams p)
                                                          0, 0, 0);
       }
   }
-  epilogue<D, float>(p, oacc, m_run, l_run, tok, h, row_ok, hi);
+  epilogue<D, float>(p, oacc, m_ref, l_run, tok, h, row_ok, hi);
 }
 
 template <typename K>

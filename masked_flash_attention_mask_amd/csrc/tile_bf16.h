@@ -21,6 +21,11 @@ struct Stage {
 };
 
 // Per-thread share of a tile gather: (4-key group, 16-byte chunk) pairs.
+// Keys at or past kv_len are clamped to the last key, so every load is in
+// bounds and branch-free: such keys are masked to probability exactly 0, and
+// the V rows they read are finite, so they add nothing.  Page-table entries
+// are looked up one tile ahead of the K/V loads that use them (pages()), so
+// the dependent page-table -> cache load chain never stalls a tile.
 template <int D, int NT>
 struct KvTile {
   static constexpr int CH = D / 8;
@@ -29,9 +34,30 @@ struct KvTile {
   u32x4 kreg[PPT][4];
   u32x4 vreg[PPT][4];
 
-  // Gathers keys [64*kt, 64*kt + 64) of one K/V head; keys >= kv_len read as
-  // zero and touch neither the page table nor the cache.
-  __device__ __forceinline__ void load(const uint16_t *kbase, const uint16_t *vbase, const int32_t *pt,
+  struct Pages {
+    int32_t id[PPT][4];
+  };
+
+  // Page of each key this thread gathers for tile kt (one per 4-key group
+  // when pages hold at least 4 keys).
+  __device__ __forceinline__ Pages pages(const int32_t *pt, int page_shift, int kt, int kv_len, int tid) const {
+    Pages pg;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pair = tid + i * NT;
+      const int kg = (PAIRS % NT == 0 || pair < PAIRS ? pair : 0) / CH;
+      const int key0 = kt * 64 + 4 * kg;
+      if (page_shift >= 2) {
+        pg.id[i][0] = pt[min(key0, kv_len - 1) >> page_shift];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pg.id[i][j] = pt[min(key0 + j, kv_len - 1) >> page_shift];
+      }
+    }
+    return pg;
+  }
+
+  __device__ __forceinline__ void load(const uint16_t *kbase, const uint16_t *vbase, const Pages &pg,
                                        int page_shift, int64_t s_page, int64_t s_slot, int kt, int kv_len,
                                        int tid) {
     const int pmask = (1 << page_shift) - 1;
@@ -41,38 +67,17 @@ struct KvTile {
       if (PAIRS % NT == 0 || pair < PAIRS) {
         const int kg = pair / CH, c = pair % CH;
         const int key0 = kt * 64 + 4 * kg;
-        if (page_shift >= 2) {  // the 4 keys share a page
-          const int32_t page = key0 < kv_len ? pt[key0 >> page_shift] : 0;
-          const int64_t base = (int64_t)page * s_page + (int64_t)(key0 & pmask) * s_slot + 8 * c;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (key0 + j < kv_len) {
-              kreg[i][j] = *(const u32x4 *)(kbase + base + j * s_slot);
-              vreg[i][j] = *(const u32x4 *)(vbase + base + j * s_slot);
-            } else {
-              kreg[i][j] = u32x4{0, 0, 0, 0};
-              vreg[i][j] = u32x4{0, 0, 0, 0};
-            }
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = key0 + j;
-            if (key < kv_len) {
-              const int32_t page = pt[key >> page_shift];
-              const int64_t off = (int64_t)page * s_page + (int64_t)(key & pmask) * s_slot + 8 * c;
-              kreg[i][j] = *(const u32x4 *)(kbase + off);
-              vreg[i][j] = *(const u32x4 *)(vbase + off);
-            } else {
-              kreg[i][j] = u32x4{0, 0, 0, 0};
-              vreg[i][j] = u32x4{0, 0, 0, 0};
-            }
-          }
+        for (int j = 0; j < 4; ++j) {
+          const int key = min(key0 + j, kv_len - 1);
+          const int32_t page = page_shift >= 2 ? pg.id[i][0] : pg.id[i][j];
+          const int64_t off = (int64_t)page * s_page + (int64_t)(key & pmask) * s_slot + 8 * c;
+          kreg[i][j] = *(const u32x4 *)(kbase + off);
+          vreg[i][j] = *(const u32x4 *)(vbase + off);
         }
       }
     }
   }
-
   __device__ __forceinline__ void store(uint16_t *stage, int tid) const {
     uint16_t *Ks = stage;
     uint16_t *Vt = stage + 64 * Stage<D>::KS;
@@ -108,45 +113,68 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 16], const uint16_t *qro
 }
 
 // S^T for keys [0, 64) of the staged tile and the wave's 32 query rows.
+// The operand reads of both 32-key blocks are issued before the products
+// (sched_barrier keeps the compiler from sinking each read onto its use), so
+// LDS latency overlaps the matrix cores instead of preceding every product.
 template <int D>
 __device__ __forceinline__ void qk_tile(const uint16_t *stage, const bf16x8 (&qf)[D / 16], f32x16 (&s)[2],
                                         int l32, int hi) {
-  s[0] = f32x16{};
-  s[1] = f32x16{};
+  // d <= 128: both blocks' operands (<= 64 registers) up front; d = 256: one
+  // block at a time to stay inside the register file.
+  constexpr int KB_AHEAD = D <= 128 ? 2 : 1;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb0 = 0; kb0 < 2; kb0 += KB_AHEAD) {
+    bf16x8 a[KB_AHEAD][D / 16];
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) {
-      const bf16x8 a = __builtin_bit_cast(
-          bf16x8, *(const u32x4 *)(stage + (32 * kb + l32) * Stage<D>::KS + 16 * k + 8 * hi));
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k], s[kb], 0, 0, 0);
+    for (int j = 0; j < KB_AHEAD; ++j) {
+      const uint16_t *row = stage + (32 * (kb0 + j) + l32) * Stage<D>::KS + 8 * hi;
+#pragma unroll
+      for (int k = 0; k < D / 16; ++k) a[j][k] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(row + 16 * k));
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < KB_AHEAD; ++j) {
+      s[kb0 + j] = f32x16{};
+#pragma unroll
+      for (int k = 0; k < D / 16; ++k)
+        s[kb0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][k], qf[k], s[kb0 + j], 0, 0, 0);
+    }
+  }
 }
 
 // O^T += V^T P^T.  P leaves the S^T accumulator as the B operand: product u
 // takes registers 8 (u % 2) .. + 7 of score block u / 2, i.e. keys
 // 32 (u/2) + 16 (u%2) + 8 (e/4) + 4 (l/32) + e % 4 for element e; the V^T
-// operand reads the same keys (two 8-byte reads per lane).
+// operand reads the same keys (two 8-byte reads per lane).  Operands of
+// product u + 1 are read while product u runs.
+template <int D>
+__device__ __forceinline__ void read_vt(const uint16_t *Vt, bf16x8 (&a)[D / 32], int u, int l32, int hi) {
+  const int koff = 32 * (u >> 1) + 16 * (u & 1) + 4 * hi;
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) {
+    const uint16_t *vr = Vt + (32 * n + l32) * Stage<D>::VS + koff;
+    const u32x2 a0 = *(const u32x2 *)vr;
+    const u32x2 a1 = *(const u32x2 *)(vr + 8);
+    a[n] = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void pv_tile(const uint16_t *stage, const f32x16 (&p)[2], f32x16 (&o)[D / 32],
                                         int l32, int hi) {
   const uint16_t *Vt = stage + 64 * Stage<D>::KS;
+  bf16x8 a[2][D / 32];
+  read_vt<D>(Vt, a[0], 0, l32, hi);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int kb = u >> 1, hh = u & 1;
+    if (u + 1 < 4) read_vt<D>(Vt, a[(u + 1) & 1], u + 1, l32, hi);
     f32x8 pv;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) pv[x] = p[kb][8 * hh + x];
+    for (int x = 0; x < 8; ++x) pv[x] = p[u >> 1][8 * (u & 1) + x];
     const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
-    const int koff = 32 * kb + 16 * hh + 4 * hi;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n) {
-      const uint16_t *vr = Vt + (32 * n + l32) * Stage<D>::VS + koff;
-      const u32x2 a0 = *(const u32x2 *)vr;
-      const u32x2 a1 = *(const u32x2 *)(vr + 8);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
-      o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[n], 0, 0, 0);
-    }
+    for (int n = 0; n < D / 32; ++n) o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u & 1][n], pb, o[n], 0, 0, 0);
   }
 }
 
@@ -167,32 +195,52 @@ __device__ __forceinline__ void apply_word(f32x16 (&s)[2], uint64_t word, int hi
   }
 }
 
-// Online-softmax update for one tile (scores -> probabilities).  Returns the
-// factor the O accumulator is rescaled by.  Rows with no visible key so far
-// keep m = -inf and produce zeros.
-__device__ __forceinline__ float softmax_tile(f32x16 (&s)[2], float &m_run, float &l_run, float c) {
-  float mx = s[0][0];
+// Both 32-lane halves of a wave hold the same 32 query rows (other keys):
+// combine a per-lane value with its partner lane l ^ 32.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Online softmax in the log2 domain with a lazily raised reference.
+// m_ref (scaled by scale * log2 e) only moves when a tile's row max exceeds
+// it by more than kRescaleSlack; until then probabilities are exp2(s c -
+// m_ref) <= 2^kRescaleSlack and the accumulators keep their scale.  The
+// result is unchanged (O and l share the reference), and most tiles skip the
+// O rescale.  Returns true when some row of the wave changed its reference;
+// alpha is then that row's rescale factor (1 for the others).
+constexpr float kRescaleSlack = 8.f;
+
+__device__ __forceinline__ bool softmax_tile(f32x16 (&s)[2], float &m_ref, float &l_run, float c, float &alpha) {
+  float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+  for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-  mx = fmaxf(mx, lane_swap32(mx));
-  const float m_new = fmaxf(m_run, mx);
-  const float m_use = m_new == neg_inf() ? 0.f : m_new;
-  const float alpha = fast_exp2((m_run - m_use) * c);
-  const float mc = m_use * c;
-  float psum = 0.f;
+  const float mxc = max_halves(mx) * c;
+  const bool raise = mxc > m_ref + kRescaleSlack;
+  alpha = 1.f;
+  if (raise) {
+    alpha = fast_exp2(m_ref - mxc);   // 0 when m_ref is still -inf
+    m_ref = mxc;
+  }
+  const bool any = __builtin_amdgcn_ballot_w64(raise) != 0ull;
+  const float mu = m_ref == neg_inf() ? 0.f : m_ref;
+  float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float pv = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
+      const float pv = fast_exp2(__builtin_fmaf(s[kb][r], c, -mu));
       s[kb][r] = pv;
-      psum += pv;
+      ps[r & 3] += pv;
     }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-  return alpha;
+  l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+  return any;
 }
 
 template <typename OutT>

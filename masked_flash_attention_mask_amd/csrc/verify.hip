@@ -129,18 +129,22 @@ __global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
   const uint16_t *kbase = (const uint16_t *)p.k + (int64_t)g * p.s_head;
   const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)g * p.s_head;
   const int32_t *pt = p.page_table + (int64_t)b * p.max_pages;
-  KvTile<D, NT> kvt;
+  using KV = KvTile<D, NT>;
+  KV kvt;
+  typename KV::Pages pg_nxt;
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
-  float m_run = neg_inf(), l_run = 0.f;
+  float m_ref = neg_inf(), l_run = 0.f;
   const float c = p.scale_log2;
 
   uint64_t word_nxt = 0;
   if (kt0 < kt1) {
-    kvt.load(kbase, vbase, pt, p.page_shift, p.s_page, p.s_slot, kt0, kv, tid);
+    const typename KV::Pages pg0 = kvt.pages(pt, p.page_shift, kt0, kv, tid);
+    kvt.load(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv, tid);
     word_nxt = fetch_word(p, moff, row_base, q_len, kv, kt0, lane);
+    if (kt0 + 1 < kt1) pg_nxt = kvt.pages(pt, p.page_shift, kt0 + 1, kv, tid);
     kvt.store(lds, tid);
     __syncthreads();
   }
@@ -149,27 +153,32 @@ __global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
     const uint64_t wcur = word_nxt;
     const bool has_next = kt + 1 < kt1;
     if (has_next) {
-      kvt.load(kbase, vbase, pt, p.page_shift, p.s_page, p.s_slot, kt + 1, kv, tid);
+      kvt.load(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, kt + 1, kv, tid);
       word_nxt = fetch_word(p, moff, row_base, q_len, kv, kt + 1, lane);
+      if (kt + 2 < kt1) pg_nxt = kvt.pages(pt, p.page_shift, kt + 2, kv, tid);
     }
     const uint16_t *stage = lds + cur * Stage<D>::ELEMS;
     f32x16 sacc[2];
     qk_tile<D>(stage, qf, sacc, l32, hi);
-    const uint64_t inb = low_bits(kv - 64 * kt);
+    const int kin = kv - 64 * kt;
+    const uint64_t inb = low_bits(kin);
     const uint64_t w = wcur & inb;
-    // Per-wave class: skip the bit tests when every valid row sees the tile.
-    if (__ballot(row_ok && w != inb) != 0ull) apply_word(sacc, w, hi);
-    const float alpha = softmax_tile(sacc, m_run, l_run, c);
+    // Per-wave class: skip the bit tests when every valid row sees the whole
+    // tile (keys past kv_len are always masked).
+    if (kin < 64 || __ballot(row_ok && w != inb) != 0ull) apply_word(sacc, w, hi);
+    float alpha;
+    if (softmax_tile(sacc, m_ref, l_run, c, alpha)) {
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+      for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+    }
     pv_tile<D>(stage, sacc, oacc, l32, hi);
     if (has_next) kvt.store(lds + (cur ^ 1) * Stage<D>::ELEMS, tid);
     __syncthreads();
   }
 
-  const float lt = l_run + lane_swap32(l_run);
+  const float lt = sum_halves(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const float lse = lt > 0.f ? m_run * p.scale + __logf(lt) : neg_inf();
+  const float lse = lt > 0.f ? (m_ref + __log2f(lt)) * kLn2 : neg_inf();
   if (!row_ok) return;
   if (nsplit <= 1) {
     store_row<D, OutT>((OutT *)p.out + (tok * p.hq + h) * D, oacc, inv, hi);

@@ -6,37 +6,16 @@ import torch
 
 import masked_flash_attention_mask_amd as ma
 from oracle import attention as OA
+from workloads.device import device_inputs, plan_kwargs  # noqa: F401
 from oracle import masks as OM
 
 TOL_F32 = 1e-5      # fp32 inputs, fp32 accumulation
 TOL_BF16 = 1.5e-2   # bf16 inputs, fp32 accumulation, fp32 output
 
 
-def device_inputs(w, dev="cuda"):
-    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
-    return {
-        "q": torch.from_numpy(w.q).to(dev).to(dt).contiguous(),
-        "k": torch.from_numpy(w.k_cache).to(dev).to(dt).contiguous(),
-        "v": torch.from_numpy(w.v_cache).to(dev).to(dt).contiguous(),
-        "pt": torch.from_numpy(w.page_table).to(dev).contiguous(),
-        "cu": torch.from_numpy(w.cu_seqlens_q).to(dev).contiguous(),
-        "kv": torch.from_numpy(w.kv_lens).to(dev).contiguous(),
-    }
-
-
 def compile_plan(w, mask_name, tile_q=128, device_mask=True):
-    mi = w.masks[mask_name]
-    kw = {}
-    if mi.kind == "window":
-        kw["window"] = mi.window
-    elif mi.kind == "prefix_lm":
-        kw["prefix_len"] = mi.prefix_len
-    elif mi.kind == "ranges":
-        kw["ranges"] = mi.ranges
-    elif mi.kind in ("dense", "packed"):
-        data = mi.data if mi.kind == "dense" else mi.data.view(np.int64)
-        kw["mask"] = torch.from_numpy(np.ascontiguousarray(data)).cuda() if device_mask else mi.data
-    return ma.mask_compile(mi.kind, w.cu_seqlens_q, w.kv_lens, tile_q=tile_q, **kw)
+    kind, kw = plan_kwargs(w, mask_name, host=not device_mask)
+    return ma.mask_compile(kind, w.cu_seqlens_q, w.kv_lens, tile_q=tile_q, **kw)
 
 
 def run_prefill(w, dev_in, mask_name, tile_q=128, out_dtype=torch.float32, device_mask=True):
