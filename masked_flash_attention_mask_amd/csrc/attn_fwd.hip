@@ -62,11 +62,11 @@ __device__ __forceinline__ void map_block(int b, int num_items, int hq, int &ite
   }
 }
 
-// m_ref is the softmax reference in log2 units (scale * log2 e applied).
+// m_ref is the softmax reference in log2 units (scale * log2 e applied); lt
+// is the row's sum of probabilities relative to it.
 template <int D, typename OutT>
 __device__ __forceinline__ void epilogue(const PrefillParams &p, const f32x16 (&o)[D / 32], float m_ref,
-                                         float l_run, int64_t tok, int h, bool row_ok, int hi) {
-  const float lt = sum_halves(l_run);
+                                         float lt, int64_t tok, int h, bool row_ok, int hi) {
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (!row_ok) return;
   store_row<D, OutT>((OutT *)p.out + (tok * p.hq + h) * D, o, inv, hi);
@@ -119,7 +119,8 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
-  float m_ref = neg_inf(), l_run = 0.f;
+  float m_ref = neg_inf();
+  f32x16 lsum = f32x16{};
   const float c = p.scale_log2;
 
   const int eb = it.ent_begin, ee = it.ent_end;
@@ -156,15 +157,16 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
       apply_word(sacc, (cls == MA_TILE_PARTIAL ? wcur : ~0ull) & low_bits(kin), hi);
 
     float alpha;
-    if (softmax_tile(sacc, m_ref, l_run, c, alpha)) {
+    if (softmax_tile(sacc, m_ref, c, alpha)) {
 #pragma unroll
       for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+      lsum *= alpha;
     }
-    pv_tile<D>(stage, sacc, oacc, l32, hi);
+    pv_tile<D>(stage, sacc, oacc, lsum, l32, hi);
     if (has_next) kv.store(lds + (cur ^ 1) * Stage<D>::ELEMS, tid);
     __syncthreads();
   }
-  epilogue<D, OutT>(p, oacc, m_ref, l_run, tok, h, row_ok, hi);
+  epilogue<D, OutT>(p, oacc, m_ref, lsum[0], tok, h, row_ok, hi);
 }
 
 // ---------------------------------------------------------------------------
@@ -250,7 +252,12 @@ __global__ __launch_bounds__(BQ * 2, 1) void prefill_f32_kernel(PrefillParams p)
     const int kin = kv_len - kt * 64;
     if (cls == MA_TILE_PARTIAL || kin < 64) apply_word(sacc, word & low_bits(kin), hi);
     float alpha;
-    if (softmax_tile(sacc, m_ref, l_run, c, alpha)) {
+    const bool any = softmax_tile(sacc, m_ref, c, alpha);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ps += sacc[0][r] + sacc[1][r];
+    l_run = l_run * alpha + ps;
+    if (any) {
 #pragma unroll
       for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
     }
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(BQ * 2, 1) void prefill_f32_kernel(PrefillParams p)
                                                          0, 0, 0);
       }
   }
-  epilogue<D, float>(p, oacc, m_ref, l_run, tok, h, row_ok, hi);
+  epilogue<D, float>(p, oacc, m_ref, sum_halves(l_run), tok, h, row_ok, hi);
 }
 
 template <typename K>

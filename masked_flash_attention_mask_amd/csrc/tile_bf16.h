@@ -9,14 +9,18 @@
 namespace maskattn {
 namespace dev {
 
-// LDS stage of one 64-key tile: K row-major [64][D + 8] and V transposed
-// [D][64 + 4] (bf16 elements).  The pads spread the matrix-core operand reads
-// of 32 rows over all banks.
+// LDS stage of one 64-key tile: K and V both row-major (bf16).  K rows are
+// padded to D + 8 elements (a row stride of 4 banks modulo 64) so the 16 rows
+// of one ds_read_b128 operand load hit distinct banks.  V rows are padded to
+// D + 32 elements (16 banks modulo 64) so the 4 rows x 32 bytes a 16-lane
+// group reads with ds_read_b64_tr_b16 hit distinct banks.  Row-wise gather
+// writes (16 lanes fill one row) are conflict-free for both.
 template <int D>
 struct Stage {
   static constexpr int KS = D + 8;
-  static constexpr int VS = 64 + 4;
-  static constexpr int ELEMS = 64 * KS + D * VS;
+  static constexpr int VS = D + 32;
+  static constexpr int V_OFF = 64 * KS;  // elements
+  static constexpr int ELEMS = 64 * KS + 64 * VS;
   static constexpr size_t BYTES = ELEMS * sizeof(uint16_t);
 };
 
@@ -61,6 +65,24 @@ struct KvTile {
                                        int page_shift, int64_t s_page, int64_t s_slot, int kt, int kv_len,
                                        int tid) {
     const int pmask = (1 << page_shift) - 1;
+    if (page_shift >= 2 && (kt + 1) * 64 <= kv_len) {
+      // Interior tile: the 4 keys of a group are consecutive slots of one page.
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        const int pair = tid + i * NT;
+        if (PAIRS % NT == 0 || pair < PAIRS) {
+          const int kg = pair / CH, c = pair % CH;
+          const int key0 = kt * 64 + 4 * kg;
+          const int64_t off0 = (int64_t)pg.id[i][0] * s_page + (int64_t)(key0 & pmask) * s_slot + 8 * c;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            kreg[i][j] = *(const u32x4 *)(kbase + off0 + j * s_slot);
+            vreg[i][j] = *(const u32x4 *)(vbase + off0 + j * s_slot);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int pair = tid + i * NT;
@@ -79,23 +101,16 @@ struct KvTile {
     }
   }
   __device__ __forceinline__ void store(uint16_t *stage, int tid) const {
-    uint16_t *Ks = stage;
-    uint16_t *Vt = stage + 64 * Stage<D>::KS;
+    uint16_t *Vs = stage + Stage<D>::V_OFF;
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int pair = tid + i * NT;
       if (PAIRS % NT == 0 || pair < PAIRS) {
         const int kg = pair / CH, c = pair % CH;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *(u32x4 *)(Ks + (4 * kg + j) * Stage<D>::KS + 8 * c) = kreg[i][j];
-        // V^T rows are head-dim indices; 4 consecutive keys per 8-byte store.
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t a0 = vreg[i][0][m], a1 = vreg[i][1][m], a2 = vreg[i][2][m], a3 = vreg[i][3][m];
-          const u32x2 lo = {perm_b32(a1, a0, 0x05040100u), perm_b32(a3, a2, 0x05040100u)};
-          const u32x2 hv = {perm_b32(a1, a0, 0x07060302u), perm_b32(a3, a2, 0x07060302u)};
-          *(u32x2 *)(Vt + (8 * c + 2 * m) * Stage<D>::VS + 4 * kg) = lo;
-          *(u32x2 *)(Vt + (8 * c + 2 * m + 1) * Stage<D>::VS + 4 * kg) = hv;
+        for (int j = 0; j < 4; ++j) {
+          *(u32x4 *)(stage + (4 * kg + j) * Stage<D>::KS + 8 * c) = kreg[i][j];
+          *(u32x4 *)(Vs + (4 * kg + j) * Stage<D>::VS + 8 * c) = vreg[i][j];
         }
       }
     }
@@ -144,30 +159,46 @@ __device__ __forceinline__ void qk_tile(const uint16_t *stage, const bf16x8 (&qf
 
 // O^T += V^T P^T.  P leaves the S^T accumulator as the B operand: product u
 // takes registers 8 (u % 2) .. + 7 of score block u / 2, i.e. keys
-// 32 (u/2) + 16 (u%2) + 8 (e/4) + 4 (l/32) + e % 4 for element e; the V^T
-// operand reads the same keys (two 8-byte reads per lane).  Operands of
-// product u + 1 are read while product u runs.
+// base + 8 (e/4) + 4 (l/32) + e % 4 for element e, base = 32 (u/2) + 16 (u%2).
+// The V^T operand is read straight from row-major V with ds_read_b64_tr_b16:
+// inside each 16-lane group, lane i receives element i % 4 of the 8 bytes
+// addressed by lane 4 j + i / 4, as its element j.  Lane 4 j + q addressing
+// V[k0 + j][d0 + 4 q .. + 3] therefore hands lane i the keys k0 .. k0 + 3 of
+// head-dim d0 + i; two such reads (k0 = base + 4 (l/32) and base + 8 +
+// 4 (l/32), d0 = 32 n + 16 (l/16 % 2)) form the lane's 8 operand elements.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
 template <int D>
-__device__ __forceinline__ void read_vt(const uint16_t *Vt, bf16x8 (&a)[D / 32], int u, int l32, int hi) {
-  const int koff = 32 * (u >> 1) + 16 * (u & 1) + 4 * hi;
+__device__ __forceinline__ void read_vt(const uint16_t *vlane, bf16x8 (&a)[D / 32], int u) {
+  // vlane = V + (4 (lane / 32) + (lane % 16) / 4) * VS + 16 ((lane / 16) % 2) + 4 (lane % 4)
+  const uint16_t *p = vlane + (32 * (u >> 1) + 16 * (u & 1)) * Stage<D>::VS;
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) {
-    const uint16_t *vr = Vt + (32 * n + l32) * Stage<D>::VS + koff;
-    const u32x2 a0 = *(const u32x2 *)vr;
-    const u32x2 a1 = *(const u32x2 *)(vr + 8);
-    a[n] = __builtin_bit_cast(bf16x8, u32x4{a0[0], a0[1], a1[0], a1[1]});
+    const i16x4 r0 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p + 32 * n));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(p + 8 * Stage<D>::VS + 32 * n));
+    const i16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    a[n] = __builtin_bit_cast(bf16x8, v);
   }
 }
 
+// lsum accumulates, through one more product per 16 keys with an all-ones
+// A operand, the row sums of exactly the bf16 probabilities that enter P V
+// (every register of lsum holds the lane's query-row sum).
 template <int D>
 __device__ __forceinline__ void pv_tile(const uint16_t *stage, const f32x16 (&p)[2], f32x16 (&o)[D / 32],
-                                        int l32, int hi) {
-  const uint16_t *Vt = stage + 64 * Stage<D>::KS;
+                                        f32x16 &lsum, int l32, int hi) {
+  const int lane = 32 * hi + l32;
+  const uint16_t *vlane = stage + Stage<D>::V_OFF + (4 * hi + ((lane & 15) >> 2)) * Stage<D>::VS +
+                          16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   bf16x8 a[2][D / 32];
-  read_vt<D>(Vt, a[0], 0, l32, hi);
+  read_vt<D>(vlane, a[0], 0);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    if (u + 1 < 4) read_vt<D>(Vt, a[(u + 1) & 1], u + 1, l32, hi);
+    if (u + 1 < 4) read_vt<D>(vlane, a[(u + 1) & 1], u + 1);
     f32x8 pv;
 #pragma unroll
     for (int x = 0; x < 8; ++x) pv[x] = p[u >> 1][8 * (u & 1) + x];
@@ -175,6 +206,7 @@ __device__ __forceinline__ void pv_tile(const uint16_t *stage, const f32x16 (&p)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u & 1][n], pb, o[n], 0, 0, 0);
+    lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb, lsum, 0, 0, 0);
   }
 }
 
@@ -210,12 +242,12 @@ __device__ __forceinline__ float sum_halves(float x) {
 // m_ref (scaled by scale * log2 e) only moves when a tile's row max exceeds
 // it by more than kRescaleSlack; until then probabilities are exp2(s c -
 // m_ref) <= 2^kRescaleSlack and the accumulators keep their scale.  The
-// result is unchanged (O and l share the reference), and most tiles skip the
-// O rescale.  Returns true when some row of the wave changed its reference;
-// alpha is then that row's rescale factor (1 for the others).
+// result is unchanged (O and its normaliser share the reference), and most
+// tiles skip the rescale.  Returns true when some row of the wave changed
+// its reference; alpha is then that row's rescale factor (1 for the others).
 constexpr float kRescaleSlack = 8.f;
 
-__device__ __forceinline__ bool softmax_tile(f32x16 (&s)[2], float &m_ref, float &l_run, float c, float &alpha) {
+__device__ __forceinline__ bool softmax_tile(f32x16 (&s)[2], float &m_ref, float c, float &alpha) {
   float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
   for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
@@ -230,16 +262,10 @@ __device__ __forceinline__ bool softmax_tile(f32x16 (&s)[2], float &m_ref, float
   }
   const bool any = __builtin_amdgcn_ballot_w64(raise) != 0ull;
   const float mu = m_ref == neg_inf() ? 0.f : m_ref;
-  float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pv = fast_exp2(__builtin_fmaf(s[kb][r], c, -mu));
-      s[kb][r] = pv;
-      ps[r & 3] += pv;
-    }
-  l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -mu));
   return any;
 }
 

@@ -136,7 +136,8 @@ __global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
-  float m_ref = neg_inf(), l_run = 0.f;
+  float m_ref = neg_inf();
+  f32x16 lsum = f32x16{};
   const float c = p.scale_log2;
 
   uint64_t word_nxt = 0;
@@ -167,16 +168,17 @@ __global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
     // tile (keys past kv_len are always masked).
     if (kin < 64 || __ballot(row_ok && w != inb) != 0ull) apply_word(sacc, w, hi);
     float alpha;
-    if (softmax_tile(sacc, m_ref, l_run, c, alpha)) {
+    if (softmax_tile(sacc, m_ref, c, alpha)) {
 #pragma unroll
       for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+      lsum *= alpha;
     }
-    pv_tile<D>(stage, sacc, oacc, l32, hi);
+    pv_tile<D>(stage, sacc, oacc, lsum, l32, hi);
     if (has_next) kvt.store(lds + (cur ^ 1) * Stage<D>::ELEMS, tid);
     __syncthreads();
   }
 
-  const float lt = sum_halves(l_run);
+  const float lt = lsum[0];
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse = lt > 0.f ? (m_ref + __log2f(lt)) * kLn2 : neg_inf();
   if (!row_ok) return;
