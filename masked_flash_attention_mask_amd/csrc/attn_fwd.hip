@@ -135,18 +135,28 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
     kv.store(lds, tid);
     __syncthreads();
   }
+  // d = 256 stages K and V of the next tile one after the other (K during
+  // Q K^T and the softmax, V during P V) to halve the staging registers.
+  constexpr bool kSplit = D == 256;
   for (int e = eb; e < ee; ++e) {
     const int cur = (e - eb) & 1;
     const Entry ec = p.entries[e];
     const uint64_t wcur = word_nxt;
     const bool has_next = e + 1 < ee;
+    int kt_next = 0;
+    typename KV::Pages pg_use = pg_nxt;
     if (has_next) {
       const Entry en = p.entries[e + 1];
-      kv.load(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, entry_kt(en.kt_cls), kv_len, tid);
+      kt_next = entry_kt(en.kt_cls);
+      if (kSplit)
+        kv.load_one(kbase, pg_use, p.page_shift, p.s_page, p.s_slot, kt_next, kv_len, tid);
+      else
+        kv.load(kbase, vbase, pg_use, p.page_shift, p.s_page, p.s_slot, kt_next, kv_len, tid);
       word_nxt = load_word(en);
       if (e + 2 < ee) pg_nxt = kv.pages(pt, p.page_shift, entry_kt(p.entries[e + 2].kt_cls), kv_len, tid);
     }
     const uint16_t *stage = lds + cur * Stage<D>::ELEMS;
+    uint16_t *next = lds + (cur ^ 1) * Stage<D>::ELEMS;
     f32x16 sacc[2];
     qk_tile<D>(stage, qf, sacc, l32, hi);
 
@@ -162,8 +172,17 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
       for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
       lsum *= alpha;
     }
+    if (kSplit && has_next) {
+      kv.store_one(next, Stage<D>::KS, tid);
+      kv.load_one(vbase, pg_use, p.page_shift, p.s_page, p.s_slot, kt_next, kv_len, tid);
+    }
     pv_tile<D>(stage, sacc, oacc, lsum, l32, hi);
-    if (has_next) kv.store(lds + (cur ^ 1) * Stage<D>::ELEMS, tid);
+    if (has_next) {
+      if (kSplit)
+        kv.store_one(next + Stage<D>::V_OFF, Stage<D>::VS, tid);
+      else
+        kv.store(next, tid);
+    }
     __syncthreads();
   }
   epilogue<D, OutT>(p, oacc, m_ref, lsum[0], tok, h, row_ok, hi);

@@ -100,6 +100,46 @@ struct KvTile {
       }
     }
   }
+  // Split gather for tight register budgets: K and V staged one after the
+  // other through the same registers (kreg).
+  __device__ __forceinline__ void load_one(const uint16_t *base, const Pages &pg, int page_shift, int64_t s_page,
+                                           int64_t s_slot, int kt, int kv_len, int tid) {
+    const int pmask = (1 << page_shift) - 1;
+    const bool interior = page_shift >= 2 && (kt + 1) * 64 <= kv_len;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pair = tid + i * NT;
+      if (PAIRS % NT == 0 || pair < PAIRS) {
+        const int kg = pair / CH, c = pair % CH;
+        const int key0 = kt * 64 + 4 * kg;
+        if (interior) {
+          const int64_t off0 = (int64_t)pg.id[i][0] * s_page + (int64_t)(key0 & pmask) * s_slot + 8 * c;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) kreg[i][j] = *(const u32x4 *)(base + off0 + j * s_slot);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = min(key0 + j, kv_len - 1);
+            const int32_t page = page_shift >= 2 ? pg.id[i][0] : pg.id[i][j];
+            kreg[i][j] = *(const u32x4 *)(base + (int64_t)page * s_page + (int64_t)(key & pmask) * s_slot + 8 * c);
+          }
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store_one(uint16_t *dst, int stride, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pair = tid + i * NT;
+      if (PAIRS % NT == 0 || pair < PAIRS) {
+        const int kg = pair / CH, c = pair % CH;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *(u32x4 *)(dst + (4 * kg + j) * stride + 8 * c) = kreg[i][j];
+      }
+    }
+  }
+
   __device__ __forceinline__ void store(uint16_t *stage, int tid) const {
     uint16_t *Vs = stage + Stage<D>::V_OFF;
 #pragma unroll
@@ -134,25 +174,26 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 16], const uint16_t *qro
 template <int D>
 __device__ __forceinline__ void qk_tile(const uint16_t *stage, const bf16x8 (&qf)[D / 16], f32x16 (&s)[2],
                                         int l32, int hi) {
-  // d <= 128: both blocks' operands (<= 64 registers) up front; d = 256: one
-  // block at a time to stay inside the register file.
-  constexpr int KB_AHEAD = D <= 128 ? 2 : 1;
+  // Operands read ahead per group of products: both 32-key blocks (64
+  // registers) for d <= 128; half a block (32 registers) for d = 256, whose
+  // accumulators already fill most of the register file.
+  constexpr int GROUP = D <= 128 ? 2 * (D / 16) : 8;
+  constexpr int NG = 2 * (D / 16) / GROUP;
 #pragma unroll
-  for (int kb0 = 0; kb0 < 2; kb0 += KB_AHEAD) {
-    bf16x8 a[KB_AHEAD][D / 16];
+  for (int gi = 0; gi < NG; ++gi) {
+    bf16x8 a[GROUP];
 #pragma unroll
-    for (int j = 0; j < KB_AHEAD; ++j) {
-      const uint16_t *row = stage + (32 * (kb0 + j) + l32) * Stage<D>::KS + 8 * hi;
-#pragma unroll
-      for (int k = 0; k < D / 16; ++k) a[j][k] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(row + 16 * k));
+    for (int x = 0; x < GROUP; ++x) {
+      const int idx = gi * GROUP + x, kb = idx / (D / 16), k = idx % (D / 16);
+      a[x] = __builtin_bit_cast(bf16x8,
+                                *(const u32x4 *)(stage + (32 * kb + l32) * Stage<D>::KS + 8 * hi + 16 * k));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < KB_AHEAD; ++j) {
-      s[kb0 + j] = f32x16{};
-#pragma unroll
-      for (int k = 0; k < D / 16; ++k)
-        s[kb0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][k], qf[k], s[kb0 + j], 0, 0, 0);
+    for (int x = 0; x < GROUP; ++x) {
+      const int idx = gi * GROUP + x, kb = idx / (D / 16), k = idx % (D / 16);
+      if (k == 0) s[kb] = f32x16{};
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], qf[k], s[kb], 0, 0, 0);
     }
   }
 }
@@ -194,18 +235,22 @@ __device__ __forceinline__ void pv_tile(const uint16_t *stage, const f32x16 (&p)
   const uint16_t *vlane = stage + Stage<D>::V_OFF + (4 * hi + ((lane & 15) >> 2)) * Stage<D>::VS +
                           16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-  bf16x8 a[2][D / 32];
-  read_vt<D>(vlane, a[0], 0);
+  // V^T operands of product u + 1 are read while product u runs (d <= 128);
+  // d = 256 reads each product's operands just before it (register budget).
+  constexpr int NB = D <= 128 ? 2 : 1;
+  bf16x8 a[NB][D / 32];
+  if (NB == 2) read_vt<D>(vlane, a[0], 0);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    if (u + 1 < 4) read_vt<D>(vlane, a[(u + 1) & 1], u + 1);
+    if (NB == 2 && u + 1 < 4) read_vt<D>(vlane, a[(u + 1) % NB], u + 1);
+    if (NB == 1) read_vt<D>(vlane, a[0], u);
     f32x8 pv;
 #pragma unroll
     for (int x = 0; x < 8; ++x) pv[x] = p[u >> 1][8 * (u & 1) + x];
     const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n) o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u & 1][n], pb, o[n], 0, 0, 0);
+    for (int n = 0; n < D / 32; ++n) o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u % NB][n], pb, o[n], 0, 0, 0);
     lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb, lsum, 0, 0, 0);
   }
 }
