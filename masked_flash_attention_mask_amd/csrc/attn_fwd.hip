@@ -25,6 +25,7 @@
 
 namespace maskattn {
 using namespace dev;
+using namespace dev::staged;
 
 namespace {
 

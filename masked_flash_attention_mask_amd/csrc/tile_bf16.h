@@ -1,6 +1,6 @@
-// bf16 tile machinery shared by the prefill and tree-verify kernels: paged
-// K/V gather of one 64-key tile into registers, the LDS stage layout, and the
-// two matrix-core products of a wave's 32 query rows against a staged tile.
+// bf16 tile machinery of the prefill kernel: paged K/V gathered through
+// registers (one tile ahead) into the padded LDS stage layout, and the two
+// matrix-core products of a wave's 32 query rows against a staged tile.
 #pragma once
 
 #include "internal.h"
@@ -8,6 +8,7 @@
 
 namespace maskattn {
 namespace dev {
+namespace staged {
 
 // LDS stage of one 64-key tile: K and V both row-major (bf16).  K rows are
 // padded to D + 8 elements (a row stride of 4 banks modulo 64) so the 16 rows
@@ -157,16 +158,6 @@ struct KvTile {
   }
 };
 
-// Q rows as B operands: lane l holds Q[row][16 s + 8 (l / 32) .. + 7].
-template <int D>
-__device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 16], const uint16_t *qrow, bool ok, int hi) {
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const u32x4 raw = ok ? *(const u32x4 *)(qrow + 16 * s + 8 * hi) : u32x4{0, 0, 0, 0};
-    qf[s] = __builtin_bit_cast(bf16x8, raw);
-  }
-}
-
 // S^T for keys [0, 64) of the staged tile and the wave's 32 query rows.
 // The operand reads of both 32-key blocks are issued before the products
 // (sched_barrier keeps the compiler from sinking each read onto its use), so
@@ -207,8 +198,6 @@ __device__ __forceinline__ void qk_tile(const uint16_t *stage, const bf16x8 (&qf
 // V[k0 + j][d0 + 4 q .. + 3] therefore hands lane i the keys k0 .. k0 + 3 of
 // head-dim d0 + i; two such reads (k0 = base + 4 (l/32) and base + 8 +
 // 4 (l/32), d0 = 32 n + 16 (l/16 % 2)) form the lane's 8 operand elements.
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
 template <int D>
 __device__ __forceinline__ void read_vt(const uint16_t *vlane, bf16x8 (&a)[D / 32], int u) {
   // vlane = V + (4 (lane / 32) + (lane % 16) / 4) * VS + 16 ((lane / 16) % 2) + 4 (lane % 4)
@@ -255,91 +244,6 @@ __device__ __forceinline__ void pv_tile(const uint16_t *stage, const f32x16 (&p)
   }
 }
 
-__device__ __forceinline__ uint64_t low_bits(int n) {  // n in [0, 64]
-  return n >= 64 ? ~0ull : (n <= 0 ? 0ull : ((1ull << n) - 1ull));
-}
-
-// Masks the two 32-key score blocks of a lane with its row's tile word.
-// Score (kb, r) of lane l is key 32 kb + 8 (r / 4) + 4 (l / 32) + r % 4.
-__device__ __forceinline__ void apply_word(f32x16 (&s)[2], uint64_t word, int hi) {
-  const uint64_t ws = word >> (4 * hi);
-  const uint32_t w0 = (uint32_t)ws, w1 = (uint32_t)(ws >> 32);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int bit = 8 * (r >> 2) + (r & 3);
-    if (!((w0 >> bit) & 1u)) s[0][r] = neg_inf();
-    if (!((w1 >> bit) & 1u)) s[1][r] = neg_inf();
-  }
-}
-
-// Both 32-lane halves of a wave hold the same 32 query rows (other keys):
-// combine a per-lane value with its partner lane l ^ 32.
-__device__ __forceinline__ float max_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Online softmax in the log2 domain with a lazily raised reference.
-// m_ref (scaled by scale * log2 e) only moves when a tile's row max exceeds
-// it by more than kRescaleSlack; until then probabilities are exp2(s c -
-// m_ref) <= 2^kRescaleSlack and the accumulators keep their scale.  The
-// result is unchanged (O and its normaliser share the reference), and most
-// tiles skip the rescale.  Returns true when some row of the wave changed
-// its reference; alpha is then that row's rescale factor (1 for the others).
-constexpr float kRescaleSlack = 8.f;
-
-__device__ __forceinline__ bool softmax_tile(f32x16 (&s)[2], float &m_ref, float c, float &alpha) {
-  float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-  for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-  const float mxc = max_halves(mx) * c;
-  const bool raise = mxc > m_ref + kRescaleSlack;
-  alpha = 1.f;
-  if (raise) {
-    alpha = fast_exp2(m_ref - mxc);   // 0 when m_ref is still -inf
-    m_ref = mxc;
-  }
-  const bool any = __builtin_amdgcn_ballot_w64(raise) != 0ull;
-  const float mu = m_ref == neg_inf() ? 0.f : m_ref;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -mu));
-  return any;
-}
-
-template <typename OutT>
-__device__ __forceinline__ void store4(OutT *dst, float a, float b, float c, float d);
-
-template <>
-__device__ __forceinline__ void store4<float>(float *dst, float a, float b, float c, float d) {
-  *(f32x4 *)dst = f32x4{a, b, c, d};
-}
-
-template <>
-__device__ __forceinline__ void store4<uint16_t>(uint16_t *dst, float a, float b, float c, float d) {
-  *(u32x2 *)dst = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
-}
-
-// Writes a lane's normalised output row slice (O^T register layout: register
-// r of block n is head-dim 32 n + 8 (r / 4) + 4 (l / 32) + r % 4).
-template <int D, typename OutT>
-__device__ __forceinline__ void store_row(OutT *dst, const f32x16 (&o)[D / 32], float inv, int hi) {
-#pragma unroll
-  for (int n = 0; n < D / 32; ++n)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d0 = 32 * n + 8 * r4 + 4 * hi;
-      store4<OutT>(dst + d0, o[n][4 * r4] * inv, o[n][4 * r4 + 1] * inv, o[n][4 * r4 + 2] * inv,
-                   o[n][4 * r4 + 3] * inv);
-    }
-}
-
+}  // namespace staged
 }  // namespace dev
 }  // namespace maskattn

@@ -1,0 +1,192 @@
+// bf16 tile machinery of the tree-verify kernel: paged K/V gathered straight
+// from the cache into LDS (global_load_lds_dwordx4), the swizzled LDS stage
+// layout, and the two matrix-core products of a wave's 32 query rows.
+#pragma once
+
+#include "internal.h"
+#include "kernels_common.h"
+
+namespace maskattn {
+namespace dev {
+namespace dma {
+
+// LDS stage of one 64-key tile: K and V, each [64 keys][D] bf16 without
+// padding, stored as 16-byte chunks whose position inside a row is XOR
+// swizzled by the row (key) index.  The gather writes whole 1 KB runs per
+// wave instruction (global_load_lds_dwordx4), so the swizzle is applied on
+// the source side.  K's swizzle makes the 16 rows x 1 chunk of an operand
+// read (ds_read_b128) hit distinct banks; V's makes the 4 rows x 4 chunks a
+// 16-lane group reads with ds_read_b64_tr_b16 hit distinct banks.
+template <int D>
+struct Stage {
+  static constexpr int CH = D / 8;          // 16-byte chunks per row
+  static constexpr int V_OFF = 64 * D;      // elements
+  static constexpr int ELEMS = 2 * 64 * D;
+  static constexpr size_t BYTES = ELEMS * sizeof(uint16_t);
+  __host__ __device__ static constexpr int fk(int r) { return CH >= 16 ? (r & 15) : ((r >> 1) & 7); }
+  __host__ __device__ static constexpr int fv(int r) { return CH >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+};
+
+// Direct global -> LDS gather of one tile by NW waves: wave instruction t
+// fills LDS chunks [64 t, 64 t + 64) of K (and of V); lane l of it loads the
+// chunk that belongs at position 64 t + l.  Keys at or past kv_len are
+// clamped to the last key, so every load is in bounds: such keys are masked
+// to probability exactly 0 and read finite V, so they add nothing.
+template <int D, int NW>
+struct KvDma {
+  static constexpr int CH = D / 8;
+  static constexpr int IPW = CH / NW;       // instructions per wave per matrix
+  static_assert(CH % NW == 0, "tile gather needs CH to be a multiple of the wave count");
+  struct Pages {
+    int32_t id[IPW];
+  };
+
+  // Page of the key each lane loads in each of its instructions for tile kt.
+  __device__ __forceinline__ static Pages pages(const int32_t *pt, int page_shift, int kt, int kv_len, int wave,
+                                               int lane) {
+    Pages pg;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = (64 * (wave * IPW + i) + lane) / CH;
+      pg.id[i] = pt[min(kt * 64 + r, kv_len - 1) >> page_shift];
+    }
+    return pg;
+  }
+
+  __device__ __forceinline__ static void issue(const uint16_t *kbase, const uint16_t *vbase, const Pages &pg,
+                                               int page_shift, int64_t s_page, int64_t s_slot, int kt,
+                                               int kv_len, uint16_t *stage, int wave, int lane) {
+    const int pmask = (1 << page_shift) - 1;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int t = wave * IPW + i;
+      const int pos = 64 * t + lane;
+      const int r = pos / CH, pc = pos % CH;
+      const int key = min(kt * 64 + r, kv_len - 1);
+      const int64_t off = (int64_t)pg.id[i] * s_page + (int64_t)(key & pmask) * s_slot;
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1))) *)(kbase + off + 8 * (pc ^ Stage<D>::fk(r))),
+          (void __attribute__((address_space(3))) *)(stage + 512 * t), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1))) *)(vbase + off + 8 * (pc ^ Stage<D>::fv(r))),
+          (void __attribute__((address_space(3))) *)(stage + Stage<D>::V_OFF + 512 * t), 16, 0, 0);
+    }
+  }
+};
+
+// Waits for this wave's outstanding global loads (the LDS gathers among them).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Per-lane LDS offsets (elements) of the matrix-core operand reads; the
+// swizzle makes them lane-dependent, so they are computed once per kernel.
+template <int D>
+struct LaneOffsets {
+  static constexpr int NK = D / 16 < 8 ? D / 16 : 8;   // distinct K operand offsets
+  static constexpr int NV = D / 32 < 4 ? D / 32 : 4;   // distinct V operand offsets
+  int k[NK];     // K operand x: chunk (2 x + hi) of row l32 -> in-row element offset
+  int krow;      // l32 * D
+  int v[NV];     // V operand n: chunk 4 n + 2 (g % 2) + q / 2 of row r -> in-row element offset
+  int vrow;      // r * D, r = 4 (lane / 32) + (lane % 16) / 4
+  __device__ __forceinline__ explicit LaneOffsets(int lane) {
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int f = Stage<D>::fk(l32);   // the same for rows l32 and l32 + 32
+#pragma unroll
+    for (int x = 0; x < NK; ++x) k[x] = 8 * ((2 * x + hi) ^ f);
+    krow = l32 * D;
+    const int g = lane >> 4, s = lane & 15, j = s >> 2, q = s & 3;
+    const int r = 4 * (g >> 1) + j;    // row offset from the product's base row (a multiple of 4)
+    const int fvr = Stage<D>::fv(r);   // the same for every base and for base + 8
+#pragma unroll
+    for (int n = 0; n < NV; ++n) v[n] = 8 * ((4 * n + 2 * (g & 1) + (q >> 1)) ^ fvr) + 4 * (q & 1);
+    vrow = r * D;
+  }
+  // K operand element offset of product x (0 .. D/16-1) inside a row: the
+  // swizzle only touches the low 4 chunk bits, so x >= 8 adds 16 chunks.
+  __device__ __forceinline__ int kop(int x) const { return x < 8 ? k[x] : k[x - 8] + 128; }
+  // V operand element offset of d-block n inside a row (n >= 4 adds 16 chunks
+  // per 4 blocks for the same reason).
+  __device__ __forceinline__ int vop(int n) const { return n < 4 ? v[n] : v[n - 4] + 128; }
+};
+
+// S^T = K Q^T for keys [0, 64) of the staged tile and the wave's 32 query
+// rows.  Operands are read in register-budget-sized groups before their
+// products (sched_barrier keeps the compiler from sinking each read onto its
+// use): both 32-key blocks for d <= 128, half a block for d = 256.
+template <int D>
+__device__ __forceinline__ void qk_tile(const uint16_t *stage, const LaneOffsets<D> &lo, const bf16x8 (&qf)[D / 16],
+                                        f32x16 (&s)[2]) {
+  constexpr int GROUP = D <= 128 ? 2 * (D / 16) : 8;
+  constexpr int NG = 2 * (D / 16) / GROUP;
+  const uint16_t *kl = stage + lo.krow;
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    bf16x8 a[GROUP];
+#pragma unroll
+    for (int x = 0; x < GROUP; ++x) {
+      const int idx = gi * GROUP + x, kb = idx / (D / 16), k = idx % (D / 16);
+      a[x] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(kl + 32 * kb * D + lo.kop(k)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < GROUP; ++x) {
+      const int idx = gi * GROUP + x, kb = idx / (D / 16), k = idx % (D / 16);
+      if (k == 0) s[kb] = f32x16{};
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], qf[k], s[kb], 0, 0, 0);
+    }
+  }
+}
+
+// O^T += V^T P^T.  P leaves the S^T accumulator as the B operand: product u
+// takes registers 8 (u % 2) .. + 7 of score block u / 2, i.e. keys
+// base + 8 (e/4) + 4 (l/32) + e % 4 for element e, base = 32 (u/2) + 16 (u%2).
+// The V^T operand is read straight from row-major V with ds_read_b64_tr_b16:
+// inside each 16-lane group, lane i receives element i % 4 of the 8 bytes
+// addressed by lane 4 j + i / 4, as its element j.  Lane 4 j + q addressing
+// V[k0 + j][d0 + 4 q .. + 3] therefore hands lane i the keys k0 .. k0 + 3 of
+// head-dim d0 + i; two such reads (k0 = base + 4 (l/32) and base + 8 +
+// 4 (l/32), d0 = 32 n + 16 (l/16 % 2)) form the lane's 8 operand elements.
+template <int D>
+__device__ __forceinline__ void read_vt(const uint16_t *stage, const LaneOffsets<D> &lo, bf16x8 (&a)[D / 32],
+                                        int u) {
+  const uint16_t *p = stage + Stage<D>::V_OFF + lo.vrow + (32 * (u >> 1) + 16 * (u & 1)) * D;
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) {
+    const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(p + lo.vop(n)));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(p + 8 * D + lo.vop(n)));
+    const i16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    a[n] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// lsum accumulates, through one more product per 16 keys with an all-ones
+// A operand, the row sums of exactly the bf16 probabilities that enter P V
+// (every register of lsum holds the lane's query-row sum).  V^T operands of
+// product u + 1 are read while product u runs (d <= 128); d = 256 reads each
+// product's operands just before it (register budget).
+template <int D>
+__device__ __forceinline__ void pv_tile(const uint16_t *stage, const LaneOffsets<D> &lo, const f32x16 (&p)[2],
+                                        f32x16 (&o)[D / 32], f32x16 &lsum) {
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  constexpr int NB = D <= 128 ? 2 : 1;
+  bf16x8 a[NB][D / 32];
+  if (NB == 2) read_vt<D>(stage, lo, a[0], 0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (NB == 2 && u + 1 < 4) read_vt<D>(stage, lo, a[(u + 1) % NB], u + 1);
+    if (NB == 1) read_vt<D>(stage, lo, a[0], u);
+    f32x8 pv;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) pv[x] = p[u >> 1][8 * (u & 1) + x];
+    const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u % NB][n], pb, o[n], 0, 0, 0);
+    lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb, lsum, 0, 0, 0);
+  }
+}
+
+}  // namespace dma
+}  // namespace dev
+}  // namespace maskattn

@@ -18,10 +18,11 @@
 
 #include "internal.h"
 #include "kernels_common.h"
-#include "tile_bf16.h"
+#include "tile_dma_bf16.h"
 
 namespace maskattn {
 using namespace dev;
+using namespace dev::dma;
 
 namespace {
 
@@ -129,8 +130,9 @@ __global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
   const uint16_t *kbase = (const uint16_t *)p.k + (int64_t)g * p.s_head;
   const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)g * p.s_head;
   const int32_t *pt = p.page_table + (int64_t)b * p.max_pages;
-  using KV = KvTile<D, NT>;
-  KV kvt;
+  using KV = KvDma<D, 2 * GH>;
+  const LaneOffsets<D> lo(lane);
+  const int wave_id = wave;
   typename KV::Pages pg_nxt;
 
   f32x16 oacc[D / 32];
@@ -142,25 +144,25 @@ __global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
 
   uint64_t word_nxt = 0;
   if (kt0 < kt1) {
-    const typename KV::Pages pg0 = kvt.pages(pt, p.page_shift, kt0, kv, tid);
-    kvt.load(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv, tid);
+    const typename KV::Pages pg0 = KV::pages(pt, p.page_shift, kt0, kv, wave_id, lane);
+    KV::issue(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv, lds, wave_id, lane);
     word_nxt = fetch_word(p, moff, row_base, q_len, kv, kt0, lane);
-    if (kt0 + 1 < kt1) pg_nxt = kvt.pages(pt, p.page_shift, kt0 + 1, kv, tid);
-    kvt.store(lds, tid);
+    if (kt0 + 1 < kt1) pg_nxt = KV::pages(pt, p.page_shift, kt0 + 1, kv, wave_id, lane);
+    wait_vmem();
     __syncthreads();
   }
   for (int kt = kt0; kt < kt1; ++kt) {
     const int cur = (kt - kt0) & 1;
     const uint64_t wcur = word_nxt;
-    const bool has_next = kt + 1 < kt1;
-    if (has_next) {
-      kvt.load(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, kt + 1, kv, tid);
+    if (kt + 1 < kt1) {
+      KV::issue(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, kt + 1, kv,
+                lds + (cur ^ 1) * Stage<D>::ELEMS, wave_id, lane);
       word_nxt = fetch_word(p, moff, row_base, q_len, kv, kt + 1, lane);
-      if (kt + 2 < kt1) pg_nxt = kvt.pages(pt, p.page_shift, kt + 2, kv, tid);
+      if (kt + 2 < kt1) pg_nxt = KV::pages(pt, p.page_shift, kt + 2, kv, wave_id, lane);
     }
     const uint16_t *stage = lds + cur * Stage<D>::ELEMS;
     f32x16 sacc[2];
-    qk_tile<D>(stage, qf, sacc, l32, hi);
+    qk_tile<D>(stage, lo, qf, sacc);
     const int kin = kv - 64 * kt;
     const uint64_t inb = low_bits(kin);
     const uint64_t w = wcur & inb;
@@ -173,8 +175,8 @@ __global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
       for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
       lsum *= alpha;
     }
-    pv_tile<D>(stage, sacc, oacc, lsum, l32, hi);
-    if (has_next) kvt.store(lds + (cur ^ 1) * Stage<D>::ELEMS, tid);
+    pv_tile<D>(stage, lo, sacc, oacc, lsum);
+    wait_vmem();
     __syncthreads();
   }
 
