@@ -51,6 +51,10 @@ class MaPlanInfo(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with masked_flash_attention_mask_amd.build.build()")
+    # torch brings its own HIP runtime.  Load it first so that the library's
+    # libamdhip64 dependency resolves to that same runtime: two HIP runtimes
+    # in one process do not share the device, and the second finds none.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     pp = ctypes.POINTER(ctypes.c_void_p)

@@ -115,3 +115,19 @@ def test_verify_validation_before_hip():
 def test_status_strings():
     for s in range(-7, 1):
         assert L.LIB.ma_status_string(s).decode()
+
+
+def test_single_hip_runtime_in_process():
+    """Importing the package alone maps exactly one HIP runtime: the library's
+    libamdhip64 dependency resolves to the one torch loads (two runtimes in
+    one process do not share the device)."""
+    import subprocess
+    import sys
+    code = ("import os, masked_flash_attention_mask_amd\n"
+            "m = open(f'/proc/{os.getpid()}/maps').read()\n"
+            "print(sorted({l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l}))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=300)
+    assert r.returncode == 0, r.stderr
+    libs = eval(r.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1, libs
