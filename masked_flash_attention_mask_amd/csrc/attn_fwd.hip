@@ -22,6 +22,7 @@
 #include "internal.h"
 #include "kernels_common.h"
 #include "tile_bf16.h"
+#include "tile_dma_bf16.h"
 
 namespace maskattn {
 using namespace dev;
@@ -77,16 +78,32 @@ __device__ __forceinline__ void epilogue(const PrefillParams &p, const f32x16 (&
 // ---------------------------------------------------------------------------
 // bf16 inputs, bf16 matrix cores
 // ---------------------------------------------------------------------------
-template <int D, int BQ>
+// Two ways to move a tile's K/V from the paged cache into LDS:
+//  * DMA (pages of at least 512 / d keys): global_load_lds writes the
+//    swizzled, unpadded stage directly; page ids are scalar loads, one per
+//    gather instruction.  No staging registers, no LDS stores.
+//  * staged (any page size): per-thread loads into registers one tile ahead,
+//    stored to the padded stage at the end of the tile.
+// Both keep two stages and one barrier per tile and compute the same
+// products in the same order, so their results are identical.
+template <int D, int BQ, bool DMA>
 struct Bf16Cfg {
   static constexpr int NW = BQ / 32;
   static constexpr int NT = NW * 64;
-  static constexpr size_t LDS_BYTES = 2 * Stage<D>::BYTES;
+  static constexpr size_t STAGE_ELEMS = DMA ? (size_t)dma::Stage<D>::ELEMS : (size_t)Stage<D>::ELEMS;
+  static constexpr size_t LDS_BYTES = 2 * STAGE_ELEMS * sizeof(uint16_t);
 };
 
-template <int D, int BQ, typename OutT>
+// Plan entries are read through the constant address space: uniform reads
+// there are scalar loads, which neither wait for nor delay the gathers.
+__device__ __forceinline__ Entry load_entry(const Entry *e, int i) {
+  const __attribute__((address_space(4))) Entry *c = (const __attribute__((address_space(4))) Entry *)e;
+  return Entry{c[i].kt_cls, c[i].wblk};
+}
+
+template <int D, int BQ, typename OutT, bool DMA>
 __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefill_bf16_kernel(PrefillParams p) {
-  using C = Bf16Cfg<D, BQ>;
+  using C = Bf16Cfg<D, BQ, DMA>;
   extern __shared__ __align__(16) uint16_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -108,9 +125,6 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
   const uint16_t *kbase = (const uint16_t *)p.k + (int64_t)g * p.s_head;
   const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)g * p.s_head;
   const int32_t *pt = p.page_table + (int64_t)it.seq * p.max_pages;
-  using KV = KvTile<D, C::NT>;
-  KV kv;
-  typename KV::Pages pg_nxt;
 
   auto load_word = [&](Entry e) -> uint64_t {
     if (entry_cls(e.kt_cls) != MA_TILE_PARTIAL) return 0ull;
@@ -126,65 +140,117 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
 
   const int eb = it.ent_begin, ee = it.ent_end;
   uint64_t word_nxt = 0;
-  if (eb < ee) {
-    const Entry e0 = p.entries[eb];
-    const int kt0 = entry_kt(e0.kt_cls);
-    const typename KV::Pages pg0 = kv.pages(pt, p.page_shift, kt0, kv_len, tid);
-    kv.load(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv_len, tid);
-    word_nxt = load_word(e0);
-    if (eb + 1 < ee) pg_nxt = kv.pages(pt, p.page_shift, entry_kt(p.entries[eb + 1].kt_cls), kv_len, tid);
-    kv.store(lds, tid);
-    __syncthreads();
-  }
-  // d = 256 stages K and V of the next tile one after the other (K during
-  // Q K^T and the softmax, V during P V) to halve the staging registers.
-  constexpr bool kSplit = D == 256;
-  for (int e = eb; e < ee; ++e) {
-    const int cur = (e - eb) & 1;
-    const Entry ec = p.entries[e];
-    const uint64_t wcur = word_nxt;
-    const bool has_next = e + 1 < ee;
-    int kt_next = 0;
-    typename KV::Pages pg_use = pg_nxt;
-    if (has_next) {
-      const Entry en = p.entries[e + 1];
-      kt_next = entry_kt(en.kt_cls);
-      if (kSplit)
-        kv.load_one(kbase, pg_use, p.page_shift, p.s_page, p.s_slot, kt_next, kv_len, tid);
-      else
-        kv.load(kbase, vbase, pg_use, p.page_shift, p.s_page, p.s_slot, kt_next, kv_len, tid);
-      word_nxt = load_word(en);
-      if (e + 2 < ee) pg_nxt = kv.pages(pt, p.page_shift, entry_kt(p.entries[e + 2].kt_cls), kv_len, tid);
+  if constexpr (DMA) {
+    using KV = dma::KvDma<D, C::NW>;
+    const dma::LaneOffsets<D> lo(lane);
+    typename KV::Pages pg_nxt;
+    if (eb < ee) {
+      const Entry e0 = load_entry(p.entries, eb);
+      const int kt0 = entry_kt(e0.kt_cls);
+      const typename KV::Pages pg0 = KV::pages_uniform(pt, p.page_shift, kt0, kv_len, wave);
+      KV::issue(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv_len, lds, wave, lane);
+      word_nxt = load_word(e0);
+      if (eb + 1 < ee)
+        pg_nxt = KV::pages_uniform(pt, p.page_shift, entry_kt(load_entry(p.entries, eb + 1).kt_cls), kv_len, wave);
+      dma::wait_vmem();
+      __syncthreads();
     }
-    const uint16_t *stage = lds + cur * Stage<D>::ELEMS;
-    uint16_t *next = lds + (cur ^ 1) * Stage<D>::ELEMS;
-    f32x16 sacc[2];
-    qk_tile<D>(stage, qf, sacc, l32, hi);
-
-    const int kt = entry_kt(ec.kt_cls);
-    const int cls = entry_cls(ec.kt_cls);
-    const int kin = kv_len - kt * 64;
-    if (cls == MA_TILE_PARTIAL || kin < 64)
-      apply_word(sacc, (cls == MA_TILE_PARTIAL ? wcur : ~0ull) & low_bits(kin), hi);
-
-    float alpha;
-    if (softmax_tile(sacc, m_ref, c, alpha)) {
+    for (int e = eb; e < ee; ++e) {
+      const int cur = (e - eb) & 1;
+      const Entry ec = load_entry(p.entries, e);
+      const uint64_t wcur = word_nxt;
+      if (e + 1 < ee) {
+        const Entry en = load_entry(p.entries, e + 1);
+        KV::issue(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, entry_kt(en.kt_cls), kv_len,
+                  lds + (cur ^ 1) * dma::Stage<D>::ELEMS, wave, lane);
+        word_nxt = load_word(en);
+        if (e + 2 < ee)
+          pg_nxt = KV::pages_uniform(pt, p.page_shift, entry_kt(load_entry(p.entries, e + 2).kt_cls), kv_len, wave);
+      }
+      const uint16_t *stage = lds + cur * dma::Stage<D>::ELEMS;
+      f32x16 sacc[2];
+      dma::qk_tile<D>(stage, lo, qf, sacc);
+      {
+        const int kt = entry_kt(ec.kt_cls);
+        const int cls = entry_cls(ec.kt_cls);
+        const int kin = kv_len - kt * 64;
+        if (cls == MA_TILE_PARTIAL || kin < 64)
+          apply_word(sacc, (cls == MA_TILE_PARTIAL ? wcur : ~0ull) & low_bits(kin), hi);
+        float alpha;
+        if (softmax_tile(sacc, m_ref, c, alpha)) {
 #pragma unroll
-      for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
-      lsum *= alpha;
+          for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+          lsum *= alpha;
+        }
+      }
+      dma::pv_tile<D>(stage, lo, sacc, oacc, lsum);
+      dma::wait_vmem();
+      __syncthreads();
     }
-    if (kSplit && has_next) {
-      kv.store_one(next, Stage<D>::KS, tid);
-      kv.load_one(vbase, pg_use, p.page_shift, p.s_page, p.s_slot, kt_next, kv_len, tid);
+  } else {
+    using KV = KvTile<D, C::NT>;
+    KV kv;
+    typename KV::Pages pg_nxt;
+    if (eb < ee) {
+      const Entry e0 = load_entry(p.entries, eb);
+      const int kt0 = entry_kt(e0.kt_cls);
+      const typename KV::Pages pg0 = kv.pages(pt, p.page_shift, kt0, kv_len, tid);
+      kv.load(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv_len, tid);
+      word_nxt = load_word(e0);
+      if (eb + 1 < ee) pg_nxt = kv.pages(pt, p.page_shift, entry_kt(load_entry(p.entries, eb + 1).kt_cls), kv_len, tid);
+      kv.store(lds, tid);
+      __syncthreads();
     }
-    pv_tile<D>(stage, sacc, oacc, lsum, l32, hi);
-    if (has_next) {
-      if (kSplit)
-        kv.store_one(next + Stage<D>::V_OFF, Stage<D>::VS, tid);
-      else
-        kv.store(next, tid);
+    // d = 256 stages K and V of the next tile one after the other (K during
+    // Q K^T and the softmax, V during P V) to halve the staging registers.
+    constexpr bool kSplit = D == 256;
+    for (int e = eb; e < ee; ++e) {
+      const int cur = (e - eb) & 1;
+      const Entry ec = load_entry(p.entries, e);
+      const uint64_t wcur = word_nxt;
+      const bool has_next = e + 1 < ee;
+      int kt_next = 0;
+      typename KV::Pages pg_use = pg_nxt;
+      if (has_next) {
+        const Entry en = load_entry(p.entries, e + 1);
+        kt_next = entry_kt(en.kt_cls);
+        if (kSplit)
+          kv.load_one(kbase, pg_use, p.page_shift, p.s_page, p.s_slot, kt_next, kv_len, tid);
+        else
+          kv.load(kbase, vbase, pg_use, p.page_shift, p.s_page, p.s_slot, kt_next, kv_len, tid);
+        word_nxt = load_word(en);
+        if (e + 2 < ee) pg_nxt = kv.pages(pt, p.page_shift, entry_kt(load_entry(p.entries, e + 2).kt_cls), kv_len, tid);
+      }
+      const uint16_t *stage = lds + cur * Stage<D>::ELEMS;
+      uint16_t *next = lds + (cur ^ 1) * Stage<D>::ELEMS;
+      f32x16 sacc[2];
+      qk_tile<D>(stage, qf, sacc, l32, hi);
+      {
+        const int kt = entry_kt(ec.kt_cls);
+        const int cls = entry_cls(ec.kt_cls);
+        const int kin = kv_len - kt * 64;
+        if (cls == MA_TILE_PARTIAL || kin < 64)
+          apply_word(sacc, (cls == MA_TILE_PARTIAL ? wcur : ~0ull) & low_bits(kin), hi);
+        float alpha;
+        if (softmax_tile(sacc, m_ref, c, alpha)) {
+#pragma unroll
+          for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+          lsum *= alpha;
+        }
+      }
+      if (kSplit && has_next) {
+        kv.store_one(next, Stage<D>::KS, tid);
+        kv.load_one(vbase, pg_use, p.page_shift, p.s_page, p.s_slot, kt_next, kv_len, tid);
+      }
+      pv_tile<D>(stage, sacc, oacc, lsum, l32, hi);
+      if (has_next) {
+        if (kSplit)
+          kv.store_one(next + Stage<D>::V_OFF, Stage<D>::VS, tid);
+        else
+          kv.store(next, tid);
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
   epilogue<D, OutT>(p, oacc, m_ref, lsum[0], tok, h, row_ok, hi);
 }
@@ -241,7 +307,7 @@ __global__ __launch_bounds__(BQ * 2, 1) void prefill_f32_kernel(PrefillParams p)
   const float c = p.scale_log2;
 
   for (int e = it.ent_begin; e < it.ent_end; ++e) {
-    const Entry ec = p.entries[e];
+    const Entry ec = load_entry(p.entries, e);
     const int kt = entry_kt(ec.kt_cls);
     const int cls = entry_cls(ec.kt_cls);
     __syncthreads();  // previous tile fully consumed
@@ -306,12 +372,20 @@ ma_status launch_kernel(K kernel, int grid, int block, size_t lds, const Prefill
   return MA_OK;
 }
 
+template <int D, int BQ, bool DMA>
+ma_status dispatch_bf16_mode(const PrefillArgs &a, const PrefillParams &prm, int grid) {
+  using C = Bf16Cfg<D, BQ, DMA>;
+  if (a.out_dtype == MA_F32)
+    return launch_kernel(prefill_bf16_kernel<D, BQ, float, DMA>, grid, C::NT, C::LDS_BYTES, prm, a.stream);
+  return launch_kernel(prefill_bf16_kernel<D, BQ, uint16_t, DMA>, grid, C::NT, C::LDS_BYTES, prm, a.stream);
+}
+
+// The direct gather needs the key rows of one gather instruction (512 / d of
+// them) inside one page.
 template <int D, int BQ>
 ma_status dispatch_bf16(const PrefillArgs &a, const PrefillParams &prm, int grid) {
-  using C = Bf16Cfg<D, BQ>;
-  if (a.out_dtype == MA_F32)
-    return launch_kernel(prefill_bf16_kernel<D, BQ, float>, grid, C::NT, C::LDS_BYTES, prm, a.stream);
-  return launch_kernel(prefill_bf16_kernel<D, BQ, uint16_t>, grid, C::NT, C::LDS_BYTES, prm, a.stream);
+  if ((1 << a.page_shift) >= dma::KvDma<D, BQ / 32>::RPI) return dispatch_bf16_mode<D, BQ, true>(a, prm, grid);
+  return dispatch_bf16_mode<D, BQ, false>(a, prm, grid);
 }
 
 template <int D, int BQ>

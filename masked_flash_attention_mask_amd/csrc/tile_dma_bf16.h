@@ -1,6 +1,6 @@
-// bf16 tile machinery of the tree-verify kernel: paged K/V gathered straight
-// from the cache into LDS (global_load_lds_dwordx4), the swizzled LDS stage
-// layout, and the two matrix-core products of a wave's 32 query rows.
+// bf16 tile machinery of the kernels that gather paged K/V straight from the
+// cache into LDS (global_load_lds_dwordx4): the swizzled LDS stage layout,
+// the gather, and the two matrix-core products of a wave's 32 query rows.
 #pragma once
 
 #include "internal.h"
@@ -27,6 +27,19 @@ struct Stage {
   __host__ __device__ static constexpr int fv(int r) { return CH >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
+// Direct global -> LDS load of 16 bytes per lane to LDS address lds + 16 lane
+// (M0 holds lds).  Inline asm keeps the compiler from tracking it: it would
+// otherwise wait for every outstanding LDS gather before each later LDS read,
+// including reads of the other stage.  The kernels order the gathers
+// themselves (wait_vmem() before the barrier that publishes a stage).  The
+// load writes no registers; its address registers are read at issue.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+__device__ __forceinline__ void lds_load16(const void *src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
 // Direct global -> LDS gather of one tile by NW waves: wave instruction t
 // fills LDS chunks [64 t, 64 t + 64) of K (and of V); lane l of it loads the
 // chunk that belongs at position 64 t + l.  Keys at or past kv_len are
@@ -41,7 +54,10 @@ struct KvDma {
     int32_t id[IPW];
   };
 
-  // Page of the key each lane loads in each of its instructions for tile kt.
+  static constexpr int RPI = 64 / CH;       // key rows per instruction
+
+  // Page of the key each lane loads in each of its instructions for tile kt
+  // (any page size; one vector load per instruction).
   __device__ __forceinline__ static Pages pages(const int32_t *pt, int page_shift, int kt, int kv_len, int wave,
                                                int lane) {
     Pages pg;
@@ -50,6 +66,21 @@ struct KvDma {
       const int r = (64 * (wave * IPW + i) + lane) / CH;
       pg.id[i] = pt[min(kt * 64 + r, kv_len - 1) >> page_shift];
     }
+    return pg;
+  }
+
+  // The same for pages of at least RPI keys: the RPI rows of an instruction
+  // (an RPI-aligned key group, or keys clamped to the last key, which lies in
+  // the same group or past it) share one page, read with a scalar load
+  // through the constant address space.  Scalar loads leave the vector
+  // memory counter to the gathers, so no wait for a page id drains them.
+  __device__ __forceinline__ static Pages pages_uniform(const int32_t *pt, int page_shift, int kt, int kv_len,
+                                                       int wave) {
+    const __attribute__((address_space(4))) int32_t *cpt = (const __attribute__((address_space(4))) int32_t *)pt;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    Pages pg;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) pg.id[i] = cpt[min(kt * 64 + RPI * (wv * IPW + i), kv_len - 1) >> page_shift];
     return pg;
   }
 
@@ -64,12 +95,8 @@ struct KvDma {
       const int r = pos / CH, pc = pos % CH;
       const int key = min(kt * 64 + r, kv_len - 1);
       const int64_t off = (int64_t)pg.id[i] * s_page + (int64_t)(key & pmask) * s_slot;
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1))) *)(kbase + off + 8 * (pc ^ Stage<D>::fk(r))),
-          (void __attribute__((address_space(3))) *)(stage + 512 * t), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1))) *)(vbase + off + 8 * (pc ^ Stage<D>::fv(r))),
-          (void __attribute__((address_space(3))) *)(stage + Stage<D>::V_OFF + 512 * t), 16, 0, 0);
+      lds_load16(kbase + off + 8 * (pc ^ Stage<D>::fk(r)), lds_addr(stage + 512 * t));
+      lds_load16(vbase + off + 8 * (pc ^ Stage<D>::fv(r)), lds_addr(stage + Stage<D>::V_OFF + 512 * t));
     }
   }
 };

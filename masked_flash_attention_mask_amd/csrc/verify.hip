@@ -155,9 +155,11 @@ __global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
     const int cur = (kt - kt0) & 1;
     const uint64_t wcur = word_nxt;
     if (kt + 1 < kt1) {
+      // The mask word first: a dense mask's ballots wait for its loads, and
+      // that wait would otherwise include the gather.
+      word_nxt = fetch_word(p, moff, row_base, q_len, kv, kt + 1, lane);
       KV::issue(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, kt + 1, kv,
                 lds + (cur ^ 1) * Stage<D>::ELEMS, wave_id, lane);
-      word_nxt = fetch_word(p, moff, row_base, q_len, kv, kt + 1, lane);
       if (kt + 2 < kt1) pg_nxt = KV::pages(pt, p.page_shift, kt + 2, kv, wave_id, lane);
     }
     const uint16_t *stage = lds + cur * Stage<D>::ELEMS;
