@@ -220,6 +220,7 @@ def main():
 
     if args.all:
         extra(args)
+        decode_lines(args.steps, args.warmup)
 
 
 def extra(args):
@@ -275,6 +276,45 @@ def extra(args):
         kv_bytes = 2 * int(w2.kv_lens.sum()) * w2.hkv * w2.d * 2
         print(json.dumps({"workload": "cfg2", "mask": form, "ms": round(ms, 4), "tflops": round(tf, 2),
                           "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def decode_lines(steps, warmup):
+    """Decode (memory bound): K/V bytes the visible keys need, per second,
+    against HBM."""
+    import torch
+    import workloads as W
+    import numpy as np
+    import masked_flash_attention_mask_amd as ma
+    from workloads.device import device_inputs
+    import copy
+    w4 = W.decode(q_len=4)
+    for q_len in (1, 4):
+        if q_len == 4:
+            w = w4
+        else:   # each sequence's last query: the same position, q_len 1
+            w = copy.copy(w4)
+            w.q = w4.q[3::4].copy()
+            w.cu_seqlens_q = np.arange(w4.batch + 1, dtype=np.int32)
+        dev = device_inputs(w)
+        max_kv = int(w.kv_lens.max())
+        ws = torch.empty(max(ma.attn_decode_workspace(w.batch, q_len, max_kv, w.hq, w.hkv, w.d), 1),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty(dev["q"].shape, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
+        for name in ("causal", "window"):
+            win = w.masks[name].window if name == "window" else 0
+
+            def step():
+                ma.attn_decode(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], q_len, max_kv,
+                               w.scale, mask_kind=name, window=win, workspace=ws, out=out, lse=lse)
+            ms = time_steps(step, steps, warmup, torch.cuda.current_stream())
+            keys = [int(k) if name == "causal" else min(int(k), win + q_len - 1) for k in w.kv_lens]
+            kv_bytes = 2 * sum(keys) * w.hkv * w.d * 2
+            gbs = kv_bytes / (ms * 1e-3) / 1e9
+            print(json.dumps({"workload": f"decode_q{q_len}", "mask": name, "ms": round(ms, 4),
+                              "kv_gbs": round(gbs, 1), "pct_of_hbm": round(100 * gbs / 8000.0, 1),
+                              "batch": w.batch, "kv_total": int(w.kv_lens.sum())}), flush=True)
+        del dev
 
 
 def _anc(parents, i):

@@ -1,6 +1,7 @@
 /*
- * maskattn — masked flash-attention prefill and speculative tree verify over
- * ragged sequences with paged K/V, for AMD Instinct MI355X (gfx950).
+ * maskattn — masked flash-attention prefill, speculative tree verify and
+ * masked decode over ragged sequences with paged K/V, for AMD Instinct MI355X
+ * (gfx950).
  *
  * C ABI of libmaskattn.so.  Plain pointers and sizes only.  "host" and
  * "device" below say where a pointer must point.  Streams are hipStream_t
@@ -226,6 +227,39 @@ ma_status attn_verify_tree(const void *q, int64_t total_q, int32_t hq, const voi
                            const void *mask, int64_t mask_numel, int32_t in_dtype,
                            int32_t out_dtype, float scale, void *workspace, size_t ws_bytes,
                            void *out, float *lse, void *stream);
+
+/* Workspace bytes attn_decode needs for these bounds (the same bound serves
+ * every mask kind; 0 when one split covers every context). */
+size_t attn_decode_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq, int32_t hkv,
+                             int32_t d);
+
+/* Masked decode (sglang-jax pull request 20, review comments: custom-mask
+ * tests for prefill and decode modes; mlxcel pull request 555: the sliding
+ * window in single and ragged decode graphs): each sequence's last q_len
+ * (1 .. 64, ragged) tokens against
+ * its paged K/V, query row t at position pos = t + kv_len - q_len, under
+ *  mask_kind CAUSAL         keys <= pos,
+ *            SLIDING_WINDOW pos - window < key <= pos (window >= 1),
+ *            PREFIX_LM      keys <= pos or key < prefix_len[b] (device
+ *                           int32 [batch]),
+ *            DENSE_BOOL / PACKED_U64  rows as for attn_verify_tree;
+ * the same definitions as the prefill masks of the same kinds (RANGES:
+ * pass the rows, MA_ERR_UNSUPPORTED otherwise).  Lengths stay on the device
+ * as for attn_verify_tree.  The query heads of a K/V head's GQA group and
+ * their queries share each gathered K/V tile; long contexts are split over
+ * workgroups and merged in a fixed order; a sliding window only walks the
+ * tiles it can see.  A row that sees no key gets O = 0 and LSE = -inf.
+ * Requires in_dtype BF16 and d in {64, 128, 256}.  workspace: device, at
+ * least attn_decode_workspace(...) bytes (NULL allowed when that is 0), owned
+ * by the caller; its contents need no initialisation. */
+ma_status attn_decode(const void *q, int64_t total_q, int32_t hq, const void *k_cache,
+                      const void *v_cache, int32_t hkv, int32_t d, int32_t page_size,
+                      const int64_t kv_strides[3], const int32_t *page_table, int32_t max_pages,
+                      const int32_t *cu_seqlens_q, const int32_t *kv_lens, int32_t batch,
+                      int32_t max_q, int32_t max_kv, int32_t mask_kind, int32_t window,
+                      const int32_t *prefix_len, const void *mask, int64_t mask_numel,
+                      int32_t in_dtype, int32_t out_dtype, float scale, void *workspace,
+                      size_t ws_bytes, void *out, float *lse, void *stream);
 
 const char *ma_status_string(int32_t status);
 const char *ma_last_error(void);

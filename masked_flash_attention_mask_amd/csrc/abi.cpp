@@ -276,15 +276,13 @@ size_t attn_verify_tree_workspace(int32_t batch, int32_t max_q, int32_t max_kv, 
   return verify_workspace(batch, max_q, max_kv, hq, hkv, d);
 }
 
-ma_status attn_verify_tree(const void *q, int64_t total_q, int32_t hq, const void *k_cache,
-                           const void *v_cache, int32_t hkv, int32_t d, int32_t page_size,
-                           const int64_t kv_strides[3], const int32_t *page_table,
-                           int32_t max_pages, const int32_t *cu_seqlens_q, const int32_t *kv_lens,
-                           int32_t batch, int32_t max_q, int32_t max_kv, int32_t mask_kind,
-                           const void *mask, int64_t mask_numel, int32_t in_dtype,
-                           int32_t out_dtype, float scale, void *workspace, size_t ws_bytes,
-                           void *out, float *lse, void *stream) {
-  clear_error();
+// Checks shared by tree verify and decode (small-q launches).
+static ma_status check_small_q(const void *q, const void *k_cache, const void *v_cache, void *out,
+                               const int32_t *page_table, int32_t hq, int32_t hkv, int32_t page_size,
+                               const int64_t kv_strides[3], int32_t max_pages, float scale,
+                               const int32_t *cu_seqlens_q, const int32_t *kv_lens, int32_t batch,
+                               int32_t max_q, int32_t max_kv, int32_t in_dtype, int32_t out_dtype, int32_t d,
+                               int64_t total_q) {
   ma_status st = check_paged(q, k_cache, v_cache, out, page_table, hq, hkv, page_size, kv_strides,
                              max_pages, scale);
   if (st != MA_OK) return st;
@@ -294,14 +292,21 @@ ma_status attn_verify_tree(const void *q, int64_t total_q, int32_t hq, const voi
   if (max_kv < 1) return set_error(MA_ERR_INVALID, "max_kv must be >= 1");
   if ((int64_t)max_pages * page_size < max_kv)
     return set_error(MA_ERR_INVALID, "page table shorter than max_kv");
-  if (mask_kind != MA_KIND_DENSE_BOOL && mask_kind != MA_KIND_PACKED_U64)
-    return set_error(MA_ERR_CONFLICT, "tree verify takes a custom mask (dense or packed), got kind %d", mask_kind);
-  if (!mask || mask_numel < 1) return set_error(MA_ERR_INVALID, "mask is required");
-  if (in_dtype != MA_BF16) return set_error(MA_ERR_UNSUPPORTED, "tree verify needs bf16 inputs");
+  if (in_dtype != MA_BF16) return set_error(MA_ERR_UNSUPPORTED, "small-q attention needs bf16 inputs");
   if (d != 64 && d != 128 && d != 256) return set_error(MA_ERR_UNSUPPORTED, "head_dim %d", d);
   if (out_dtype != MA_BF16 && out_dtype != MA_F32) return set_error(MA_ERR_UNSUPPORTED, "out dtype %d", out_dtype);
   if (kv_strides[2] < d) return set_error(MA_ERR_INVALID, "head stride < head_dim");
   if (total_q < 0 || total_q > (int64_t)batch * max_q) return set_error(MA_ERR_INVALID, "total_q out of range");
+  return MA_OK;
+}
+
+static ma_status run_small_q(const void *q, int32_t hq, const void *k_cache, const void *v_cache, int32_t hkv,
+                             int32_t d, int32_t page_size, const int64_t kv_strides[3], const int32_t *page_table,
+                             int32_t max_pages, const int32_t *cu_seqlens_q, const int32_t *kv_lens,
+                             int32_t batch, int32_t max_q, int32_t max_kv, int32_t mask_kind, int32_t window,
+                             const int32_t *prefix_len, const void *mask, int64_t mask_numel, int32_t out_dtype,
+                             float scale, void *workspace, size_t ws_bytes, void *out, float *lse,
+                             void *stream) {
   const size_t need = verify_workspace(batch, max_q, max_kv, hq, hkv, d);
   if (need > 0 && (!workspace || ws_bytes < need))
     return set_error(MA_ERR_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
@@ -326,6 +331,8 @@ ma_status attn_verify_tree(const void *q, int64_t total_q, int32_t hq, const voi
   a.mask_kind = mask_kind;
   a.mask = mask;
   a.mask_numel = mask_numel;
+  a.window = window;
+  a.prefix_len = prefix_len;
   a.out_dtype = out_dtype;
   a.scale = scale;
   a.workspace = workspace;
@@ -334,6 +341,65 @@ ma_status attn_verify_tree(const void *q, int64_t total_q, int32_t hq, const voi
   a.lse = lse;
   a.stream = stream;
   return launch_verify(a);
+}
+
+size_t attn_decode_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq, int32_t hkv, int32_t d) {
+  if (batch < 1 || max_q < 1 || max_q > 64 || max_kv < 1 || hq < 1 || hkv < 1 || d < 1 || hq % hkv != 0) return 0;
+  return verify_workspace(batch, max_q, max_kv, hq, hkv, d);
+}
+
+ma_status attn_decode(const void *q, int64_t total_q, int32_t hq, const void *k_cache, const void *v_cache,
+                      int32_t hkv, int32_t d, int32_t page_size, const int64_t kv_strides[3],
+                      const int32_t *page_table, int32_t max_pages, const int32_t *cu_seqlens_q,
+                      const int32_t *kv_lens, int32_t batch, int32_t max_q, int32_t max_kv, int32_t mask_kind,
+                      int32_t window, const int32_t *prefix_len, const void *mask, int64_t mask_numel,
+                      int32_t in_dtype, int32_t out_dtype, float scale, void *workspace, size_t ws_bytes,
+                      void *out, float *lse, void *stream) {
+  clear_error();
+  ma_status st = check_small_q(q, k_cache, v_cache, out, page_table, hq, hkv, page_size, kv_strides, max_pages,
+                               scale, cu_seqlens_q, kv_lens, batch, max_q, max_kv, in_dtype, out_dtype, d, total_q);
+  if (st != MA_OK) return st;
+  switch (mask_kind) {
+    case MA_KIND_CAUSAL:
+      break;
+    case MA_KIND_SLIDING_WINDOW:
+      if (window < 1) return set_error(MA_ERR_INVALID, "window must be >= 1 (got %d)", window);
+      break;
+    case MA_KIND_PREFIX_LM:
+      if (!prefix_len) return set_error(MA_ERR_INVALID, "prefix_len is required for PREFIX_LM");
+      break;
+    case MA_KIND_DENSE_BOOL:
+    case MA_KIND_PACKED_U64:
+      if (!mask || mask_numel < 1) return set_error(MA_ERR_INVALID, "mask is required");
+      break;
+    case MA_KIND_RANGES:
+      return set_error(MA_ERR_UNSUPPORTED, "decode takes RANGES masks as dense or packed rows");
+    default:
+      return set_error(MA_ERR_INVALID, "mask kind %d", mask_kind);
+  }
+  return run_small_q(q, hq, k_cache, v_cache, hkv, d, page_size, kv_strides, page_table, max_pages, cu_seqlens_q,
+                     kv_lens, batch, max_q, max_kv, mask_kind, window, prefix_len, mask, mask_numel, out_dtype,
+                     scale, workspace, ws_bytes, out, lse, stream);
+}
+
+ma_status attn_verify_tree(const void *q, int64_t total_q, int32_t hq, const void *k_cache,
+                           const void *v_cache, int32_t hkv, int32_t d, int32_t page_size,
+                           const int64_t kv_strides[3], const int32_t *page_table,
+                           int32_t max_pages, const int32_t *cu_seqlens_q, const int32_t *kv_lens,
+                           int32_t batch, int32_t max_q, int32_t max_kv, int32_t mask_kind,
+                           const void *mask, int64_t mask_numel, int32_t in_dtype,
+                           int32_t out_dtype, float scale, void *workspace, size_t ws_bytes,
+                           void *out, float *lse, void *stream) {
+  clear_error();
+  ma_status st = check_small_q(q, k_cache, v_cache, out, page_table, hq, hkv, page_size, kv_strides, max_pages,
+                               scale, cu_seqlens_q, kv_lens, batch, max_q, max_kv, in_dtype, out_dtype, d, total_q);
+  if (st != MA_OK) return st;
+  if (mask_kind != MA_KIND_DENSE_BOOL && mask_kind != MA_KIND_PACKED_U64)
+    return set_error(MA_ERR_CONFLICT, "tree verify takes a custom mask (dense or packed), got kind %d", mask_kind);
+  if (!mask || mask_numel < 1) return set_error(MA_ERR_INVALID, "mask is required");
+  return run_small_q(q, hq, k_cache, v_cache, hkv, d, page_size, kv_strides, page_table, max_pages, cu_seqlens_q,
+                     kv_lens, batch, max_q, max_kv, mask_kind, 0, nullptr, mask, mask_numel, out_dtype, scale,
+                     workspace, ws_bytes, out, lse, stream);
 }
 
 }  // extern "C"

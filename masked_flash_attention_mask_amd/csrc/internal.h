@@ -118,6 +118,8 @@ struct VerifyArgs {
   int32_t mask_kind;
   const void *mask;
   int64_t mask_numel;
+  int32_t window;              // SLIDING_WINDOW
+  const int32_t *prefix_len;   // PREFIX_LM, device [batch]
   int32_t out_dtype;
   float scale;
   void *workspace;

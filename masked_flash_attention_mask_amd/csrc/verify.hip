@@ -1,19 +1,27 @@
-// Speculative tree verify (gfx950): every sequence's draft-tree queries
-// (q_len <= 64) against its cached context plus the draft tokens, under a
-// full-row custom mask that changes every decoding step (tree attention
-// through a custom mask, flashinfer issue 724).
+// Small-q attention over paged K/V (gfx950): speculative tree verify and
+// masked decode.  Every sequence's few queries (q_len <= 64) attend to its
+// cached keys under a per-row mask:
+//  * a full-row custom mask that changes every decoding step (tree attention
+//    through a custom mask, flashinfer issue 724), dense bytes or packed
+//    words, or
+//  * a closed form evaluated per row from its position pos = t + kv_len -
+//    q_len: causal (keys <= pos), sliding window (pos - W < key <= pos),
+//    prefixLM (keys <= pos or < P).
 //
-// The mask is classified on the fly, per tile and per wave, instead of in a
-// separate pass: each lane fetches its query row's 64-bit word for the tile
-// (one word per row of a packed mask; for a dense mask a wavefront ballot
-// over 64 contiguous bytes of the row), and a wave whose rows all see the
-// whole tile (every context tile) skips masking.
+// Rows: the (query head, query) pairs of one GQA group are packed 32 to a
+// wave, head-major, max_q row slots per head.  A workgroup takes GH heads of
+// a group, so each K/V tile gathered from the paged cache serves all of
+// their queries: a 64-node tree over 4 heads fills 8 waves; a single-token
+// decode over a group of 8 heads fills 8 rows of one wave.
 //
-// Work split: a workgroup takes GH query heads of one GQA group (two waves of
-// 32 rows per head), so each K/V tile gathered from the paged cache serves
-// GH heads.  Long contexts are cut into contiguous k-tile ranges handled by
-// separate workgroups; each writes a partial (O, LSE) and a second kernel
-// merges the partials in fixed split order (deterministic, no atomics).
+// The mask is turned into each row's 64-bit word per tile on the fly (a
+// packed word is one load; a dense row's 64 bytes are one coalesced load
+// and a wavefront ballot; a closed form is a bit interval), and a wave
+// whose rows all see the whole tile skips masking.  A sliding window starts
+// the walk at the first tile any row can see.  Long contexts are cut into
+// contiguous k-tile ranges handled by separate workgroups; each writes a
+// partial (O, LSE) and a second kernel merges the partials in fixed split
+// order (deterministic, no atomics).
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -28,26 +36,57 @@ namespace {
 
 constexpr int kTargetWorkgroups = 512;
 
+enum MaskMode : int32_t { kDense = 0, kPacked = 1, kCausal = 2, kWindow = 3, kPrefix = 4 };
+
 struct SplitShape {
   int tiles_per_split;
   int max_splits;
 };
 
-SplitShape split_shape(int batch, int max_kv, int hkv) {
-  const int max_nkt = (max_kv + 63) / 64;
-  int want = (kTargetWorkgroups + batch * hkv - 1) / (batch * hkv);
-  want = want < 1 ? 1 : (want > max_nkt ? max_nkt : want);
-  const int t = (max_nkt + want - 1) / want;
-  return SplitShape{t, (max_nkt + t - 1) / t};
+// Splits of a walk of at most max_tiles k-tiles so that about
+// kTargetWorkgroups workgroups run.
+SplitShape split_shape(int units, int max_tiles) {
+  if (max_tiles < 1) return SplitShape{1, 1};
+  int want = (kTargetWorkgroups + units - 1) / units;
+  want = want < 1 ? 1 : (want > max_tiles ? max_tiles : want);
+  const int t = (max_tiles + want - 1) / want;
+  return SplitShape{t, (max_tiles + t - 1) / t};
 }
 
-// Query heads per workgroup: the largest of 4, 2, 1 that divides the GQA
-// group (2 at most for d = 256, whose accumulators fill the register file).
-int heads_per_workgroup(int group, int d) {
-  const int cap = d == 256 ? 2 : 4;
-  for (int gh = cap; gh > 1; gh >>= 1)
-    if (group % gh == 0) return gh;
-  return 1;
+struct Shape {
+  int gh;      // query heads per workgroup
+  int nw;      // waves per workgroup (1, 2, 4 or 8)
+  SplitShape sp;
+};
+
+// The largest GH dividing the GQA group whose GH x max_q rows fit the waves
+// a workgroup may have (8; 4 at d = 256, whose accumulators need a whole
+// SIMD's registers per wave).  Memory-bound decode loses nothing to the
+// padding rows of a wave.
+Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles) {
+  const int group = hq / hkv;
+  const int max_rows = 32 * (d == 256 ? 4 : 8);
+  int gh = 1;
+  for (int c = group; c >= 1; --c)
+    if (group % c == 0 && c * max_q <= max_rows) {
+      gh = c;
+      break;
+    }
+  const int need = (gh * max_q + 31) / 32;
+  // At d = 256 a workgroup keeps 4 waves even for a few rows: each wave's
+  // share of the tile gather (addresses in registers) then stays small.
+  int nw = d == 256 ? 4 : 1;
+  while (nw < need) nw <<= 1;
+  return Shape{gh, nw, split_shape(batch * (hq / gh), max_tiles)};
+}
+
+// Tiles a sequence's walk can need: all of them, or for a sliding window the
+// ones from the first visible key of row 0.
+int max_walk_tiles(int mode, int window, int max_q, int max_kv) {
+  const int all = (max_kv + 63) / 64;
+  if (mode != kWindow) return all;
+  const int span = (window + max_q - 1 + 63) / 64 + 1;
+  return span < all ? span : all;
 }
 
 struct VerifyParams {
@@ -56,56 +95,88 @@ struct VerifyParams {
   const int32_t *cu_seqlens_q, *kv_lens;
   const void *mask;
   int64_t mask_numel;
+  const int32_t *prefix_len;
   void *out;
   float *lse;
-  float *ws_o;    // [batch][max_splits][hq][64][d]
-  float *ws_lse;  // [batch][max_splits][hq][64]
+  float *ws_o;    // [batch][max_splits][hq][qs][d]
+  float *ws_lse;  // [batch][max_splits][hq][qs]
   int64_t s_page, s_slot, s_head;
   int32_t max_pages, page_shift;
-  int32_t hq, group, packed;
+  int32_t hq, group, gh, qs;
+  int32_t mode, window;
   int32_t tiles_per_split, max_splits, max_kv;
   float scale, scale_log2;
 };
 
 __device__ __forceinline__ int64_t mask_offset(const VerifyParams &p, int b) {
   int64_t off = 0;
+  if (p.mode != kDense && p.mode != kPacked) return 0;
   for (int i = 0; i < b; ++i) {
     const int64_t ql = p.cu_seqlens_q[i + 1] - p.cu_seqlens_q[i], kv = p.kv_lens[i];
-    off += p.packed ? ql * ((kv + 63) / 64) : ql * kv;
+    off += p.mode == kPacked ? ql * ((kv + 63) / 64) : ql * kv;
   }
   return off;
 }
 
-// The lane's row word for k-tile kt (rows of this wave: base + 0..31; lanes
-// l and l + 32 hold the same row).
-__device__ __forceinline__ uint64_t fetch_word(const VerifyParams &p, int64_t moff, int row_base, int q_len,
-                                               int kv, int kt, int lane) {
-  const int l32 = lane & 31;
-  const int keys = min(64, kv - 64 * kt);
-  if (p.packed) {
-    const int row = row_base + l32;
-    if (row >= q_len) return 0ull;
-    const int64_t idx = moff + (int64_t)row * ((kv + 63) / 64) + kt;
-    return idx < p.mask_numel ? ((const uint64_t *)p.mask)[idx] : 0ull;
+// First k-tile any row of the sequence can see.
+__device__ __forceinline__ int first_tile(const VerifyParams &p, int q_len, int kv) {
+  if (p.mode != kWindow) return 0;
+  const int lo = kv - q_len + 1 - p.window;
+  return lo > 0 ? lo / 64 : 0;
+}
+
+// Bits of keys [lo, hi] inside k-tile kt.
+__device__ __forceinline__ uint64_t interval_word(int lo, int hi, int kt) {
+  const int a = max(lo - 64 * kt, 0), b = min(hi - 64 * kt, 63);
+  if (a > b) return 0ull;
+  return (~0ull >> (63 - b)) & (~0ull << a);
+}
+
+// The word of query t of the sequence for k-tile kt (closed forms and packed
+// masks: this lane's own row).
+__device__ __forceinline__ uint64_t row_word(const VerifyParams &p, int64_t moff, int plen, int t, bool ok,
+                                             int q_len, int kv, int kt) {
+  if (!ok) return 0ull;
+  const int pos = t + kv - q_len;
+  switch (p.mode) {
+    case kPacked: {
+      const int64_t idx = moff + (int64_t)t * ((kv + 63) / 64) + kt;
+      return idx < p.mask_numel ? ((const uint64_t *)p.mask)[idx] : 0ull;
+    }
+    case kCausal: return interval_word(0, pos, kt);
+    case kWindow: return interval_word(pos - p.window + 1, pos, kt);
+    default: return interval_word(0, max(pos, plen - 1), kt);  // kPrefix
   }
+}
+
+// The lane's row word for k-tile kt.  A dense mask is read one row at a time
+// across the wave: lane j loads byte j of row i's 64, a ballot forms the
+// word, and the lanes holding row i keep it (rows of the wave: r0 .. r0+31).
+__device__ __forceinline__ uint64_t fetch_word(const VerifyParams &p, int64_t moff, int plen, int t, bool ok,
+                                               int r0, int q_len, int kv, int kt, int lane) {
+  if (p.mode != kDense) return row_word(p, moff, plen, t, ok, q_len, kv, kt);
+  const int keys = min(64, kv - 64 * kt);
   const uint8_t *m8 = (const uint8_t *)p.mask;
   uint64_t w = 0;
   for (int i = 0; i < 32; ++i) {
-    const int row = row_base + i;
+    const int r = r0 + i;
+    const int ti = r % p.qs;
     bool bit = false;
-    if (row < q_len && lane < keys) {
-      const int64_t idx = moff + (int64_t)row * kv + 64 * kt + lane;
+    if (r / p.qs < p.gh && ti < q_len && lane < keys) {
+      const int64_t idx = moff + (int64_t)ti * kv + 64 * kt + lane;
       bit = idx < p.mask_numel && m8[idx] != 0;
     }
     const uint64_t word = __ballot(bit);
-    if (l32 == i) w = word;
+    if ((lane & 31) == i) w = word;
   }
   return w;
 }
 
-template <int D, int GH, typename OutT>
-__global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
-  constexpr int NT = GH * 128;
+// UP: pages hold at least the key rows of one gather instruction, so page
+// ids are scalar loads (uniform per instruction) instead of one vector load
+// per lane and instruction.
+template <int D, int NW, typename OutT, bool UP>
+__global__ __launch_bounds__(NW * 64, 1) void verify_kernel(VerifyParams p) {
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -113,27 +184,38 @@ __global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
   const int q0 = p.cu_seqlens_q[b], q_len = p.cu_seqlens_q[b + 1] - q0;
   const int kv = min(p.kv_lens[b], p.max_kv);  // the page table covers max_kv keys
   const int nkt = (kv + 63) / 64;
-  const int nsplit = (nkt + p.tiles_per_split - 1) / p.tiles_per_split;
-  if (split >= nsplit && !(split == 0 && nkt == 0)) return;
-  const int kt0 = split * p.tiles_per_split;
+  const int ktf = first_tile(p, q_len, kv);
+  const int ntiles = nkt - ktf;
+  const int nsplit = (ntiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  if (split >= nsplit && !(split == 0 && ntiles <= 0)) return;
+  const int kt0 = ktf + split * p.tiles_per_split;
   const int kt1 = min(nkt, kt0 + p.tiles_per_split);
-  const int h = blockIdx.y * GH + (wave >> 1);
-  const int g = h / p.group;
-  const int row_base = (wave & 1) * 32;
-  const int t = row_base + l32;
-  const bool row_ok = t < q_len;
+  // Row of this lane: (head hh of the workgroup's GH, query t).
+  const int r0 = wave * 32;
+  const int r = r0 + l32;
+  const int hh = min(r / p.qs, p.gh - 1);
+  const int t = r % p.qs;
+  const bool row_ok = r / p.qs < p.gh && t < q_len;
+  const int h = blockIdx.y * p.gh + hh;
+  const int g = (blockIdx.y * p.gh) / p.group;
   const int64_t tok = (int64_t)q0 + t;
   const int64_t moff = mask_offset(p, b);
+  const int plen = p.mode == kPrefix ? p.prefix_len[b] : 0;
 
   bf16x8 qf[D / 16];
   load_q<D>(qf, (const uint16_t *)p.q + (tok * p.hq + h) * D, row_ok, hi);
   const uint16_t *kbase = (const uint16_t *)p.k + (int64_t)g * p.s_head;
   const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)g * p.s_head;
   const int32_t *pt = p.page_table + (int64_t)b * p.max_pages;
-  using KV = KvDma<D, 2 * GH>;
+  using KV = KvDma<D, NW>;
   const LaneOffsets<D> lo(lane);
-  const int wave_id = wave;
   typename KV::Pages pg_nxt;
+  auto pages = [&](int kt) {
+    if constexpr (UP)
+      return KV::pages_uniform(pt, p.page_shift, kt, kv, wave);
+    else
+      return KV::pages(pt, p.page_shift, kt, kv, wave, lane);
+  };
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -144,10 +226,10 @@ __global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
 
   uint64_t word_nxt = 0;
   if (kt0 < kt1) {
-    const typename KV::Pages pg0 = KV::pages(pt, p.page_shift, kt0, kv, wave_id, lane);
-    KV::issue(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv, lds, wave_id, lane);
-    word_nxt = fetch_word(p, moff, row_base, q_len, kv, kt0, lane);
-    if (kt0 + 1 < kt1) pg_nxt = KV::pages(pt, p.page_shift, kt0 + 1, kv, wave_id, lane);
+    const typename KV::Pages pg0 = pages(kt0);
+    KV::issue(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv, lds, wave, lane);
+    word_nxt = fetch_word(p, moff, plen, t, row_ok, r0, q_len, kv, kt0, lane);
+    if (kt0 + 1 < kt1) pg_nxt = pages(kt0 + 1);
     wait_vmem();
     __syncthreads();
   }
@@ -157,10 +239,10 @@ __global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
     if (kt + 1 < kt1) {
       // The mask word first: a dense mask's ballots wait for its loads, and
       // that wait would otherwise include the gather.
-      word_nxt = fetch_word(p, moff, row_base, q_len, kv, kt + 1, lane);
+      word_nxt = fetch_word(p, moff, plen, t, row_ok, r0, q_len, kv, kt + 1, lane);
       KV::issue(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, kt + 1, kv,
-                lds + (cur ^ 1) * Stage<D>::ELEMS, wave_id, lane);
-      if (kt + 2 < kt1) pg_nxt = KV::pages(pt, p.page_shift, kt + 2, kv, wave_id, lane);
+                lds + (cur ^ 1) * Stage<D>::ELEMS, wave, lane);
+      if (kt + 2 < kt1) pg_nxt = pages(kt + 2);
     }
     const uint16_t *stage = lds + cur * Stage<D>::ELEMS;
     f32x16 sacc[2];
@@ -190,7 +272,7 @@ __global__ __launch_bounds__(GH * 128, 1) void verify_kernel(VerifyParams p) {
     store_row<D, OutT>((OutT *)p.out + (tok * p.hq + h) * D, oacc, inv, hi);
     if (p.lse && hi == 0) p.lse[tok * p.hq + h] = lse;
   } else {
-    const int64_t slot = (((int64_t)b * p.max_splits + split) * p.hq + h) * 64 + t;
+    const int64_t slot = (((int64_t)b * p.max_splits + split) * p.hq + h) * p.qs + t;
     store_row<D, float>(p.ws_o + slot * D, oacc, inv, hi);
     if (hi == 0) p.ws_lse[slot] = lse;
   }
@@ -203,19 +285,19 @@ __global__ __launch_bounds__(256) void verify_combine(VerifyParams p) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int q0 = p.cu_seqlens_q[b], q_len = p.cu_seqlens_q[b + 1] - q0;
   const int kv = min(p.kv_lens[b], p.max_kv);
-  const int nkt = (kv + 63) / 64;
-  const int nsplit = (nkt + p.tiles_per_split - 1) / p.tiles_per_split;
+  const int ntiles = (kv + 63) / 64 - first_tile(p, q_len, kv);
+  const int nsplit = (ntiles + p.tiles_per_split - 1) / p.tiles_per_split;
   if (nsplit <= 1) return;
   const int64_t sbase = (int64_t)b * p.max_splits;
   for (int idx = threadIdx.x; idx < q_len * (D / 4); idx += blockDim.x) {
     const int t = idx / (D / 4), c4 = idx % (D / 4);
     float mx = neg_inf();
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, p.ws_lse[((sbase + s) * p.hq + h) * 64 + t]);
+    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, p.ws_lse[((sbase + s) * p.hq + h) * p.qs + t]);
     float wsum = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (mx != neg_inf()) {
       for (int s = 0; s < nsplit; ++s) {
-        const int64_t slot = ((sbase + s) * p.hq + h) * 64 + t;
+        const int64_t slot = ((sbase + s) * p.hq + h) * p.qs + t;
         const float wgt = __expf(p.ws_lse[slot] - mx);
         const f32x4 o = *(const f32x4 *)(p.ws_o + slot * D + 4 * c4);
         acc += wgt * o;
@@ -230,18 +312,19 @@ __global__ __launch_bounds__(256) void verify_combine(VerifyParams p) {
   }
 }
 
-template <int D, int GH, typename OutT>
-ma_status run(const VerifyArgs &a, const VerifyParams &prm, const SplitShape &sp) {
+template <int D, int NW, typename OutT>
+ma_status run(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh) {
   const size_t lds = 2 * Stage<D>::BYTES;
-  auto kern = verify_kernel<D, GH, OutT>;
+  auto kern = (1 << a.page_shift) >= KvDma<D, NW>::RPI ? verify_kernel<D, NW, OutT, true>
+                                                       : verify_kernel<D, NW, OutT, false>;
   hipError_t e = hipSuccess;
   if (lds > 64 * 1024) e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
   hipStream_t s = (hipStream_t)a.stream;
-  hipLaunchKernelGGL(kern, dim3(sp.max_splits, a.hq / GH, a.batch), dim3(GH * 128), lds, s, prm);
+  hipLaunchKernelGGL(kern, dim3(sh.sp.max_splits, a.hq / sh.gh, a.batch), dim3(NW * 64), lds, s, prm);
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify launch: %s", hipGetErrorString(e));
-  if (sp.max_splits > 1) {
+  if (sh.sp.max_splits > 1) {
     hipLaunchKernelGGL((verify_combine<D, OutT>), dim3(a.hq, a.batch), dim3(256), 0, s, prm);
     e = hipGetLastError();
     if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify combine launch: %s", hipGetErrorString(e));
@@ -250,32 +333,57 @@ ma_status run(const VerifyArgs &a, const VerifyParams &prm, const SplitShape &sp
 }
 
 template <int D, typename OutT>
-ma_status run_gh(const VerifyArgs &a, const VerifyParams &prm, const SplitShape &sp) {
-  switch (heads_per_workgroup(a.hq / a.hkv, D)) {
-    case 1: return run<D, 1, OutT>(a, prm, sp);
-    case 2: return run<D, 2, OutT>(a, prm, sp);
-    default: return run<D, 4, OutT>(a, prm, sp);
+ma_status run_nw(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh) {
+  if constexpr (D == 256) {
+    if (sh.nw != 4) return set_error(MA_ERR_UNSUPPORTED, "%d waves at head_dim 256", sh.nw);
+    return run<D, 4, OutT>(a, prm, sh);
+  } else {
+    switch (sh.nw) {
+      case 1: return run<D, 1, OutT>(a, prm, sh);
+      case 2: return run<D, 2, OutT>(a, prm, sh);
+      case 4: return run<D, 4, OutT>(a, prm, sh);
+    }
+    return run<D, 8, OutT>(a, prm, sh);
   }
 }
 
 template <int D>
-ma_status run_d(const VerifyArgs &a, const VerifyParams &prm, const SplitShape &sp) {
-  if (a.out_dtype == MA_F32) return run_gh<D, float>(a, prm, sp);
-  return run_gh<D, uint16_t>(a, prm, sp);
+ma_status run_d(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh) {
+  if (a.out_dtype == MA_F32) return run_nw<D, float>(a, prm, sh);
+  return run_nw<D, uint16_t>(a, prm, sh);
+}
+
+int mode_of(int32_t kind) {
+  switch (kind) {
+    case MA_KIND_DENSE_BOOL: return kDense;
+    case MA_KIND_PACKED_U64: return kPacked;
+    case MA_KIND_CAUSAL: return kCausal;
+    case MA_KIND_SLIDING_WINDOW: return kWindow;
+    default: return kPrefix;
+  }
+}
+
+// The workspace a launch uses: max_splits x max_q partial rows per head and
+// sequence (none when one split suffices).  The window only shortens the
+// walk, so the bound for the whole context holds for every kind.
+size_t workspace_bytes(const Shape &sh, int32_t batch, int32_t max_q, int32_t hq, int32_t d) {
+  if (sh.sp.max_splits <= 1) return 0;
+  return (size_t)batch * sh.sp.max_splits * hq * max_q * (d + 1) * sizeof(float);
 }
 
 }  // namespace
 
 size_t verify_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq, int32_t hkv, int32_t d) {
-  (void)max_q;
-  const SplitShape sp = split_shape(batch, max_kv, hkv);
-  if (sp.max_splits <= 1) return 0;
-  return (size_t)batch * sp.max_splits * hq * 64 * (d + 1) * sizeof(float);
+  const Shape sh = shape_for(batch, hq, hkv, d, max_q, max_walk_tiles(kDense, 0, max_q, max_kv));
+  return workspace_bytes(sh, batch, max_q, hq, d);
 }
 
 ma_status launch_verify(const VerifyArgs &a) {
-  const int group = a.hq / a.hkv;
-  const SplitShape sp = split_shape(a.batch, a.max_kv, a.hkv);
+  const int mode = mode_of(a.mask_kind);
+  Shape sh = shape_for(a.batch, a.hq, a.hkv, a.d, a.max_q, max_walk_tiles(mode, a.window, a.max_q, a.max_kv));
+  // Never more splits than the whole-context shape the workspace was sized for.
+  const Shape full = shape_for(a.batch, a.hq, a.hkv, a.d, a.max_q, max_walk_tiles(kDense, 0, a.max_q, a.max_kv));
+  if (sh.sp.max_splits > full.sp.max_splits) sh.sp = full.sp;
   VerifyParams prm{};
   prm.q = a.q;
   prm.k = a.k;
@@ -285,27 +393,31 @@ ma_status launch_verify(const VerifyArgs &a) {
   prm.kv_lens = a.kv_lens;
   prm.mask = a.mask;
   prm.mask_numel = a.mask_numel;
+  prm.prefix_len = a.prefix_len;
   prm.out = a.out;
   prm.lse = a.lse;
   prm.ws_o = (float *)a.workspace;
-  prm.ws_lse = sp.max_splits > 1 ? prm.ws_o + (size_t)a.batch * sp.max_splits * a.hq * 64 * a.d : nullptr;
+  prm.ws_lse = sh.sp.max_splits > 1 ? prm.ws_o + (size_t)a.batch * sh.sp.max_splits * a.hq * a.max_q * a.d : nullptr;
   prm.s_page = a.s_page;
   prm.s_slot = a.s_slot;
   prm.s_head = a.s_head;
   prm.max_pages = a.max_pages;
   prm.page_shift = a.page_shift;
   prm.hq = a.hq;
-  prm.group = group;
-  prm.packed = a.mask_kind == MA_KIND_PACKED_U64 ? 1 : 0;
-  prm.tiles_per_split = sp.tiles_per_split;
-  prm.max_splits = sp.max_splits;
+  prm.group = a.hq / a.hkv;
+  prm.gh = sh.gh;
+  prm.qs = a.max_q;
+  prm.mode = mode;
+  prm.window = a.window;
+  prm.tiles_per_split = sh.sp.tiles_per_split;
+  prm.max_splits = sh.sp.max_splits;
   prm.max_kv = a.max_kv;
   prm.scale = a.scale;
   prm.scale_log2 = a.scale * kLog2e;
   switch (a.d) {
-    case 64: return run_d<64>(a, prm, sp);
-    case 128: return run_d<128>(a, prm, sp);
-    case 256: return run_d<256>(a, prm, sp);
+    case 64: return run_d<64>(a, prm, sh);
+    case 128: return run_d<128>(a, prm, sh);
+    case 256: return run_d<256>(a, prm, sh);
   }
   return set_error(MA_ERR_UNSUPPORTED, "head_dim %d", a.d);
 }

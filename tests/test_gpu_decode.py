@@ -1,0 +1,132 @@
+"""GPU parity of masked decode (HIP path through the C ABI) against the fp64
+oracle: ragged q_len 1..8 against ragged paged contexts (tails, one-key
+contexts, contexts long enough to split), every mask kind, GQA and MHA."""
+
+import numpy as np
+import pytest
+import torch
+
+import masked_flash_attention_mask_amd as ma
+import workloads as W
+from helpers import TOL_BF16, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle
+from oracle import masks as OM
+
+pytestmark = pytest.mark.gpu
+
+Q_LENS = [1, 1, 3, 8, 2]
+KV_LENS = [1, 64, 700, 2100, 130]
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _workload(seed, d, hq, hkv):
+    rng = W.rng_for(seed)
+    w = W.gen._build(f"decode{seed}", rng, "bf16", Q_LENS, KV_LENS, hq, hkv, d, permute=True)
+    mrng = np.random.default_rng(seed + 1)
+    prefix = np.array([mrng.integers(0, k + 1) for k in KV_LENS], np.int32)
+    dense = []
+    for q, k in zip(Q_LENS, KV_LENS):
+        m = mrng.random((q, k)) < 0.3
+        m[:, k - 1] = True                   # every row sees its last key
+        dense.append(m)
+    w.masks["causal"] = W.MaskInput("causal")
+    w.masks["window"] = W.MaskInput("window", window=37)
+    w.masks["wide_window"] = W.MaskInput("window", window=5000)
+    w.masks["prefix"] = W.MaskInput("prefix_lm", prefix_len=prefix)
+    w.masks["dense"] = W.MaskInput("dense", data=np.concatenate([m.astype(np.uint8).reshape(-1) for m in dense]))
+    w.masks["packed"] = W.MaskInput("packed", data=np.concatenate([W.pack_rows(m).reshape(-1) for m in dense]))
+    causal = [OM.causal(q, k) for q, k in zip(Q_LENS, KV_LENS)]
+    w.masks["causal_dense"] = W.MaskInput(
+        "dense", data=np.concatenate([m.astype(np.uint8).reshape(-1) for m in causal]))
+    return w
+
+
+def _decode(w, dev, name, out_dtype=torch.float32):
+    mi = w.masks[name]
+    kw = {}
+    if mi.kind == "window":
+        kw["window"] = mi.window
+    elif mi.kind == "prefix_lm":
+        kw["prefix_len"] = torch.from_numpy(mi.prefix_len).cuda()
+    elif mi.kind in ("dense", "packed"):
+        data = mi.data if mi.kind == "dense" else mi.data.view(np.int64)
+        kw["mask"] = torch.from_numpy(np.ascontiguousarray(data)).cuda()
+    out, lse = ma.attn_decode(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], max(Q_LENS),
+                              max(KV_LENS), w.scale, mask_kind=mi.kind, out_dtype=out_dtype, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 8, 2), (128, 4, 4), (256, 4, 1)])
+def test_decode_mask_kinds(d, hq, hkv):
+    w = _workload(700 + d + hq, d, hq, hkv)
+    dev = device_inputs(w)
+    for name in ("causal", "window", "wide_window", "prefix", "dense", "packed"):
+        _say("decode", d, hq, hkv, name)
+        out, lse = _decode(w, dev, name)
+        ref_o, ref_l = oracle(w, name)
+        err = max_abs_err(out, ref_o)
+        assert err <= TOL_BF16, (name, err)
+        assert lse_err(lse, ref_l) <= 1e-2, name
+
+
+def test_decode_equivalent_forms_bit_identical():
+    """Equal masks in different forms give identical words, hence identical
+    outputs: causal vs its dense rows, a window wider than every context vs
+    causal, dense vs packed."""
+    w = _workload(801, 128, 8, 2)
+    dev = device_inputs(w)
+    c, lc = _decode(w, dev, "causal")
+    for name in ("causal_dense", "wide_window"):
+        o, lo = _decode(w, dev, name)
+        assert torch.equal(o, c) and torch.equal(lo, lc), name
+    o1, l1 = _decode(w, dev, "dense")
+    o2, l2 = _decode(w, dev, "packed")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_bf16_output_and_window_bites():
+    w = _workload(802, 128, 8, 2)
+    dev = device_inputs(w)
+    ob, _ = _decode(w, dev, "window", out_dtype=torch.bfloat16)
+    assert ob.dtype == torch.bfloat16
+    ref_o, _ = oracle(w, "window")
+    assert bf16_out_err(ob, ref_o) <= TOL_BF16
+    # the 37-key window changes the long sequences' outputs
+    oc, _ = _decode(w, dev, "causal")
+    ow, _ = _decode(w, dev, "window")
+    rows = slice(int(w.cu_seqlens_q[3]), int(w.cu_seqlens_q[4]))
+    assert (oc[rows] - ow[rows]).abs().max().item() > 0.05
+
+
+def test_decode_workspace_and_validation():
+    assert ma.attn_decode_workspace(8, 1, 32768, 32, 8, 128) > 0
+    assert ma.attn_decode_workspace(8, 1, 64, 32, 8, 128) == 0
+    w = _workload(803, 64, 4, 2)
+    dev = device_inputs(w)
+    with pytest.raises(ma.MaskAttnError):
+        ma.attn_decode(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], max(Q_LENS), max(KV_LENS),
+                       w.scale, mask_kind="window", window=0)
+    with pytest.raises(ma.MaskAttnError):
+        ma.attn_decode(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], max(Q_LENS), max(KV_LENS),
+                       w.scale, mask_kind="prefix_lm")
+
+
+def test_decode_full_size_sampled():
+    """The decode workload at full size (16 sequences, contexts 4k-16k, 4
+    queries each): causal and a 4096-key window, oracle on sampled heads."""
+    w = W.decode(q_len=4)
+    dev = device_inputs(w)
+    max_kv = int(w.kv_lens.max())
+    rows = {b: np.arange(4) for b in (0, 5, 15)}
+    for name in ("causal", "window"):
+        _say("decode full", name)
+        win = w.masks[name].window if name == "window" else 0
+        out, lse = ma.attn_decode(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], 4, max_kv,
+                                  w.scale, mask_kind=name, window=win)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle(w, name, heads=[0, 13, 31], rows=rows)
+        assert max_abs_err(out, ref_o) <= TOL_BF16, name
+        assert lse_err(lse, ref_l) <= 1e-2, name

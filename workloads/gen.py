@@ -304,3 +304,17 @@ def config5(seed=5, q_len=32768, kv_len=29576, dense_keys=24576, blocks=50, bloc
     w.masks["causal"] = MaskInput("causal")
     w.info.update(dense_keys=dense_keys, blocks=blocks, block=block)
     return w
+
+
+# ------------------------------------------------------------------- decode --
+def decode(seed=6, batch=16, q_len=1, ctx_lo=4096, ctx_hi=16384, hq=32, hkv=8, d=128, window=4096):
+    """Masked decode: per sequence the last q_len tokens against a paged
+    context of U[ctx_lo, ctx_hi] keys (the query tokens' own K/V included),
+    GQA hq/hkv, bf16, random page permutation.  Masks: causal, and a sliding
+    window of `window` keys (a Gemma2-style local layer)."""
+    rng = rng_for(seed)
+    kv = rng.integers(ctx_lo, ctx_hi + 1, size=batch)
+    w = _build("decode", rng, "bf16", [q_len] * batch, kv, hq, hkv, d, permute=True)
+    w.masks["causal"] = MaskInput("causal")
+    w.masks["window"] = MaskInput("window", window=window)
+    return w
