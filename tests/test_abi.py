@@ -112,6 +112,31 @@ def test_verify_validation_before_hip():
     assert ma.attn_verify_tree_workspace(0, 64, 4000, 4, 1, 128) == 0
 
 
+def _decode(kind=L.KIND["causal"], window=0, prefix=None, mask=None, numel=0, max_q=1, ws=None, ws_bytes=0,
+            d=128, in_dt=L.BF16, batch=2, max_kv=4000):
+    st = (ctypes.c_int64 * 3)(2048, 128, 128)
+    return L.LIB.attn_decode(FAKE, 2, 4, FAKE, FAKE, 1, d, 16, st, FAKE, 300, FAKE, FAKE, batch, max_q, max_kv,
+                             kind, window, prefix, mask, numel, in_dt, L.F32, 0.1, ws, ws_bytes, FAKE, None, None)
+
+
+def test_decode_validation_before_hip():
+    need = ma.attn_decode_workspace(2, 1, 4000, 4, 1, 128)
+    assert need > 0
+    ok = dict(ws=FAKE, ws_bytes=need)
+    assert _decode(kind=L.KIND["window"], window=0, **ok) == L.MA_ERR_INVALID
+    assert _decode(kind=L.KIND["prefix_lm"], prefix=None, **ok) == L.MA_ERR_INVALID
+    assert _decode(kind=L.KIND["dense"], mask=None, **ok) == L.MA_ERR_INVALID
+    assert _decode(kind=L.KIND["ranges"], **ok) == L.MA_ERR_UNSUPPORTED
+    assert _decode(kind=17, **ok) == L.MA_ERR_INVALID
+    assert _decode(max_q=65, **ok) == L.MA_ERR_UNSUPPORTED
+    assert _decode(d=96, **ok) == L.MA_ERR_UNSUPPORTED
+    assert _decode(in_dt=L.F32, **ok) == L.MA_ERR_UNSUPPORTED
+    assert _decode(ws=FAKE, ws_bytes=need - 1) == L.MA_ERR_SIZE
+    assert ma.attn_decode_workspace(2, 65, 4000, 4, 1, 128) == 0
+    # the same bound serves tree verify: a 64-row tree needs more than decode
+    assert ma.attn_verify_tree_workspace(2, 64, 4000, 4, 1, 128) >= need
+
+
 def test_status_strings():
     for s in range(-7, 1):
         assert L.LIB.ma_status_string(s).decode()
