@@ -276,6 +276,18 @@ def extra(args):
         kv_bytes = 2 * int(w2.kv_lens.sum()) * w2.hkv * w2.d * 2
         print(json.dumps({"workload": "cfg2", "mask": form, "ms": round(ms, 4), "tflops": round(tf, 2),
                           "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    # causal comparator at the same shape (the same queries, kernel and splits)
+    need = ma.attn_decode_workspace(w2.batch, 64, int(w2.kv_lens.max()), w2.hq, w2.hkv, w2.d)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+
+    def cstep():
+        ma.attn_decode(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], 64, int(w2.kv_lens.max()),
+                       w2.scale, mask_kind="causal", workspace=ws, out=out, lse=lse)
+    ms = time_steps(cstep, 50, 10, torch.cuda.current_stream())
+    n = sum(64 * int(c) + 64 * 65 // 2 for c in w2.info["ctx"])
+    tf = 4.0 * w2.d * w2.hq * n / (ms * 1e-3) / 1e12
+    print(json.dumps({"workload": "cfg2", "mask": "causal", "ms": round(ms, 4), "tflops": round(tf, 2),
+                      "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def decode_lines(steps, warmup):

@@ -149,27 +149,47 @@ __device__ __forceinline__ uint64_t row_word(const VerifyParams &p, int64_t moff
   }
 }
 
-// The lane's row word for k-tile kt.  A dense mask is read one row at a time
-// across the wave: lane j loads byte j of row i's 64, a ballot forms the
-// word, and the lanes holding row i keep it (rows of the wave: r0 .. r0+31).
+// Bits (LSB = lowest address) of the nonzero bytes of a dword: per byte the
+// high bit is set iff the byte is nonzero (SWAR), then one multiply moves the
+// four high bits to bits 21..24 (distinct partial products, no carries).
+__device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t x) {
+  const uint32_t t = ((((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) >> 7) & 0x01010101u;
+  return ((t * 0x00204081u) >> 21) & 0xFu;
+}
+
+// The lane's row word for k-tile kt.  A dense mask is read by lane pairs:
+// lanes 2i and 2i + 1 load the two 32-byte halves of wave row i's 64 bytes
+// (two 16-byte loads each, one coalesced 2 KB read per wave), turn them into
+// 32 bits, and the lanes holding row i (i and i + 32) take both halves with
+// two shuffles (rows of the wave: r0 .. r0+31).
 __device__ __forceinline__ uint64_t fetch_word(const VerifyParams &p, int64_t moff, int plen, int t, bool ok,
                                                int r0, int q_len, int kv, int kt, int lane) {
   if (p.mode != kDense) return row_word(p, moff, plen, t, ok, q_len, kv, kt);
-  const int keys = min(64, kv - 64 * kt);
-  const uint8_t *m8 = (const uint8_t *)p.mask;
-  uint64_t w = 0;
-  for (int i = 0; i < 32; ++i) {
-    const int r = r0 + i;
-    const int ti = r % p.qs;
-    bool bit = false;
-    if (r / p.qs < p.gh && ti < q_len && lane < keys) {
-      const int64_t idx = moff + (int64_t)ti * kv + 64 * kt + lane;
-      bit = idx < p.mask_numel && m8[idx] != 0;
+  const int i = lane >> 1, half = lane & 1;
+  const int r = r0 + i;
+  const int ti = r % p.qs;
+  uint32_t bits = 0;
+  if (r / p.qs < p.gh && ti < q_len) {
+    const uint8_t *m8 = (const uint8_t *)p.mask;
+    const int64_t base = moff + (int64_t)ti * kv + 64 * kt + 32 * half;
+    const int nb = min(32, kv - 64 * kt - 32 * half);   // this half's bytes inside the row
+    if (nb == 32 && base + 32 <= p.mask_numel) {
+      u32x4 v0, v1;
+      __builtin_memcpy(&v0, m8 + base, 16);
+      __builtin_memcpy(&v1, m8 + base + 16, 16);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bits |= nonzero_bytes4(v0[c]) << (4 * c);
+        bits |= nonzero_bytes4(v1[c]) << (16 + 4 * c);
+      }
+    } else {
+      for (int j = 0; j < nb; ++j)
+        if (base + j < p.mask_numel && m8[base + j] != 0) bits |= 1u << j;
     }
-    const uint64_t word = __ballot(bit);
-    if ((lane & 31) == i) w = word;
   }
-  return w;
+  const int src = 2 * (lane & 31);
+  const uint32_t lo = __shfl(bits, src, 64), hi_bits = __shfl(bits, src + 1, 64);
+  return ((uint64_t)hi_bits << 32) | lo;
 }
 
 // UP: pages hold at least the key rows of one gather instruction, so page
