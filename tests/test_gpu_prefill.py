@@ -41,6 +41,37 @@ def test_config1_host_and_device_classify_agree():
     assert np.array_equal(c1, c2) and np.array_equal(w1, w2)
 
 
+@pytest.mark.parametrize("tile_q", [64, 128])
+def test_device_classify_matches_host_compile(tile_q):
+    """Device-classified dense and packed masks give the host compiler's
+    classes and words bit for bit: ragged rows (q_len not a multiple of the
+    tile), contexts spanning several 64-tile chunks with a ragged tail, FULL,
+    SKIP and PARTIAL tiles, empty and one-key rows."""
+    rng = np.random.default_rng(900 + tile_q)
+    q_lens, kv_lens = [300, 5, 130], [4500, 70, 8300]
+    dense = []
+    for q, k in zip(q_lens, kv_lens):
+        m = rng.random((q, k)) < 0.2
+        m[:, : min(k, 256)] = True          # FULL tiles
+        m[:, k // 2: k // 2 + 700] = False   # SKIP tiles
+        m[q // 2, :] = False                 # an empty row
+        m[q - 1, :] = False
+        m[q - 1, k - 1] = True               # a one-key row in the tail tile
+        dense.append(m)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    kv = np.asarray(kv_lens, np.int32)
+    flat = np.concatenate([m.astype(np.uint8).reshape(-1) for m in dense])
+    packed = np.concatenate([W.pack_rows(m).reshape(-1) for m in dense])
+    host = ma.mask_compile_host("dense", cu, kv, mask=flat, tile_q=tile_q)
+    hc, hw = host.export()
+    for kind, data in (("dense", flat), ("packed", packed.view(np.int64))):
+        _say("device classify", kind, tile_q)
+        p = ma.mask_compile(kind, cu, kv, mask=torch.from_numpy(np.ascontiguousarray(data)).cuda(), tile_q=tile_q)
+        dc, dw = p.export()
+        assert np.array_equal(dc, hc), kind
+        assert np.array_equal(dw, hw), kind
+
+
 # ------------------------------------------- small ragged bf16 shapes, all d --
 def _ragged(seed, d, hq, hkv, q_lens, kv_lens, permute=True):
     rng = W.rng_for(seed)
