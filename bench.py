@@ -12,7 +12,7 @@ Effective TFLOP/s counts 4 * d * Hq FLOPs per unmasked (query, key) entry
 (2d for Q K^T and 2d for P V); masked entries, skipped tiles and the softmax
 are not counted.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--decode] [--classify]
 """
 
 import argparse
@@ -147,11 +147,20 @@ def main():
                     help="time only the headline kernel (no comparator, no CPU baseline): for profilers")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--decode", action="store_true", help="print only the decode lines")
+    ap.add_argument("--classify", action="store_true",
+                    help="print only the device mask-classify lines (block mask, packed and dense)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    if args.decode or args.classify:
+        if args.decode:
+            decode_lines(args.steps, args.warmup)
+        if args.classify:
+            classify_lines(args.steps)
+        return
 
     import torch
     import workloads as W
@@ -327,6 +336,36 @@ def decode_lines(steps, warmup):
                               "kv_gbs": round(gbs, 1), "pct_of_hbm": round(100 * gbs / 8000.0, 1),
                               "batch": w.batch, "kv_total": int(w.kv_lens.sum())}), flush=True)
         del dev
+
+
+def classify_lines(steps):
+    """Device mask classify (an HBM scan) on the 32768 x 29576 block mask,
+    packed (121 MB) and dense (969 MB).  The wall time of mask_compile covers
+    the host part too (metadata upload and a stream sync); the kernel's own
+    time comes from a kernel trace."""
+    import time
+    import numpy as np
+    import torch
+    import workloads as W
+    import masked_flash_attention_mask_amd as ma
+    w = W.config5()
+    q, k = int(w.q_lens[0]), int(w.kv_lens[0])
+    words = w.masks["custom_packed"].data
+    dense = np.unpackbits(words.view(np.uint8).reshape(q, -1), axis=1, bitorder="little")[:, :k]
+    forms = (("packed", torch.from_numpy(np.ascontiguousarray(words.view(np.int64))).cuda()),
+             ("dense", torch.from_numpy(np.ascontiguousarray(dense)).cuda()))
+    for kind, m in forms:
+        for _ in range(3):
+            ma.mask_compile(kind, w.cu_seqlens_q, w.kv_lens, mask=m)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            ma.mask_compile(kind, w.cu_seqlens_q, w.kv_lens, mask=m)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t) / steps * 1e3
+        nbytes = m.numel() * m.element_size()
+        print(json.dumps({"workload": "cfg5_classify", "form": kind, "mask_bytes": nbytes,
+                          "compile_ms": round(ms, 4)}), flush=True)
 
 
 def _anc(parents, i):
