@@ -1,7 +1,7 @@
 /*
- * maskattn — masked flash-attention prefill, speculative tree verify and
- * masked decode over ragged sequences with paged K/V, for AMD Instinct MI355X
- * (gfx950).
+ * maskattn — masked flash-attention prefill (and its backward), speculative
+ * tree verify and masked decode over ragged sequences with paged K/V, for AMD
+ * Instinct MI355X (gfx950).
  *
  * C ABI of libmaskattn.so.  Plain pointers and sizes only.  "host" and
  * "device" below say where a pointer must point.  Streams are hipStream_t
@@ -201,6 +201,44 @@ ma_status attn_prefill_masked(const ma_plan *plan, const void *q, int64_t total_
                               int32_t page_size, const int64_t kv_strides[3],
                               const int32_t *page_table, int32_t max_pages, int32_t in_dtype,
                               int32_t out_dtype, float scale, void *out, float *lse, void *stream);
+
+/* Workspace bytes attn_backward_masked needs for this plan and Hq (two fp32
+ * values per (query, head)); 0 for a NULL plan or hq < 1. */
+size_t attn_backward_workspace(const ma_plan *plan, int32_t hq);
+
+/* Gradients of masked prefill over the same plan (the training-side cost of
+ * masks made of many small ranges is the motivation of the feature request
+ * "chunk-causal mask type for Flex Flash Attention", MagiAttention issue 316,
+ * problem statement).  With P = exp(scale Q K^T - LSE) on visible entries:
+ * D = rowsum(dO * O), dS = P (dO V^T - D), dQ = scale dS K, dK = scale dS^T Q,
+ * dV = P^T dO; a K/V head sums its GQA group's query heads.
+ *  q, k_cache, v_cache, page_table, page_size, kv_strides, max_pages: as for
+ *           attn_prefill_masked (bf16 inputs)
+ *  out      device [total_q, Hq, d] of out_dtype (BF16 or F32): the forward's
+ *           output;  lse  device fp32 [total_q, Hq]: the forward's LSE (-inf
+ *           for a row with no visible key)
+ *  dout     device bf16 [total_q, Hq, d], contiguous
+ *  dq       device fp32 [total_q, Hq, d]: every element written (0 for rows
+ *           with no visible key)
+ *  dk_cache, dv_cache  device fp32 caches with the element strides of
+ *           k_cache: the slot of every key below kv_len is written once (0
+ *           when no query sees the key); other slots are not touched.  No two
+ *           sequences may map keys to the same slot.
+ *  workspace device, >= attn_backward_workspace(plan, hq) bytes, scratch.
+ * Supported: d in {64, 128}; plans with tile_k 64 and tile_q 64 or 128.
+ * The first call on a plan builds its key-major transpose (one device
+ * allocation, held until mask_plan_destroy; synchronises `stream` once);
+ * later calls only launch.  Arithmetic: bf16 matrix products (P and dS
+ * rounded to bf16 for theirs) with fp32 accumulation.  Deterministic: no
+ * atomics; each gradient element is summed by one workgroup in a fixed order.
+ * Errors: INVALID (NULL arguments, bad shapes), SIZE (workspace too small),
+ * PLAN_MISMATCH (total_q or tiles), UNSUPPORTED (d, dtype), NOMEM / HIP. */
+ma_status attn_backward_masked(ma_plan *plan, const void *q, int64_t total_q, int32_t hq, const void *k_cache,
+                               const void *v_cache, int32_t hkv, int32_t d, int32_t page_size,
+                               const int64_t kv_strides[3], const int32_t *page_table, int32_t max_pages,
+                               const void *out, int32_t out_dtype, const void *dout, const float *lse,
+                               float scale, float *dq, float *dk_cache, float *dv_cache, void *workspace,
+                               size_t ws_bytes, void *stream);
 
 /* Workspace bytes attn_verify_tree needs for these bounds. */
 size_t attn_verify_tree_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq,

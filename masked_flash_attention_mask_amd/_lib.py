@@ -23,7 +23,8 @@ TILE_SKIP, TILE_FULL, TILE_PARTIAL = 0, 1, 2
 
 EXPORTS = ["mask_compile", "mask_compile_host", "mask_plan_upload", "mask_plan_destroy",
            "mask_plan_info_get", "mask_plan_export", "mask_plan_serialize", "attn_prefill_masked",
-           "attn_verify_tree_workspace", "attn_verify_tree", "attn_decode_workspace", "attn_decode",
+           "attn_backward_workspace", "attn_backward_masked", "attn_verify_tree_workspace", "attn_verify_tree",
+           "attn_decode_workspace", "attn_decode",
            "ma_status_string", "ma_last_error"]
 
 
@@ -69,6 +70,9 @@ def _load():
         "mask_plan_serialize": (i32, [vp, vp, ctypes.POINTER(sz)]),
         "attn_prefill_masked": (i32, [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, i32, i32, f32,
                                       vp, vp, vp]),
+        "attn_backward_workspace": (sz, [vp, i32]),
+        "attn_backward_masked": (i32, [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, vp, i32, vp, vp, f32,
+                                       vp, vp, vp, vp, sz, vp]),
         "attn_verify_tree_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
         "attn_verify_tree": (i32, [vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp, i32, i32, i32,
                                    i32, vp, i64, i32, i32, f32, vp, sz, vp, vp, vp]),
@@ -244,6 +248,48 @@ def attn_prefill_masked(plan, q, k_cache, v_cache, page_table, scale, out=None, 
         float(scale), out.data_ptr(), lse.data_ptr() if lse is not False else None, _stream(stream))
     check(st, "attn_prefill_masked")
     return out, lse
+
+
+def attn_backward_workspace(plan, hq):
+    return int(LIB.attn_backward_workspace(plan.handle, hq))
+
+
+def attn_backward_masked(plan, q, k_cache, v_cache, page_table, out, lse, dout, scale, dq=None, dk_cache=None,
+                         dv_cache=None, workspace=None, stream=None):
+    """Gradients of attn_prefill_masked given its out and lse and the upstream
+    gradient dout (bf16, like q).  Returns fp32 (dq [total_q, Hq, d],
+    dk_cache, dv_cache); the caches take k_cache's shape and strides, and
+    slots of no key are left as passed (zero when allocated here)."""
+    import torch
+    for t in (q, page_table, out, lse, dout):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("backward tensors must be contiguous device tensors")
+    if dout.shape != q.shape or dout.dtype != q.dtype or out.shape != q.shape:
+        raise ValueError("out and dout must match q's shape (dout also its dtype)")
+    total_q, hq, d = q.shape
+    hkv, page_size = k_cache.shape[2], k_cache.shape[1]
+    strides = _cache_args(k_cache, v_cache)
+    if dq is None:
+        dq = torch.empty((total_q, hq, d), dtype=torch.float32, device=q.device)
+    grads = []
+    for g in (dk_cache, dv_cache):
+        if g is None:
+            g = torch.zeros_like(k_cache, dtype=torch.float32)
+        if g.dtype != torch.float32 or g.shape != k_cache.shape or g.stride() != k_cache.stride():
+            raise ValueError("dk_cache and dv_cache must be fp32 with k_cache's shape and strides")
+        grads.append(g)
+    need = attn_backward_workspace(plan, hq)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = LIB.attn_backward_masked(
+        plan.handle, q.data_ptr(), total_q, hq, k_cache.data_ptr(), v_cache.data_ptr(), hkv, d, page_size, strides,
+        page_table.data_ptr(), page_table.shape[1], out.data_ptr(), _dtype_code(out.dtype), dout.data_ptr(),
+        lse.data_ptr(), float(scale), dq.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), ws_ptr, ws_bytes,
+        _stream(stream))
+    check(st, "attn_backward_masked")
+    return dq, grads[0], grads[1]
 
 
 def attn_verify_tree_workspace(batch, max_q, max_kv, hq, hkv, d):

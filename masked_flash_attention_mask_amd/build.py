@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmaskattn.so")
-SOURCES = ["abi.cpp", "plan.cpp", "attn_fwd.hip", "mask_classify.hip", "verify.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "attn_fwd.hip", "mask_classify.hip", "verify.hip", "attn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are disabled on purpose: plain scalar fp32 code

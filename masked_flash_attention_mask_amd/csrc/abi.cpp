@@ -113,13 +113,7 @@ ma_status mask_plan_upload(ma_plan *plan, void *stream) {
 
 ma_status mask_plan_destroy(ma_plan *plan) {
   if (!plan) return MA_OK;
-  if (plan->dbuf) {
-    int cur = 0;
-    (void)hipGetDevice(&cur);
-    if (plan->device_id >= 0 && plan->device_id != cur) (void)hipSetDevice(plan->device_id);
-    (void)hipFree(plan->dbuf);
-    if (plan->device_id >= 0 && plan->device_id != cur) (void)hipSetDevice(cur);
-  }
+  if (plan->dbuf || plan->kbuf) plan_free_device(plan);
   delete plan;
   return MA_OK;
 }
@@ -268,6 +262,73 @@ ma_status attn_prefill_masked(const ma_plan *plan, const void *q, int64_t total_
   a.lse = lse;
   a.stream = stream;
   return launch_prefill(a);
+}
+
+size_t attn_backward_workspace(const ma_plan *plan, int32_t hq) {
+  if (!plan || hq < 1) return 0;
+  return backward_workspace(plan->total_q, hq);
+}
+
+ma_status attn_backward_masked(ma_plan *plan, const void *q, int64_t total_q, int32_t hq, const void *k_cache,
+                               const void *v_cache, int32_t hkv, int32_t d, int32_t page_size,
+                               const int64_t kv_strides[3], const int32_t *page_table, int32_t max_pages,
+                               const void *out, int32_t out_dtype, const void *dout, const float *lse,
+                               float scale, float *dq, float *dk_cache, float *dv_cache, void *workspace,
+                               size_t ws_bytes, void *stream) {
+  clear_error();
+  if (!plan) return set_error(MA_ERR_INVALID, "plan is NULL");
+  ma_status st = check_paged(q, k_cache, v_cache, out, page_table, hq, hkv, page_size, kv_strides,
+                             max_pages, scale);
+  if (st != MA_OK) return st;
+  if (!dout || !lse || !dq || !dk_cache || !dv_cache)
+    return set_error(MA_ERR_INVALID, "dout, lse, dq, dk_cache and dv_cache are required");
+  if (total_q != plan->total_q)
+    return set_error(MA_ERR_PLAN_MISMATCH, "total_q %lld differs from the plan's %lld",
+                     (long long)total_q, (long long)plan->total_q);
+  if (plan->tile_k != 64 || (plan->tile_q != 64 && plan->tile_q != 128))
+    return set_error(MA_ERR_PLAN_MISMATCH, "plan tiles %dx%d have no backward kernel", plan->tile_q, plan->tile_k);
+  for (int b = 0; b < plan->batch; ++b)
+    if ((int64_t)max_pages * page_size < plan->kv_len[b])
+      return set_error(MA_ERR_INVALID, "page table (max_pages %d x page_size %d) shorter than kv_len %d",
+                       max_pages, page_size, plan->kv_len[b]);
+  if (d != 64 && d != 128) return set_error(MA_ERR_UNSUPPORTED, "backward head_dim %d (supported: 64, 128)", d);
+  if (out_dtype != MA_BF16 && out_dtype != MA_F32)
+    return set_error(MA_ERR_UNSUPPORTED, "out dtype %d", out_dtype);
+  if (kv_strides[2] < d) return set_error(MA_ERR_INVALID, "head stride %lld < head_dim", (long long)kv_strides[2]);
+  if (total_q == 0 || plan->num_rows == 0) return MA_OK;
+  const size_t need = backward_workspace(total_q, hq);
+  if (!workspace || ws_bytes < need)
+    return set_error(MA_ERR_SIZE, "workspace of %zu bytes is below the %zu required", ws_bytes, need);
+  if (!plan->on_device) {
+    st = plan_upload(plan, stream);
+    if (st != MA_OK) return st;
+  }
+  BackwardArgs a{};
+  a.plan = plan;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.page_shift = log2i(page_size);
+  a.total_q = total_q;
+  a.s_page = kv_strides[0];
+  a.s_slot = kv_strides[1];
+  a.s_head = kv_strides[2];
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.o_dtype = out_dtype;
+  a.scale = scale;
+  a.dq = dq;
+  a.dk = dk_cache;
+  a.dv = dv_cache;
+  a.workspace = workspace;
+  a.stream = stream;
+  return launch_backward(a);
 }
 
 size_t attn_verify_tree_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq,

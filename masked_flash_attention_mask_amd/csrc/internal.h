@@ -69,6 +69,13 @@ struct ma_plan {
   size_t dbytes = 0;
   size_t off_seqs = 0, off_aux = 0, off_items = 0, off_entries = 0, off_words = 0;
   int64_t cap_entries = 0, cap_wblk = 0;
+
+  // k-major transpose for the backward (built on first use): one item per
+  // (sequence, k-tile), every k-tile included, entries (q-tile | class,
+  // word block) in ascending q-tile order, items most work first.
+  void *kbuf = nullptr;
+  size_t off_kitems = 0, off_kentries = 0;
+  int32_t num_kitems = 0;
 };
 
 namespace maskattn {
@@ -85,6 +92,10 @@ ma_status plan_upload(ma_plan *p, void *stream);
 void fill_seqinfo(const ma_plan *p, int32_t kind, std::vector<SeqInfo> &s, std::vector<SeqAux> &aux);
 ma_status plan_fetch_host_view(const ma_plan *p, std::vector<Item> &items,
                                std::vector<Entry> &entries, std::vector<uint64_t> &words);
+// Builds and uploads the k-major transpose (KItem.qt holds the k-tile; the
+// entries' first field holds q-tile | class << 30).  Synchronises `stream`.
+ma_status plan_build_kmajor(ma_plan *p, void *stream);
+void plan_free_device(ma_plan *p);
 
 // mask_classify.hip
 ma_status launch_classify(ma_plan *p, const void *mask, int32_t kind, int64_t mask_numel,
@@ -105,6 +116,25 @@ struct PrefillArgs {
   void *stream;
 };
 ma_status launch_prefill(const PrefillArgs &a);
+
+// attn_bwd.hip
+struct BackwardArgs {
+  ma_plan *plan;
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  int32_t hq, hkv, d, page_shift;
+  int64_t total_q;
+  int64_t s_page, s_slot, s_head;
+  const int32_t *page_table;
+  int32_t max_pages;
+  int32_t o_dtype;
+  float scale;
+  float *dq, *dk, *dv;
+  void *workspace;
+  void *stream;
+};
+size_t backward_workspace(int64_t total_q, int32_t hq);
+ma_status launch_backward(const BackwardArgs &a);
 
 // verify.hip
 struct VerifyArgs {

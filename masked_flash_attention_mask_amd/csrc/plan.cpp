@@ -509,4 +509,74 @@ ma_status plan_fetch_host_view(const ma_plan *p, std::vector<Item> &items, std::
   return MA_OK;
 }
 
+ma_status plan_build_kmajor(ma_plan *p, void *stream) {
+  if (p->kbuf) return MA_OK;
+  std::vector<Item> items;
+  std::vector<Entry> ents;
+  std::vector<uint64_t> words;
+  ma_status st = plan_fetch_host_view(p, items, ents, words);
+  if (st != MA_OK) return st;
+  // Bucket every non-SKIP tile by (sequence, k-tile); q-tiles ascending.
+  std::vector<int64_t> kbase(p->batch + 1, 0);
+  for (int b = 0; b < p->batch; ++b) kbase[b + 1] = kbase[b] + p->nkt[b];
+  const int64_t nk = kbase[p->batch];
+  if (nk > INT32_MAX) return set_error(MA_ERR_UNSUPPORTED, "too many k-tiles for the backward");
+  std::vector<std::vector<Entry>> bucket((size_t)nk);
+  for (const Item &it : items)
+    for (int32_t e = it.ent_begin; e < it.ent_end; ++e) {
+      const int32_t kt = entry_kt(ents[e].kt_cls), cls = entry_cls(ents[e].kt_cls);
+      bucket[(size_t)(kbase[it.seq] + kt)].push_back(Entry{it.qt | (cls << kClsShift), ents[e].wblk});
+    }
+  std::vector<Item> kitems;
+  std::vector<Entry> kents;
+  kitems.reserve((size_t)nk);
+  for (int b = 0; b < p->batch; ++b)
+    for (int32_t kt = 0; kt < p->nkt[b]; ++kt) {
+      std::vector<Entry> &bk = bucket[(size_t)(kbase[b] + kt)];
+      std::sort(bk.begin(), bk.end(), [](const Entry &x, const Entry &y) {
+        return entry_kt(x.kt_cls) < entry_kt(y.kt_cls);
+      });
+      if (kents.size() + bk.size() > (size_t)INT32_MAX)
+        return set_error(MA_ERR_UNSUPPORTED, "plan has too many tiles for the backward");
+      Item it{b, kt, (int32_t)kents.size(), 0};
+      kents.insert(kents.end(), bk.begin(), bk.end());
+      it.ent_end = (int32_t)kents.size();
+      kitems.push_back(it);
+    }
+  std::stable_sort(kitems.begin(), kitems.end(), [](const Item &x, const Item &y) {
+    return (x.ent_end - x.ent_begin) > (y.ent_end - y.ent_begin);
+  });
+  const size_t off_ke = align_up(sizeof(Item) * std::max<size_t>(kitems.size(), 1), 256);
+  const size_t bytes = off_ke + sizeof(Entry) * std::max<size_t>(kents.size(), 1);
+  std::vector<char> h(bytes, 0);
+  memcpy(h.data(), kitems.data(), sizeof(Item) * kitems.size());
+  memcpy(h.data() + off_ke, kents.data(), sizeof(Entry) * kents.size());
+  void *buf = nullptr;
+  hipError_t e = hipMalloc(&buf, bytes);
+  if (e != hipSuccess) return set_error(MA_ERR_NOMEM, "hipMalloc(%zu) for the k-major plan: %s", bytes, hipGetErrorString(e));
+  e = hipMemcpyAsync(buf, h.data(), bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);  // h is freed on return
+  if (e != hipSuccess) {
+    (void)hipFree(buf);
+    return set_error(MA_ERR_HIP, "k-major plan upload: %s", hipGetErrorString(e));
+  }
+  p->kbuf = buf;
+  p->off_kitems = 0;
+  p->off_kentries = off_ke;
+  p->num_kitems = (int32_t)kitems.size();
+  return MA_OK;
+}
+
+void plan_free_device(ma_plan *p) {
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  const bool other = p->device_id >= 0 && p->device_id != cur;
+  if (other) (void)hipSetDevice(p->device_id);
+  if (p->dbuf) (void)hipFree(p->dbuf);
+  if (p->kbuf) (void)hipFree(p->kbuf);
+  if (other) (void)hipSetDevice(cur);
+  p->dbuf = nullptr;
+  p->kbuf = nullptr;
+}
+
 }  // namespace maskattn

@@ -11,6 +11,12 @@ from oracle import masks as OM
 
 TOL_F32 = 1e-5      # fp32 inputs, fp32 accumulation
 TOL_BF16 = 1.5e-2   # bf16 inputs, fp32 accumulation, fp32 output
+# Backward (grad_err below): the kernels round P and dS to bf16 (unit
+# roundoff u = 2^-9) before their products and accumulate in fp32, so each
+# gradient element is off by about u times the RMS of its terms; 2^-5 = 16u
+# leaves room for the max over a row against the row's RMS.  A wrong index,
+# sign, scale or a dropped term moves a row by O(1) of its RMS.
+TOL_GRAD = 2.0 ** -5
 
 
 def compile_plan(w, mask_name, tile_q=128, device_mask=True):
@@ -64,6 +70,24 @@ def lse_err(gpu_lse, ref_lse):
     fin = sel & np.isfinite(ref_lse)
     assert np.array_equal(np.isneginf(g[sel]), np.isneginf(ref_lse[sel])), "fully masked rows differ"
     return float(np.abs(g[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
+
+
+def grad_err(gpu, ref):
+    """Largest error of a gradient row (the last axis) relative to that row's
+    reference RMS, plus a floor of 2^-8 of the whole tensor's RMS for rows
+    whose exact gradient is (near) zero.  Rows the oracle left NaN (heads it
+    did not compute) are skipped; every compared GPU value must be finite."""
+    d = ref.shape[-1]
+    g = gpu.float().cpu().numpy().astype(np.float64).reshape(-1, d)
+    r = ref.reshape(-1, d)
+    sel = ~np.isnan(r).any(axis=1)
+    g, r = g[sel], r[sel]
+    assert np.isfinite(g).all(), "GPU gradient has a non-finite value"
+    rms_row = np.sqrt((r ** 2).mean(axis=1))
+    floor = 2.0 ** -8 * np.sqrt((r ** 2).mean()) if r.size else 0.0
+    if not r.size:
+        return 0.0
+    return float((np.abs(g - r).max(axis=1) / (rms_row + floor + 1e-30)).max())
 
 
 def bf16_out_err(gpu_bf16, ref):

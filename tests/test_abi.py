@@ -137,6 +137,27 @@ def test_decode_validation_before_hip():
     assert ma.attn_verify_tree_workspace(2, 64, 4000, 4, 1, 128) >= need
 
 
+def _backward(plan, d=128, out_dt=L.BF16, total_q=8, ws=FAKE, ws_bytes=1 << 20, dout=FAKE, lse=FAKE, maxp=300):
+    st = (ctypes.c_int64 * 3)(2048, 128, 128)
+    return L.LIB.attn_backward_masked(plan.handle if plan else None, FAKE, total_q, 4, FAKE, FAKE, 1, d, 16, st,
+                                      FAKE, maxp, FAKE, out_dt, dout, lse, 0.1, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_backward_validation_before_hip():
+    plan = ma.mask_compile_host("causal", [0, 8], [8])
+    need = ma.attn_backward_workspace(plan, 4)
+    assert need == 2 * 8 * 4 * 4
+    assert _backward(None) == L.MA_ERR_INVALID
+    assert _backward(plan, dout=None) == L.MA_ERR_INVALID
+    assert _backward(plan, lse=None) == L.MA_ERR_INVALID
+    assert _backward(plan, total_q=9) == L.MA_ERR_PLAN_MISMATCH
+    assert _backward(plan, d=256) == L.MA_ERR_UNSUPPORTED
+    assert _backward(plan, out_dt=7) == L.MA_ERR_UNSUPPORTED
+    assert _backward(plan, ws_bytes=need - 1) == L.MA_ERR_SIZE
+    assert _backward(plan, ws=None) == L.MA_ERR_SIZE
+    assert plan.info().on_device == 0       # nothing was uploaded
+
+
 def test_status_strings():
     for s in range(-7, 1):
         assert L.LIB.ma_status_string(s).decode()

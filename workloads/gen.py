@@ -318,3 +318,51 @@ def decode(seed=6, batch=16, q_len=1, ctx_lo=4096, ctx_hi=16384, hq=32, hkv=8, d
     w.masks["causal"] = MaskInput("causal")
     w.masks["window"] = MaskInput("window", window=window)
     return w
+
+
+# ----------------------------------------------------------------- backward --
+def upstream_grad(w, seed):
+    """dO for a backward pass: N(0, 1) of q's shape, rounded to bf16 (kept as
+    the float32 values of those bf16 numbers), drawn from PCG64(seed)."""
+    g = rng_for(seed).standard_normal(w.q.shape, dtype=np.float32)
+    return round_bf16(g)
+
+
+def backward_small(seed=7, d=128, hq=4, hkv=2, q_lens=(300, 5, 130, 64, 1, 200),
+                   kv_lens=(900, 70, 130, 1000, 1, 200)):
+    """Ragged batch for backward parity: tails in every tile direction, a
+    one-key sequence, q_len = kv_len and q_len << kv_len, GQA, bf16, random
+    page permutation.  Masks: causal, a 37-key window, PrefixLM (prefix
+    uniform in [0, kv_len]), a range list (a causal prefix of a third of the
+    rows plus CHUNK_CAUSAL with chunk 16, and one INV_CAUSAL block), and a
+    Bernoulli(0.3) custom mask with an empty row and a one-key row per
+    sequence (q_len > 2), as dense bytes and as packed words."""
+    rng = rng_for(seed)
+    q_lens, kv_lens = list(q_lens), list(kv_lens)
+    plen = np.array([rng.integers(0, k + 1) for k in kv_lens], np.int32)
+    dense = []
+    for q, k in zip(q_lens, kv_lens):
+        m = rng.random((q, k)) < 0.3
+        if q > 2:
+            m[1, :] = False
+            m[2, :] = False
+            m[2, k - 1] = True
+        dense.append(m)
+    ranges = []
+    for q, k in zip(q_lens, kv_lens):
+        p = q // 3
+        off = k - q
+        rs = [(0, q, 0, off + p, R_CAUSAL, 0)] if p > 0 else []
+        if q > p:
+            rs.append((p, q, 0, k, R_CHUNK_CAUSAL, 16))
+        if q >= 8 and k >= 8:
+            rs.append((0, 8, k - 8, k, R_INV_CAUSAL, 0))
+        ranges.append(rs)
+    w = _build(f"bwd{seed}", rng, "bf16", q_lens, kv_lens, hq, hkv, d, permute=True)
+    w.masks["causal"] = MaskInput("causal")
+    w.masks["window"] = MaskInput("window", window=37)
+    w.masks["prefix_lm"] = MaskInput("prefix_lm", prefix_len=plen)
+    w.masks["ranges"] = MaskInput("ranges", ranges=ranges)
+    w.masks["dense"] = MaskInput("dense", data=np.concatenate([m.astype(np.uint8).reshape(-1) for m in dense]))
+    w.masks["packed"] = MaskInput("packed", data=np.concatenate([pack_rows(m).reshape(-1) for m in dense]))
+    return w
