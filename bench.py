@@ -12,7 +12,12 @@ Effective TFLOP/s counts 4 * d * Hq FLOPs per unmasked (query, key) entry
 (2d for Q K^T and 2d for P V); masked entries, skipped tiles and the softmax
 are not counted.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--decode] [--classify]
+Backward lines (--backward, and under --all) time dQ, dK and dV of the same
+workload through the same plan, counting 10 * d * Hq FLOPs per unmasked entry
+(the five products S, dP, dV, dQ, dK; the kernels recompute S and dP once
+more, which is not counted).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--decode] [--classify] [--backward]
 """
 
 import argparse
@@ -150,16 +155,19 @@ def main():
     ap.add_argument("--decode", action="store_true", help="print only the decode lines")
     ap.add_argument("--classify", action="store_true",
                     help="print only the device mask-classify lines (block mask, packed and dense)")
+    ap.add_argument("--backward", action="store_true", help="print only the backward lines")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
-    if args.decode or args.classify:
+    if args.decode or args.classify or args.backward:
         if args.decode:
             decode_lines(args.steps, args.warmup)
         if args.classify:
             classify_lines(args.steps)
+        if args.backward:
+            backward_lines(args.steps, args.warmup)
         return
 
     import torch
@@ -230,6 +238,7 @@ def main():
     if args.all:
         extra(args)
         decode_lines(args.steps, args.warmup)
+        backward_lines(args.steps, args.warmup)
 
 
 def extra(args):
@@ -336,6 +345,39 @@ def decode_lines(steps, warmup):
                               "kv_gbs": round(gbs, 1), "pct_of_hbm": round(100 * gbs / 8000.0, 1),
                               "batch": w.batch, "kv_total": int(w.kv_lens.sum())}), flush=True)
         del dev
+
+
+def backward_lines(steps, warmup):
+    """Backward (dQ, dK, dV) of the headline workload and of causal at the
+    same shape, each through its plan, forward outputs resident."""
+    import torch
+    import workloads as W
+    import masked_flash_attention_mask_amd as ma
+    from workloads.device import device_inputs, plan_kwargs
+    seq, prefix, cs, hq, d = 16384, 1024, 2, 16, 128
+    w = W.config4(seq=seq, prefix=prefix, hq=hq, d=d, chunk_sizes=(cs,))
+    dev = device_inputs(w)
+    do = torch.from_numpy(W.upstream_grad(w, 4001)).cuda().to(torch.bfloat16).contiguous()
+    stream = torch.cuda.current_stream()
+    for name, n_unmasked in ((f"chunk{cs}", chunk_unmasked(seq, prefix, cs)), ("causal", seq * (seq + 1) // 2)):
+        kind, kw = plan_kwargs(w, name)
+        plan = ma.mask_compile(kind, w.cu_seqlens_q, w.kv_lens, **kw)
+        out, lse = ma.attn_prefill_masked(plan, dev["q"], dev["k"], dev["v"], dev["pt"], w.scale)
+        dq = torch.empty(dev["q"].shape, dtype=torch.float32, device="cuda")
+        dk = torch.zeros(dev["k"].shape, dtype=torch.float32, device="cuda")
+        dv = torch.zeros_like(dk)
+        ws = torch.empty(ma.attn_backward_workspace(plan, hq), dtype=torch.uint8, device="cuda")
+
+        def step():
+            ma.attn_backward_masked(plan, dev["q"], dev["k"], dev["v"], dev["pt"], out, lse, do, w.scale, dq=dq,
+                                    dk_cache=dk, dv_cache=dv, workspace=ws)
+        ms = time_steps(step, steps, warmup, stream)
+        tf = 10.0 * d * hq * n_unmasked / (ms * 1e-3) / 1e12
+        print(json.dumps({"workload": f"backward_{name}_16k", "mask": name, "ms": round(ms, 4),
+                          "tflops": round(tf, 2), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                          "flops_per_step": 10.0 * d * hq * n_unmasked,
+                          "kernels": "bwd_prep, bwd_dq<128,128>, bwd_dkdv<128>"}), flush=True)
+        del plan
 
 
 def classify_lines(steps):

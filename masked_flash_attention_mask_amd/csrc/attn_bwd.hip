@@ -21,6 +21,7 @@
 #include "internal.h"
 #include "kernels_common.h"
 #include "tile_bf16.h"
+#include "tile_dma_bf16.h"
 
 namespace maskattn {
 using namespace dev;
@@ -231,55 +232,91 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq(BwdParams p)
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (k-tile, K/V head), 2 waves x 32 keys.
+// dK, dV: one workgroup per (k-tile, K/V head), 4 waves.  Wave w owns keys
+// 32 (w % 2) .. + 31 of the tile (K and V rows held as B operands) and query
+// rows 32 (w / 2) .. + 31 of every 64-row block; the two waves of a key half
+// add their partial sums at the end.  Query blocks (Q, dO, and per row L2, D
+// and the tile word) are gathered straight into LDS (global_load_lds) one
+// block ahead, into two alternating stages.
 // ---------------------------------------------------------------------------
+
+// One 64-row block of Q or dO in LDS: dense rows of D bf16, 16-byte chunks
+// XOR swizzled by the row so that both the row reads (ds_read_b128 over 16
+// rows, one chunk each) and the transposed reads (ds_read_b64_tr_b16 over 4
+// rows x 4 chunks per half wave) hit distinct banks.  f is a bijection of the
+// row's low bits that keeps 16 consecutive rows on distinct chunks and puts
+// the 4 rows of a transposed read into distinct 4-chunk groups.
 template <int D>
-__global__ __launch_bounds__(128, 1) void bwd_dkdv(BwdParams p) {
-  constexpr int NT = 128, S = BwdStage<D>::S, CH = D / 8;
-  extern __shared__ __align__(16) uint16_t lds[];   // K tile, V tile, Q block, dO block
-  __shared__ float l2s[32], dds[32];
-  __shared__ uint64_t wds[32];
+struct QBlk {
+  static constexpr int CH = D / 8;
+  static constexpr int ELEMS = 64 * D;
+  __host__ __device__ static constexpr int f(int r) {
+    return CH >= 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
+  static constexpr int META = 2 * ELEMS;          // element offset of the row metadata
+  static constexpr int STAGE = META + 4 * 64 * 2;  // Q, dO, then l2, dd, word low, word high (64 x 4 bytes each)
+  static constexpr size_t BYTES = 2 * STAGE * sizeof(uint16_t);   // two stages
+};
+
+__device__ __forceinline__ void lds_load4(const void *src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ Entry load_entry(const Entry *e, int i) {
+  const __attribute__((address_space(4))) Entry *c = (const __attribute__((address_space(4))) Entry *)e;
+  return Entry{c[i].kt_cls, c[i].wblk};
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv(BwdParams p) {
+  using QB = QBlk<D>;
+  constexpr int CH = D / 8, NI = CH / 4;   // gather instructions per wave per matrix
+  extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int item_idx = blockIdx.x / (p.hq / p.group), g = blockIdx.x - item_idx * (p.hq / p.group);
+  const int kh = wave & 1, qh = wave >> 1;
+  const int hkv = p.hq / p.group;
+  const int item_idx = blockIdx.x / hkv, g = blockIdx.x - item_idx * hkv;
   const Item it = p.kitems[item_idx];   // it.qt holds the k-tile
   const SeqInfo sq = p.seqs[it.seq];
-  const int kt = it.qt;
-  const int kv_len = sq.kv_len;
-  const int kin = kv_len - kt * 64;
-  const int kk = wave * 32 + l32;       // this lane's key inside the tile
-  uint16_t *ks = lds, *vs = lds + 64 * S, *qs = lds + 2 * 64 * S, *ds = qs + 32 * S;
+  const int kt = it.qt, kv_len = sq.kv_len;
+  const int kk = 32 * kh + l32;         // the lane's key inside the tile
+  const bool key_ok = kk < kv_len - kt * 64;
+  const int32_t *pt = p.page_table + (int64_t)it.seq * p.max_pages;
+  const int pmask = (1 << p.page_shift) - 1;
+  const int tq = p.tile_q;
 
-  // K and V of the tile -> LDS (clamped keys), then the lane's key rows -> registers
-  {
-    using KV = staged::KvTile<D, NT>;
-    KV kv;
-    const int32_t *pt = p.page_table + (int64_t)it.seq * p.max_pages;
-    const typename KV::Pages pg = kv.pages(pt, p.page_shift, kt, kv_len, tid);
-    kv.load(p.k + (int64_t)g * p.s_head, p.v + (int64_t)g * p.s_head, pg, p.page_shift, p.s_page, p.s_slot, kt,
-            kv_len, tid);
-#pragma unroll
-    for (int i = 0; i < KV::PPT; ++i) {
-      const int pair = tid + i * NT;
-      if (KV::PAIRS % NT == 0 || pair < KV::PAIRS) {
-        const int kg = pair / KV::CH, cc = pair % KV::CH;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          *(u32x4 *)(ks + (4 * kg + j) * S + 8 * cc) = kv.kreg[i][j];
-          *(u32x4 *)(vs + (4 * kg + j) * S + 8 * cc) = kv.vreg[i][j];
-        }
-      }
-    }
-  }
-  __syncthreads();
+  // K and V rows of the lane's key (clamped to the last key) as B operands.
   bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-  for (int k = 0; k < D / 16; ++k) {
-    kf[k] = row_op<D>(ks + wave * 32 * S, l32, hi, k);
-    vf[k] = row_op<D>(vs + wave * 32 * S, l32, hi, k);
+  {
+    const int key = min(kt * 64 + kk, kv_len - 1);
+    const int64_t off =
+        (int64_t)pt[key >> p.page_shift] * p.s_page + (int64_t)(key & pmask) * p.s_slot + (int64_t)g * p.s_head;
+    load_q<D>(kf, p.k + off, true, hi);
+    load_q<D>(vf, p.v + off, true, hi);
   }
-  const bool key_ok = kk < kin;
-  const float c = p.scale_log2;
+
+  // Per-lane LDS offsets (elements) inside a block.  Row reads: row 32 qh +
+  // l32, chunk 2 k + hi, stored at chunk (2 k + hi) ^ f = 2 k ^ (hi ^ f).
+  // Transposed reads: rows 32 qh + 16 u + j (+ 8), j = 4 hi + (lane % 16) / 4,
+  // columns 32 n + 16 ((lane / 16) % 2) + 4 (lane % 4), i.e. chunk 4 n + cb
+  // at 4 n ^ (cb ^ f).  The swizzle depends on the row modulo 16 only.
+  const int rrow = (32 * qh + l32) * D;
+  const int rx = 8 * (hi ^ QB::f(l32));
+  const int j = 4 * hi + ((lane & 15) >> 2);
+  const int trow = (32 * qh + j) * D;
+  const int cb = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tax = 8 * (cb ^ QB::f(j)) + 4 * (lane & 1);
+  const int tbx = 8 * (cb ^ QB::f(j + 8)) + 4 * (lane & 1);
+  auto tr_read = [&](const uint16_t *m, int u, int n) -> bf16x8 {
+    const uint16_t *b = m + trow + 16 * u * D;
+    const i16x4 r0 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(b + ((32 * n) ^ tax)));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(b + 8 * D + ((32 * n) ^ tbx)));
+    const i16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
 
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
@@ -288,74 +325,149 @@ __global__ __launch_bounds__(128, 1) void bwd_dkdv(BwdParams p) {
     dvacc[n] = f32x16{};
   }
 
-  const int tq = p.tile_q;
-  for (int e = it.ent_begin; e < it.ent_end; ++e) {
-    const Entry en = p.kentries[e];
+  // Work list: entries (q-tiles, ascending) x query heads of the group x the
+  // q-tile's 64-row blocks that hold rows of the sequence.
+  const int eb = it.ent_begin, ee = it.ent_end;
+  auto nblk = [&](int e) {
+    const int qt = entry_kt(load_entry(p.kentries, e).kt_cls);
+    return min(tq / 64, (sq.q_len - qt * tq + 63) / 64);
+  };
+  auto issue = [&](int e, int hh, int qb, uint16_t *st) {
+    const Entry en = load_entry(p.kentries, e);
     const int qt = entry_kt(en.kt_cls), cls = entry_cls(en.kt_cls);
-    for (int hh = 0; hh < p.group; ++hh) {
-      const int h = g * p.group + hh;
-      for (int qb = 0; qb < tq / 32; ++qb) {
-        const int t0 = qt * tq + qb * 32;             // first query row of the block
-        if (t0 >= sq.q_len) break;
-        // Q and dO blocks (32 rows), L2, D and the block's row words -> LDS
-        __syncthreads();
-        for (int x = tid; x < 32 * CH; x += NT) {
-          const int r = x / CH, cc = x % CH;
-          const int t = t0 + r;
-          u32x4 qv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
-          if (t < sq.q_len) {
-            const int64_t off = (((int64_t)sq.q_start + t) * p.hq + h) * D + 8 * cc;
-            qv = *(const u32x4 *)(p.q + off);
-            gv = *(const u32x4 *)(p.dout + off);
-          }
-          *(u32x4 *)(qs + r * S + 8 * cc) = qv;
-          *(u32x4 *)(ds + r * S + 8 * cc) = gv;
-        }
-        if (tid < 32) {
-          const int t = t0 + tid;
-          const bool ok = t < sq.q_len;
-          const int64_t row = ((int64_t)sq.q_start + t) * p.hq + h;
-          l2s[tid] = ok ? p.l2[row] : __builtin_inff();
-          dds[tid] = ok ? p.dd[row] : 0.f;
-          wds[tid] = (ok && cls == MA_TILE_PARTIAL) ? p.words[(int64_t)en.wblk * tq + qb * 32 + tid] : ~0ull;
-        }
-        __syncthreads();
-        // S = Q K^T, dP = dO V^T (32 queries x this wave's 32 keys)
-        f32x16 sb = f32x16{}, dpb = f32x16{};
+    const int h = g * p.group + hh;
+    const int t0 = qt * tq + qb * 64, last = sq.q_len - 1;
 #pragma unroll
-        for (int k = 0; k < D / 16; ++k) {
-          sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<D>(qs, l32, hi, k), kf[k], sb, 0, 0, 0);
-          dpb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<D>(ds, l32, hi, k), vf[k], dpb, 0, 0, 0);
-        }
-        // P and dS for the lane's key and the queries of its registers
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qr = 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool vis = key_ok && ((wds[qr] >> kk) & 1ull);
-          const float pr = vis ? fast_exp2(__builtin_fmaf(sb[r], c, -l2s[qr])) : 0.f;
-          sb[r] = pr;
-          dpb[r] = pr * (dpb[r] - dds[qr]);
-        }
-        const bf16x8 pb0 = to_bf16x8(sb, 0), pb1 = to_bf16x8(sb, 1);
-        const bf16x8 sb0 = to_bf16x8(dpb, 0), sb1 = to_bf16x8(dpb, 1);
-        // dV^T += dO^T P, dK^T += Q^T dS
-#pragma unroll
-        for (int n = 0; n < D / 32; ++n) {
-          dvacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_op<D>(ds, lane, 0, n), pb0, dvacc[n], 0, 0, 0);
-          dvacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_op<D>(ds, lane, 1, n), pb1, dvacc[n], 0, 0, 0);
-          dkacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_op<D>(qs, lane, 0, n), sb0, dkacc[n], 0, 0, 0);
-          dkacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_op<D>(qs, lane, 1, n), sb1, dkacc[n], 0, 0, 0);
+    for (int i = 0; i < NI; ++i) {
+      const int t = wave * NI + i;
+      const int pos = 64 * t + lane, r = pos / CH, pc = pos % CH;
+      const int row = min(t0 + r, last);
+      const int64_t src = (((int64_t)sq.q_start + row) * p.hq + h) * D + 8 * (pc ^ QB::f(r));
+      dma::lds_load16(p.q + src, dma::lds_addr(st + 512 * t));
+      dma::lds_load16(p.dout + src, dma::lds_addr(st + QB::ELEMS + 512 * t));
+    }
+    const int row = min(t0 + lane, last);
+    const int64_t ridx = ((int64_t)sq.q_start + row) * p.hq + h;
+    uint16_t *meta = st + QB::META + 128 * wave;   // 64 x 4 bytes per wave
+    if (wave == 0) {
+      lds_load4(p.l2 + ridx, dma::lds_addr(meta));
+    } else if (wave == 1) {
+      lds_load4(p.dd + ridx, dma::lds_addr(meta));
+    } else if (cls == MA_TILE_PARTIAL) {
+      const uint32_t *wp = (const uint32_t *)(p.words + (int64_t)en.wblk * tq + qb * 64 + lane) + (wave - 2);
+      lds_load4(wp, dma::lds_addr(meta));
+    }
+  };
+
+  if (eb < ee) {
+    int e = eb, hh = 0, qb = 0, nb = nblk(eb);
+    issue(e, hh, qb, lds);
+    for (int i = 0;; ++i) {
+      dma::wait_vmem();
+      __syncthreads();   // stage i % 2 is filled; every wave is done with stage (i + 1) % 2
+      // next block
+      int e2 = e, hh2 = hh, qb2 = qb + 1, nb2 = nb;
+      if (qb2 >= nb) {
+        qb2 = 0;
+        if (++hh2 >= p.group) {
+          hh2 = 0;
+          ++e2;
+          if (e2 < ee) nb2 = nblk(e2);
         }
       }
+      const bool more = e2 < ee;
+      if (more) issue(e2, hh2, qb2, lds + ((i + 1) & 1) * QB::STAGE);
+
+      const uint16_t *st = lds + (i & 1) * QB::STAGE;
+      const uint16_t *qs = st, *ds = st + QB::ELEMS;
+      const Entry en = load_entry(p.kentries, e);
+      const int cls = entry_cls(en.kt_cls);
+      const int nrows = sq.q_len - (entry_kt(en.kt_cls) * tq + qb * 64);
+      // S = Q K^T, dP = dO V^T: this wave's 32 query rows x 32 keys (lane = key)
+      f32x16 sb = f32x16{}, dpb = f32x16{};
+#pragma unroll
+      for (int k = 0; k < D / 16; ++k) {
+        const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qs + rrow + ((16 * k) ^ rx)));
+        const bf16x8 da = __builtin_bit_cast(bf16x8, *(const u32x4 *)(ds + rrow + ((16 * k) ^ rx)));
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[k], sb, 0, 0, 0);
+        dpb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[k], dpb, 0, 0, 0);
+      }
+      // P and dS: register r holds query row 32 qh + 8 (r / 4) + 4 hi + r % 4
+      const float *meta = (const float *)(st + QB::META);
+      const uint32_t *wd = (const uint32_t *)(st + QB::META + 128 * (2 + kh));
+      const float c = p.scale_log2;
+      // Branch-free: every probability is computed, then selected; a FULL
+      // tile's words are read (stale) and overridden by `full`.
+      const uint32_t full = cls == MA_TILE_PARTIAL ? 0u : ~0u;
+      const uint32_t kbit = key_ok ? (1u << l32) : 0u;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int r0 = 32 * qh + 8 * a + 4 * hi;
+        const f32x4 l2v = *(const f32x4 *)(meta + r0);
+        const f32x4 ddv = *(const f32x4 *)(meta + 64 + r0);
+        const u32x4 wv = *(const u32x4 *)(wd + r0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int r = 4 * a + b;
+          const uint32_t bits = (wv[b] | full) & (r0 + b < nrows ? kbit : 0u);
+          const float ex = fast_exp2(__builtin_fmaf(sb[r], c, -l2v[b]));
+          const float pr = bits ? ex : 0.f;
+          sb[r] = pr;
+          dpb[r] = pr * (dpb[r] - ddv[b]);
+        }
+      }
+      const bf16x8 pb0 = to_bf16x8(sb, 0), pb1 = to_bf16x8(sb, 1);
+      const bf16x8 sb0 = to_bf16x8(dpb, 0), sb1 = to_bf16x8(dpb, 1);
+      // dV^T += dO^T P, dK^T += Q^T dS (query rows 16 u .. of this wave's 32)
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n) {
+        dvacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(ds, 0, n), pb0, dvacc[n], 0, 0, 0);
+        dvacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(ds, 1, n), pb1, dvacc[n], 0, 0, 0);
+        dkacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qs, 0, n), sb0, dkacc[n], 0, 0, 0);
+        dkacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qs, 1, n), sb1, dkacc[n], 0, 0, 0);
+      }
+      if (!more) break;
+      e = e2;
+      hh = hh2;
+      qb = qb2;
+      nb = nb2;
     }
+  }
+
+  // The two waves of a key half add their partial sums: wave (kh, 0) keeps
+  // dK and receives the other's dK, wave (kh, 1) keeps dV and receives dV.
+  __syncthreads();   // every wave is done with the stages (no gather is outstanding)
+  float *red = (float *)lds;
+  constexpr int RSZ = (D / 32) * 16 * 64;   // floats per wave region
+  {
+    float *mine = red + (2 * kh + qh) * RSZ;
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mine[(16 * n + r) * 64 + lane] = qh == 0 ? dvacc[n][r] : dkacc[n][r];
+  }
+  __syncthreads();
+  {
+    const float *other = red + (2 * kh + (qh ^ 1)) * RSZ;
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = other[(16 * n + r) * 64 + lane];
+        if (qh == 0)
+          dkacc[n][r] += x;
+        else
+          dvacc[n][r] += x;
+      }
   }
   if (!key_ok) return;
   const int key = kt * 64 + kk;
-  const int pmask = (1 << p.page_shift) - 1;
-  const int64_t off = (int64_t)p.page_table[(int64_t)it.seq * p.max_pages + (key >> p.page_shift)] * p.s_page +
-                      (int64_t)(key & pmask) * p.s_slot + (int64_t)g * p.s_head;
-  store_row<D, float>(p.dk + off, dkacc, p.scale, hi);
-  store_row<D, float>(p.dv + off, dvacc, 1.f, hi);
+  const int64_t off =
+      (int64_t)pt[key >> p.page_shift] * p.s_page + (int64_t)(key & pmask) * p.s_slot + (int64_t)g * p.s_head;
+  if (qh == 0)
+    store_row<D, float>(p.dk + off, dkacc, p.scale, hi);
+  else
+    store_row<D, float>(p.dv + off, dvacc, 1.f, hi);
 }
 
 template <typename K>
@@ -381,8 +493,7 @@ ma_status run(const BackwardArgs &a, const BwdParams &prm) {
   else
     st = launch(bwd_dq<D, 64>, prm.num_items * a.hq, 128, dq_lds, prm, a.stream, "backward dQ");
   if (st != MA_OK) return st;
-  return launch(bwd_dkdv<D>, prm.num_kitems * a.hkv, 128, (2 * 64 + 2 * 32) * BwdStage<D>::S * sizeof(uint16_t), prm,
-                a.stream, "backward dK dV");
+  return launch(bwd_dkdv<D>, prm.num_kitems * a.hkv, 256, QBlk<D>::BYTES, prm, a.stream, "backward dK dV");
 }
 
 }  // namespace
