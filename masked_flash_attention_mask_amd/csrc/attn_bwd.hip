@@ -118,7 +118,7 @@ template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq(BwdParams p) {
   constexpr int NT = BQ * 2, S = BwdStage<D>::S;
   extern __shared__ __align__(16) uint16_t lds[];   // [2 stages][K tile, V tile]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int item_idx = blockIdx.x / p.hq, h = blockIdx.x - item_idx * p.hq;
   const Item it = p.items[item_idx];
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv(BwdParams p) {
   using QB = QBlk<D>;
   constexpr int CH = D / 8, NI = CH / 4;   // gather instructions per wave per matrix
   extern __shared__ __align__(16) uint16_t lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int kh = wave & 1, qh = wave >> 1;
   const int hkv = p.hq / p.group;
@@ -337,10 +337,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv(BwdParams p) {
     const int qt = entry_kt(en.kt_cls), cls = entry_cls(en.kt_cls);
     const int h = g * p.group + hh;
     const int t0 = qt * tq + qb * 64, last = sq.q_len - 1;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));   // recompute the per-lane addressing here rather than hold it in registers
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int t = wave * NI + i;
-      const int pos = 64 * t + lane, r = pos / CH, pc = pos % CH;
+      const int pos = 64 * t + ln, r = pos / CH, pc = pos % CH;
       const int row = min(t0 + r, last);
       const int64_t src = (((int64_t)sq.q_start + row) * p.hq + h) * D + 8 * (pc ^ QB::f(r));
       dma::lds_load16(p.q + src, dma::lds_addr(st + 512 * t));
@@ -470,6 +472,300 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv(BwdParams p) {
     store_row<D, float>(p.dv + off, dvacc, 1.f, hi);
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV for plans with 128-row q-tiles: one workgroup per (k-tile, K/V
+// head), 4 waves, each wave all 64 keys and query rows 32 w .. + 31 of every
+// 128-row block, so every Q / dO operand read from LDS feeds two products.
+// K rows of both 32-key blocks are held as B operands; V rows (the B
+// operands of dP) are read from an LDS copy of the tile, for the register
+// budget.  The four partial sums are added at the end.  Query blocks are
+// gathered into LDS one block ahead, as above.
+// ---------------------------------------------------------------------------
+template <int D>
+struct QBlkW {
+  static constexpr int ELEMS = 128 * D;
+  static constexpr int META = 2 * ELEMS;
+  static constexpr int STAGE = META + 4 * 128 * 2;   // + l2, dd, word low, word high (128 x 4 bytes each)
+  static constexpr size_t BYTES = 2 * STAGE * sizeof(uint16_t);
+  static constexpr int V_OFF = 2 * STAGE;   // V tile, 64 x D, swizzled like a block
+  static constexpr size_t LDS = BYTES + 64 * D * sizeof(uint16_t);
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_wide(BwdParams p) {
+  using QB = QBlk<D>;
+  using QW = QBlkW<D>;
+  constexpr int CH = D / 8, NI = 2 * CH / 4;   // gather instructions per wave per matrix
+  extern __shared__ __align__(16) uint16_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int hkv = p.hq / p.group;
+  const int item_idx = blockIdx.x / hkv, g = blockIdx.x - item_idx * hkv;
+  const Item it = p.kitems[item_idx];
+  const SeqInfo sq = p.seqs[it.seq];
+  const int kt = it.qt, kv_len = sq.kv_len;
+  const int kin = kv_len - kt * 64;
+  const int32_t *pt = p.page_table + (int64_t)it.seq * p.max_pages;
+  const int pmask = (1 << p.page_shift) - 1;
+
+  bf16x8 kf[2][D / 16];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = min(kt * 64 + 32 * kb + l32, kv_len - 1);
+    const int64_t off =
+        (int64_t)pt[key >> p.page_shift] * p.s_page + (int64_t)(key & pmask) * p.s_slot + (int64_t)g * p.s_head;
+    load_q<D>(kf[kb], p.k + off, true, hi);
+  }
+  uint16_t *vt = lds + QW::V_OFF;
+  {
+    // thread -> key tid / 4, chunks (tid % 4) + 4 x; published by the first
+    // barrier of the block loop
+    const int r = tid >> 2;
+    const int key = min(kt * 64 + r, kv_len - 1);
+    const uint16_t *src = p.v + (int64_t)pt[key >> p.page_shift] * p.s_page + (int64_t)(key & pmask) * p.s_slot +
+                          (int64_t)g * p.s_head;
+#pragma unroll
+    for (int x = 0; x < CH / 4; ++x) {
+      const int c = (tid & 3) + 4 * x;
+      *(u32x4 *)(vt + r * D + 8 * (c ^ QB::f(r))) = *(const u32x4 *)(src + 8 * c);
+    }
+  }
+
+  const int rrow = (32 * wave + l32) * D;
+  const int rx = 8 * (hi ^ QB::f(l32));
+  const int j = 4 * hi + ((lane & 15) >> 2);
+  const int trow = (32 * wave + j) * D;
+  const int cb = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tax = 8 * (cb ^ QB::f(j)) + 4 * (lane & 1);
+  const int tbx = 8 * (cb ^ QB::f(j + 8)) + 4 * (lane & 1);
+  auto tr_read = [&](const uint16_t *m, int u, int n) -> bf16x8 {
+    const uint16_t *b = m + trow + 16 * u * D;
+    const i16x4 r0 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(b + ((32 * n) ^ tax)));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(b + 8 * D + ((32 * n) ^ tbx)));
+    const i16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  f32x16 dkacc[2][D / 32], dvacc[2][D / 32];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) {
+      dkacc[kb][n] = f32x16{};
+      dvacc[kb][n] = f32x16{};
+    }
+
+  const int eb = it.ent_begin, ee = it.ent_end;
+  auto issue = [&](int e, int hh, uint16_t *st) {
+    const Entry en = load_entry(p.kentries, e);
+    const int qt = entry_kt(en.kt_cls), cls = entry_cls(en.kt_cls);
+    const int h = g * p.group + hh;
+    const int t0 = qt * 128, last = sq.q_len - 1;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));   // recompute the per-lane addressing here rather than hold it in registers
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int t = wave * NI + i;
+      const int pos = 64 * t + ln, r = pos / CH, pc = pos % CH;
+      const int row = min(t0 + r, last);
+      const int64_t src = (((int64_t)sq.q_start + row) * p.hq + h) * D + 8 * (pc ^ QB::f(r));
+      dma::lds_load16(p.q + src, dma::lds_addr(st + 512 * t));
+      dma::lds_load16(p.dout + src, dma::lds_addr(st + QW::ELEMS + 512 * t));
+    }
+    // metadata: wave w loads array w (l2, dd, word low, word high) for the
+    // block's 128 rows, two instructions of 64 rows
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int rr = 64 * half + lane;
+      const int row = min(t0 + rr, last);
+      const int64_t ridx = ((int64_t)sq.q_start + row) * p.hq + h;
+      uint16_t *meta = st + QW::META + 256 * wave + 128 * half;
+      if (wave == 0) {
+        lds_load4(p.l2 + ridx, dma::lds_addr(meta));
+      } else if (wave == 1) {
+        lds_load4(p.dd + ridx, dma::lds_addr(meta));
+      } else if (cls == MA_TILE_PARTIAL) {
+        const uint32_t *wp = (const uint32_t *)(p.words + (int64_t)en.wblk * 128 + rr) + (wave - 2);
+        lds_load4(wp, dma::lds_addr(meta));
+      }
+    }
+  };
+
+  if (eb < ee) {
+    int e = eb, hh = 0;
+    issue(e, hh, lds);
+    for (int i = 0;; ++i) {
+      dma::wait_vmem();
+      __syncthreads();
+      int e2 = e, hh2 = hh + 1;
+      if (hh2 >= p.group) {
+        hh2 = 0;
+        ++e2;
+      }
+      const bool more = e2 < ee;
+      if (more) issue(e2, hh2, lds + ((i + 1) & 1) * QW::STAGE);
+
+      const uint16_t *st = lds + (i & 1) * QW::STAGE;
+      const uint16_t *qs = st, *ds = st + QW::ELEMS;
+      const Entry en = load_entry(p.kentries, e);
+      const int cls = entry_cls(en.kt_cls);
+      const int nrows = sq.q_len - entry_kt(en.kt_cls) * 128;
+      // S = Q K^T, dP = dO V^T for this wave's 32 query rows and both key
+      // blocks; the operands of step k + 1 are read while step k's products
+      // run.
+      f32x16 sb[2], dpb[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sb[kb] = f32x16{};
+        dpb[kb] = f32x16{};
+      }
+      {
+        bf16x8 qa[2], da[2], vb[2][2];
+        auto read_a = [&](int k, int sl) {
+          qa[sl] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qs + rrow + ((16 * k) ^ rx)));
+          da[sl] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(ds + rrow + ((16 * k) ^ rx)));
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            vb[sl][kb] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(vt + (32 * kb + l32) * D + ((16 * k) ^ rx)));
+        };
+        read_a(0, 0);
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) {
+          if (k + 1 < D / 16) read_a(k + 1, (k + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            sb[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[k & 1], kf[kb][k], sb[kb], 0, 0, 0);
+            dpb[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[k & 1], vb[k & 1][kb], dpb[kb], 0, 0, 0);
+          }
+        }
+      }
+      // P and dS (branch-free; a FULL tile's words are read stale and
+      // overridden by `full`), rounded to bf16 for their products.
+      const float *meta = (const float *)(st + QW::META);
+      const uint32_t *wd0 = (const uint32_t *)(st + QW::META + 512);
+      const uint32_t *wd1 = (const uint32_t *)(st + QW::META + 768);
+      const float c = p.scale_log2;
+      const uint32_t full = cls == MA_TILE_PARTIAL ? 0u : ~0u;
+      const uint32_t kbit0 = l32 < kin ? (1u << l32) : 0u;
+      const uint32_t kbit1 = 32 + l32 < kin ? (1u << l32) : 0u;
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int r0 = 32 * wave + 8 * a4 + 4 * hi;
+        const f32x4 l2v = *(const f32x4 *)(meta + r0);
+        const f32x4 ddv = *(const f32x4 *)(meta + 128 + r0);
+        const u32x4 w0 = *(const u32x4 *)(wd0 + r0);
+        const u32x4 w1 = *(const u32x4 *)(wd1 + r0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int r = 4 * a4 + b;
+          const bool rok = r0 + b < nrows;
+          const uint32_t bits0 = (w0[b] | full) & (rok ? kbit0 : 0u);
+          const uint32_t bits1 = (w1[b] | full) & (rok ? kbit1 : 0u);
+          const float e0 = fast_exp2(__builtin_fmaf(sb[0][r], c, -l2v[b]));
+          const float e1 = fast_exp2(__builtin_fmaf(sb[1][r], c, -l2v[b]));
+          const float p0 = bits0 ? e0 : 0.f, p1 = bits1 ? e1 : 0.f;
+          sb[0][r] = p0;
+          sb[1][r] = p1;
+          dpb[0][r] = p0 * (dpb[0][r] - ddv[b]);
+          dpb[1][r] = p1 * (dpb[1][r] - ddv[b]);
+        }
+      }
+      bf16x8 pb[2][2], sbf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        pb[kb][0] = to_bf16x8(sb[kb], 0);
+        pb[kb][1] = to_bf16x8(sb[kb], 1);
+        sbf[kb][0] = to_bf16x8(dpb[kb], 0);
+        sbf[kb][1] = to_bf16x8(dpb[kb], 1);
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS; transposed operands read one step ahead
+      {
+        constexpr int NS = 2 * (D / 32);   // steps (n, u)
+        bf16x8 ta[2], tb[2];
+        auto read_t = [&](int x, int sl) {
+          ta[sl] = tr_read(ds, x & 1, x >> 1);
+          tb[sl] = tr_read(qs, x & 1, x >> 1);
+        };
+        read_t(0, 0);
+#pragma unroll
+        for (int x = 0; x < NS; ++x) {
+          if (x + 1 < NS) read_t(x + 1, (x + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          const int n = x >> 1, u = x & 1;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            dvacc[kb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[x & 1], pb[kb][u], dvacc[kb][n], 0, 0, 0);
+            dkacc[kb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[x & 1], sbf[kb][u], dkacc[kb][n], 0, 0, 0);
+          }
+        }
+      }
+      if (!more) break;
+      e = e2;
+      hh = hh2;
+    }
+  }
+
+  // Four partial sums per key are added in OWN rounds: in round q, wave w
+  // owns accumulator w * OWN + q (accumulators indexed (matrix, kb, n)); the
+  // other waves park their copies of it in LDS and the owner adds them, in
+  // wave order, and stores the result.
+  constexpr int NACC = 2 * 2 * (D / 32);
+  constexpr int OWN = NACC / 4;
+  constexpr int RSZ = 16 * 64;            // floats of one accumulator over a wave
+  static_assert(16 * RSZ * 4 <= QW::BYTES, "reduction does not fit the stages");
+  float *red = (float *)lds;              // [owner][writer][RSZ]
+  auto acc_ref = [&](int a) -> f32x16 & {
+    const int m = a / (2 * (D / 32)), kb = (a / (D / 32)) % 2, n = a % (D / 32);
+    return m == 0 ? dkacc[kb][n] : dvacc[kb][n];
+  };
+  int64_t off[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = min(kt * 64 + 32 * kb + l32, kv_len - 1);
+    off[kb] = (int64_t)pt[key >> p.page_shift] * p.s_page + (int64_t)(key & pmask) * p.s_slot +
+              (int64_t)g * p.s_head;
+  }
+#pragma unroll
+  for (int q = 0; q < OWN; ++q) {
+    __syncthreads();   // the stages (or the previous round's slots) are free
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (w == wave) continue;
+      float *dst = red + (4 * w + wave) * RSZ;
+      const f32x16 &v = acc_ref(w * OWN + q);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[r * 64 + lane] = v[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (w != wave) continue;
+      const int a = w * OWN + q;
+      f32x16 &v = acc_ref(a);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if (x == w) continue;
+        const float *src = red + (4 * w + x) * RSZ;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] += src[r * 64 + lane];
+      }
+      const int m = a / (2 * (D / 32)), kb = (a / (D / 32)) % 2, n = a % (D / 32);
+      if (32 * kb + l32 < kin) {
+        float *dst = (m == 0 ? p.dk : p.dv) + off[kb];
+        const float sc = m == 0 ? p.scale : 1.f;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = 32 * n + 8 * r4 + 4 * hi;
+          store4<float>(dst + d0, v[4 * r4] * sc, v[4 * r4 + 1] * sc, v[4 * r4 + 2] * sc, v[4 * r4 + 3] * sc);
+        }
+      }
+    }
+  }
+}
+
 template <typename K>
 ma_status launch(K kern, int grid, int block, size_t lds, const BwdParams &prm, void *stream, const char *what) {
   if (grid == 0) return MA_OK;
@@ -493,6 +789,8 @@ ma_status run(const BackwardArgs &a, const BwdParams &prm) {
   else
     st = launch(bwd_dq<D, 64>, prm.num_items * a.hq, 128, dq_lds, prm, a.stream, "backward dQ");
   if (st != MA_OK) return st;
+  if (prm.tile_q == 128)
+    return launch(bwd_dkdv_wide<D>, prm.num_kitems * a.hkv, 256, QBlkW<D>::LDS, prm, a.stream, "backward dK dV");
   return launch(bwd_dkdv<D>, prm.num_kitems * a.hkv, 256, QBlk<D>::BYTES, prm, a.stream, "backward dK dV");
 }
 
