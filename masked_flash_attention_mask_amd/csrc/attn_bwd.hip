@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv(BwdParams p) {
     dvacc[n] = f32x16{};
   }
 
-  // Work list: entries (q-tiles, ascending) x query heads of the group x the
+  // Work list: entries (q-tiles, descending) x query heads of the group x the
   // q-tile's 64-row blocks that hold rows of the sequence.
   const int eb = it.ent_begin, ee = it.ent_end;
   auto nblk = [&](int e) {
@@ -476,26 +476,41 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv(BwdParams p) {
 // dK, dV for plans with 128-row q-tiles: one workgroup per (k-tile, K/V
 // head), 4 waves, each wave all 64 keys and query rows 32 w .. + 31 of every
 // 128-row block, so every Q / dO operand read from LDS feeds two products.
-// K rows of both 32-key blocks are held as B operands; V rows (the B
-// operands of dP) are read from an LDS copy of the tile, for the register
-// budget.  The four partial sums are added at the end.  Query blocks are
-// gathered into LDS one block ahead, as above.
+// K rows of the first 32 keys are held as B operands; the other K rows and
+// the V rows (the B operands of dP) are read from LDS copies of the tile,
+// for the register budget.  Each wave gathers its own 32 query rows (Q, dO, L2, D) straight
+// into its own pair of LDS stages one block ahead, so the waves run without
+// barriers until the four partial sums are added at the end.
 // ---------------------------------------------------------------------------
 template <int D>
 struct QBlkW {
-  static constexpr int ELEMS = 128 * D;
-  static constexpr int META = 2 * ELEMS;
-  static constexpr int STAGE = META + 4 * 128 * 2;   // + l2, dd, word low, word high (128 x 4 bytes each)
-  static constexpr size_t BYTES = 2 * STAGE * sizeof(uint16_t);
-  static constexpr int V_OFF = 2 * STAGE;   // V tile, 64 x D, swizzled like a block
-  static constexpr size_t LDS = BYTES + 64 * D * sizeof(uint16_t);
+  static constexpr int ROWS = 32;                    // rows per wave
+  static constexpr int ELEMS = ROWS * D;
+  static constexpr int META = 2 * ELEMS;             // l2 [64], dd [64] floats (lanes 32..63 repeat 0..31),
+                                                     // then the 32 rows' tile words (u64)
+  static constexpr int WSTAGE = META + 3 * 64 * 2;   // elements of one wave stage
+  static constexpr int V_OFF = 4 * 2 * WSTAGE;       // V tile, 64 x D, swizzled like a block
+  static constexpr int K1_OFF = V_OFF + 64 * D;      // K rows of keys 32..63, 32 x D, swizzled likewise
+  static constexpr size_t LDS = (size_t)(K1_OFF + 32 * D) * sizeof(uint16_t);
 };
+
+typedef const __attribute__((address_space(1))) void *gptr_t;
+
+// Direct global -> LDS loads with a scalar base and a 32-bit per-lane byte
+// offset (the SGPR-base form of the instruction): lane l writes LDS address
+// m0 + 16 l (4 l).  See dma::lds_load16 for how the kernels order them.
+__device__ __forceinline__ void lds_load16_s(gptr_t base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void lds_load4_s(gptr_t base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+}
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide(BwdParams p) {
   using QB = QBlk<D>;
   using QW = QBlkW<D>;
-  constexpr int CH = D / 8, NI = 2 * CH / 4;   // gather instructions per wave per matrix
+  constexpr int CH = D / 8, NI = CH / 2;   // gather instructions per wave per matrix (32 rows)
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -508,33 +523,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide(BwdParams p) {
   const int32_t *pt = p.page_table + (int64_t)it.seq * p.max_pages;
   const int pmask = (1 << p.page_shift) - 1;
 
-  bf16x8 kf[2][D / 16];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int key = min(kt * 64 + 32 * kb + l32, kv_len - 1);
+  // K rows of keys 0..31 as B operands in registers; K rows of keys 32..63
+  // and all V rows in LDS (the register file holds the dK / dV sums).
+  bf16x8 kf[D / 16];
+  {
+    const int key = min(kt * 64 + l32, kv_len - 1);
     const int64_t off =
         (int64_t)pt[key >> p.page_shift] * p.s_page + (int64_t)(key & pmask) * p.s_slot + (int64_t)g * p.s_head;
-    load_q<D>(kf[kb], p.k + off, true, hi);
+    load_q<D>(kf, p.k + off, true, hi);
   }
   uint16_t *vt = lds + QW::V_OFF;
+  uint16_t *k1t = lds + QW::K1_OFF;
   {
-    // thread -> key tid / 4, chunks (tid % 4) + 4 x; published by the first
-    // barrier of the block loop
+    // thread -> key tid / 4, chunks (tid % 4) + 4 x
     const int r = tid >> 2;
     const int key = min(kt * 64 + r, kv_len - 1);
-    const uint16_t *src = p.v + (int64_t)pt[key >> p.page_shift] * p.s_page + (int64_t)(key & pmask) * p.s_slot +
-                          (int64_t)g * p.s_head;
+    const int64_t off =
+        (int64_t)pt[key >> p.page_shift] * p.s_page + (int64_t)(key & pmask) * p.s_slot + (int64_t)g * p.s_head;
 #pragma unroll
     for (int x = 0; x < CH / 4; ++x) {
       const int c = (tid & 3) + 4 * x;
-      *(u32x4 *)(vt + r * D + 8 * (c ^ QB::f(r))) = *(const u32x4 *)(src + 8 * c);
+      *(u32x4 *)(vt + r * D + 8 * (c ^ QB::f(r))) = *(const u32x4 *)(p.v + off + 8 * c);
+      if (r >= 32) *(u32x4 *)(k1t + (r - 32) * D + 8 * (c ^ QB::f(r))) = *(const u32x4 *)(p.k + off + 8 * c);
     }
   }
 
-  const int rrow = (32 * wave + l32) * D;
+  // Row reads: row l32 of the wave's block, chunk 2 k + hi, stored at chunk
+  // 2 k ^ (hi ^ f).  Transposed reads: rows 16 u + j (+ 8), j = 4 hi +
+  // (lane % 16) / 4, columns 32 n + 16 ((lane / 16) % 2) + 4 (lane % 4), i.e.
+  // chunk 4 n + cb at 4 n ^ (cb ^ f).  f depends on the row modulo 16.
+  const int rrow = l32 * D;
   const int rx = 8 * (hi ^ QB::f(l32));
   const int j = 4 * hi + ((lane & 15) >> 2);
-  const int trow = (32 * wave + j) * D;
+  const int trow = j * D;
   const int cb = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int tax = 8 * (cb ^ QB::f(j)) + 4 * (lane & 1);
   const int tbx = 8 * (cb ^ QB::f(j + 8)) + 4 * (lane & 1);
@@ -548,6 +569,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide(BwdParams p) {
     return __builtin_bit_cast(bf16x8, v);
   };
 
+  // Gather addressing: instruction i, lane l loads row (64 / CH) i + l / CH of
+  // the wave's 32, logical chunk (l % CH) ^ f(row) into LDS position 64 i + l.
+  const uint32_t lds_base = dma::lds_addr(lds);
+  const uint32_t row_bytes = (uint32_t)p.hq * D * 2;
+
   f32x16 dkacc[2][D / 32], dvacc[2][D / 32];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -558,147 +584,172 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide(BwdParams p) {
     }
 
   const int eb = it.ent_begin, ee = it.ent_end;
-  auto issue = [&](int e, int hh, uint16_t *st) {
+  // Gathers the wave's rows of block (e, hh) into its stage sl; rows past the
+  // sequence repeat its last row (their probabilities are masked to 0).
+  auto issue = [&](int e, int hh, int sl) {
     const Entry en = load_entry(p.kentries, e);
-    const int qt = entry_kt(en.kt_cls), cls = entry_cls(en.kt_cls);
+    const int qt = entry_kt(en.kt_cls);
     const int h = g * p.group + hh;
-    const int t0 = qt * 128, last = sq.q_len - 1;
+    const int t0 = qt * 128 + 32 * wave;
+    const int rb = min(t0, sq.q_len - 1);
+    const int rmax = max(0, min(31, sq.q_len - 1 - t0));
+    const int64_t row0 = ((int64_t)sq.q_start + rb) * p.hq + h;
+    const gptr_t qb = (gptr_t)(p.q + row0 * D);
+    const gptr_t db = (gptr_t)(p.dout + row0 * D);
+    const uint32_t st = lds_base + (uint32_t)((2 * wave + sl) * QW::WSTAGE) * 2;
     int ln = lane;
-    asm volatile("" : "+v"(ln));   // recompute the per-lane addressing here rather than hold it in registers
+    asm volatile("" : "+v"(ln));   // keep the per-lane addressing local to the gather
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int t = wave * NI + i;
-      const int pos = 64 * t + ln, r = pos / CH, pc = pos % CH;
-      const int row = min(t0 + r, last);
-      const int64_t src = (((int64_t)sq.q_start + row) * p.hq + h) * D + 8 * (pc ^ QB::f(r));
-      dma::lds_load16(p.q + src, dma::lds_addr(st + 512 * t));
-      dma::lds_load16(p.dout + src, dma::lds_addr(st + QW::ELEMS + 512 * t));
+      const int r = (64 / CH) * i + ln / CH, pc = ln % CH;
+      const uint32_t voff = (uint32_t)min(r, rmax) * row_bytes + 16 * (pc ^ QB::f(r));
+      lds_load16_s(qb, voff, st + 1024 * i);
+      lds_load16_s(db, voff, st + QW::ELEMS * 2 + 1024 * i);
     }
-    // metadata: wave w loads array w (l2, dd, word low, word high) for the
-    // block's 128 rows, two instructions of 64 rows
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int rr = 64 * half + lane;
-      const int row = min(t0 + rr, last);
-      const int64_t ridx = ((int64_t)sq.q_start + row) * p.hq + h;
-      uint16_t *meta = st + QW::META + 256 * wave + 128 * half;
-      if (wave == 0) {
-        lds_load4(p.l2 + ridx, dma::lds_addr(meta));
-      } else if (wave == 1) {
-        lds_load4(p.dd + ridx, dma::lds_addr(meta));
-      } else if (cls == MA_TILE_PARTIAL) {
-        const uint32_t *wp = (const uint32_t *)(p.words + (int64_t)en.wblk * 128 + rr) + (wave - 2);
-        lds_load4(wp, dma::lds_addr(meta));
-      }
-    }
+    const uint32_t moff = (uint32_t)min(ln & 31, rmax) * (uint32_t)p.hq * 4;
+    lds_load4_s((gptr_t)(p.l2 + row0), moff, st + QW::META * 2);
+    lds_load4_s((gptr_t)(p.dd + row0), moff, st + QW::META * 2 + 256);
+    if (entry_cls(en.kt_cls) == MA_TILE_PARTIAL)   // lane l: dword l of the wave's 32 words
+      lds_load4_s((gptr_t)(p.words + (int64_t)en.wblk * 128 + 32 * wave), 4 * ln, st + QW::META * 2 + 512);
   };
 
+  __syncthreads();   // the V tile
   if (eb < ee) {
     int e = eb, hh = 0;
-    issue(e, hh, lds);
+    issue(e, hh, 0);
     for (int i = 0;; ++i) {
-      dma::wait_vmem();
-      __syncthreads();
+      dma::wait_vmem();   // this wave's gathers of block i have landed
       int e2 = e, hh2 = hh + 1;
       if (hh2 >= p.group) {
         hh2 = 0;
         ++e2;
       }
       const bool more = e2 < ee;
-      if (more) issue(e2, hh2, lds + ((i + 1) & 1) * QW::STAGE);
+      if (more) issue(e2, hh2, (i + 1) & 1);
 
-      const uint16_t *st = lds + (i & 1) * QW::STAGE;
-      const uint16_t *qs = st, *ds = st + QW::ELEMS;
       const Entry en = load_entry(p.kentries, e);
       const int cls = entry_cls(en.kt_cls);
-      const int nrows = sq.q_len - entry_kt(en.kt_cls) * 128;
-      // S = Q K^T, dP = dO V^T for this wave's 32 query rows and both key
-      // blocks; the operands of step k + 1 are read while step k's products
-      // run.
-      f32x16 sb[2], dpb[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sb[kb] = f32x16{};
-        dpb[kb] = f32x16{};
-      }
+      const int nv = sq.q_len - (entry_kt(en.kt_cls) * 128 + 32 * wave);   // valid rows of this wave
       {
-        bf16x8 qa[2], da[2], vb[2][2];
-        auto read_a = [&](int k, int sl) {
-          qa[sl] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qs + rrow + ((16 * k) ^ rx)));
-          da[sl] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(ds + rrow + ((16 * k) ^ rx)));
+        const uint16_t *qs = lds + (2 * wave + (i & 1)) * QW::WSTAGE;
+        const uint16_t *ds = qs + QW::ELEMS;
+        float *meta = (float *)(lds + (2 * wave + (i & 1)) * QW::WSTAGE + QW::META);
+        // Rows past the sequence (gathered as copies of its last row) get
+        // L2 = +inf, so their probabilities are exactly 0.
+        if (nv < 32 && l32 >= nv) meta[lane] = __builtin_inff();
+        // The block in four phases, each VALU phase placed beside the
+        // products of the next so that one wave keeps the matrix cores busy:
+        //   S = Q K^T | dP = dO V^T beside P | dV^T += dO^T P beside dS |
+        //   dK^T += Q^T dS.
+        // Register r of a lane holds query row 8 (r / 4) + 4 hi + r % 4 and
+        // key 32 kb + l32; its visibility is bit l32 of half kb of the row's
+        // tile word (all ones for a FULL tile).  Operands of step k + 1 are
+        // read while step k's products run.
+        constexpr int KS = D / 16;              // k-steps of S and dP
+        constexpr int RPS = 16 / KS;            // rows of P finished per dP step
+        const uint32_t *wd = (const uint32_t *)(qs + QW::META + 256);
+        const uint32_t full = cls == MA_TILE_PARTIAL ? 0u : ~0u;
+        const uint32_t kbit0 = l32 < kin ? (1u << l32) : 0u;
+        const uint32_t kbit1 = 32 + l32 < kin ? (1u << l32) : 0u;
+        const float c = p.scale_log2;
+
+        f32x16 sb[2];
+        {
+          bf16x8 qa[2], kb1[2];
+          auto read_s = [&](int k, int sl) {
+            qa[sl] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qs + rrow + ((16 * k) ^ rx)));
+            kb1[sl] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(k1t + rrow + ((16 * k) ^ rx)));
+          };
+          read_s(0, 0);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            vb[sl][kb] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(vt + (32 * kb + l32) * D + ((16 * k) ^ rx)));
-        };
-        read_a(0, 0);
-#pragma unroll
-        for (int k = 0; k < D / 16; ++k) {
-          if (k + 1 < D / 16) read_a(k + 1, (k + 1) & 1);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            sb[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[k & 1], kf[kb][k], sb[kb], 0, 0, 0);
-            dpb[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[k & 1], vb[k & 1][kb], dpb[kb], 0, 0, 0);
+          for (int k = 0; k < KS; ++k) {
+            if (k + 1 < KS) read_s(k + 1, (k + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int sl = k & 1;
+            sb[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[sl], kf[k], k == 0 ? f32x16{} : sb[0], 0, 0, 0);
+            sb[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[sl], kb1[sl], k == 0 ? f32x16{} : sb[1], 0, 0, 0);
           }
         }
-      }
-      // P and dS (branch-free; a FULL tile's words are read stale and
-      // overridden by `full`), rounded to bf16 for their products.
-      const float *meta = (const float *)(st + QW::META);
-      const uint32_t *wd0 = (const uint32_t *)(st + QW::META + 512);
-      const uint32_t *wd1 = (const uint32_t *)(st + QW::META + 768);
-      const float c = p.scale_log2;
-      const uint32_t full = cls == MA_TILE_PARTIAL ? 0u : ~0u;
-      const uint32_t kbit0 = l32 < kin ? (1u << l32) : 0u;
-      const uint32_t kbit1 = 32 + l32 < kin ? (1u << l32) : 0u;
+        // dP, and beside it P = exp2(S c - L2) on visible entries
+        f32x16 dpb[2];
+        f32x8 pv[2][2];   // P as fp32 (for dS), [kb][u]
+        bf16x8 pb[2][2];
+        {
+          bf16x8 da[2], vb[2][2];
+          auto read_p = [&](int k, int sl) {
+            da[sl] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(ds + rrow + ((16 * k) ^ rx)));
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int r0 = 32 * wave + 8 * a4 + 4 * hi;
-        const f32x4 l2v = *(const f32x4 *)(meta + r0);
-        const f32x4 ddv = *(const f32x4 *)(meta + 128 + r0);
-        const u32x4 w0 = *(const u32x4 *)(wd0 + r0);
-        const u32x4 w1 = *(const u32x4 *)(wd1 + r0);
+            for (int kb = 0; kb < 2; ++kb)
+              vb[sl][kb] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(vt + (32 * kb + l32) * D + ((16 * k) ^ rx)));
+          };
+          read_p(0, 0);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int r = 4 * a4 + b;
-          const bool rok = r0 + b < nrows;
-          const uint32_t bits0 = (w0[b] | full) & (rok ? kbit0 : 0u);
-          const uint32_t bits1 = (w1[b] | full) & (rok ? kbit1 : 0u);
-          const float e0 = fast_exp2(__builtin_fmaf(sb[0][r], c, -l2v[b]));
-          const float e1 = fast_exp2(__builtin_fmaf(sb[1][r], c, -l2v[b]));
-          const float p0 = bits0 ? e0 : 0.f, p1 = bits1 ? e1 : 0.f;
-          sb[0][r] = p0;
-          sb[1][r] = p1;
-          dpb[0][r] = p0 * (dpb[0][r] - ddv[b]);
-          dpb[1][r] = p1 * (dpb[1][r] - ddv[b]);
+          for (int k = 0; k < KS; ++k) {
+            if (k + 1 < KS) read_p(k + 1, (k + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int sl = k & 1;
+            dpb[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[sl], vb[sl][0], k == 0 ? f32x16{} : dpb[0], 0, 0, 0);
+            dpb[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[sl], vb[sl][1], k == 0 ? f32x16{} : dpb[1], 0, 0, 0);
+#pragma unroll
+            for (int rr = 0; rr < RPS; ++rr) {
+              const int r = RPS * k + rr, a4 = r >> 2, b = r & 3;
+              const int row = 8 * a4 + 4 * hi + b;
+              const float l2 = meta[row];
+              const uint32_t wlo = wd[2 * row], whi = wd[2 * row + 1];
+              const float e0 = fast_exp2(__builtin_fmaf(sb[0][r], c, -l2));
+              const float e1 = fast_exp2(__builtin_fmaf(sb[1][r], c, -l2));
+              pv[0][r >> 3][r & 7] = ((wlo | full) & kbit0) ? e0 : 0.f;
+              pv[1][r >> 3][r & 7] = ((whi | full) & kbit1) ? e1 : 0.f;
+            }
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) pb[kb][u] = __builtin_convertvector(pv[kb][u], bf16x8);
         }
-      }
-      bf16x8 pb[2][2], sbf[2][2];
+        // dV^T += dO^T P, and beside it dS = P (dP - D)
+        bf16x8 sbf[2][2];
+        {
+          constexpr int NS = 2 * (D / 32);   // steps (n, u)
+          constexpr int EPS = 32 / NS;       // dS elements finished per step
+          f32x8 dv[2][2];
+          bf16x8 ta[2];
+          auto read_v = [&](int x, int sl) { ta[sl] = tr_read(ds, x & 1, x >> 1); };
+          read_v(0, 0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        pb[kb][0] = to_bf16x8(sb[kb], 0);
-        pb[kb][1] = to_bf16x8(sb[kb], 1);
-        sbf[kb][0] = to_bf16x8(dpb[kb], 0);
-        sbf[kb][1] = to_bf16x8(dpb[kb], 1);
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS; transposed operands read one step ahead
-      {
-        constexpr int NS = 2 * (D / 32);   // steps (n, u)
-        bf16x8 ta[2], tb[2];
-        auto read_t = [&](int x, int sl) {
-          ta[sl] = tr_read(ds, x & 1, x >> 1);
-          tb[sl] = tr_read(qs, x & 1, x >> 1);
-        };
-        read_t(0, 0);
+          for (int x = 0; x < NS; ++x) {
+            if (x + 1 < NS) read_v(x + 1, (x + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int n = x >> 1, u = x & 1;
 #pragma unroll
-        for (int x = 0; x < NS; ++x) {
-          if (x + 1 < NS) read_t(x + 1, (x + 1) & 1);
-          __builtin_amdgcn_sched_barrier(0);
-          const int n = x >> 1, u = x & 1;
+            for (int kb = 0; kb < 2; ++kb)
+              dvacc[kb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[x & 1], pb[kb][u], dvacc[kb][n], 0, 0, 0);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            dvacc[kb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[x & 1], pb[kb][u], dvacc[kb][n], 0, 0, 0);
-            dkacc[kb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[x & 1], sbf[kb][u], dkacc[kb][n], 0, 0, 0);
+            for (int ee2 = 0; ee2 < EPS; ++ee2) {
+              const int el = EPS * x + ee2, kb = el >> 4, r = el & 15;
+              const int row = 8 * (r >> 2) + 4 * hi + (r & 3);
+              dv[kb][r >> 3][r & 7] = pv[kb][r >> 3][r & 7] * (dpb[kb][r] - meta[64 + row]);
+            }
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) sbf[kb][u] = __builtin_convertvector(dv[kb][u], bf16x8);
+        }
+        // dK^T += Q^T dS
+        {
+          constexpr int NS = 2 * (D / 32);
+          bf16x8 tb[2];
+          auto read_k = [&](int x, int sl) { tb[sl] = tr_read(qs, x & 1, x >> 1); };
+          read_k(0, 0);
+#pragma unroll
+          for (int x = 0; x < NS; ++x) {
+            if (x + 1 < NS) read_k(x + 1, (x + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const int n = x >> 1, u = x & 1;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+              dkacc[kb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[x & 1], sbf[kb][u], dkacc[kb][n], 0, 0, 0);
           }
         }
       }
@@ -715,7 +766,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide(BwdParams p) {
   constexpr int NACC = 2 * 2 * (D / 32);
   constexpr int OWN = NACC / 4;
   constexpr int RSZ = 16 * 64;            // floats of one accumulator over a wave
-  static_assert(16 * RSZ * 4 <= QW::BYTES, "reduction does not fit the stages");
+  static_assert(16 * RSZ * 4 <= QW::V_OFF * 2, "reduction does not fit the stages");
   float *red = (float *)lds;              // [owner][writer][RSZ]
   auto acc_ref = [&](int a) -> f32x16 & {
     const int m = a / (2 * (D / 32)), kb = (a / (D / 32)) % 2, n = a % (D / 32);

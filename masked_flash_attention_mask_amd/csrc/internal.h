@@ -72,7 +72,7 @@ struct ma_plan {
 
   // k-major transpose for the backward (built on first use): one item per
   // (sequence, k-tile), every k-tile included, entries (q-tile | class,
-  // word block) in ascending q-tile order, items most work first.
+  // word block) in descending q-tile order, items most work first.
   void *kbuf = nullptr;
   size_t off_kitems = 0, off_kentries = 0;
   int32_t num_kitems = 0;

@@ -516,7 +516,7 @@ ma_status plan_build_kmajor(ma_plan *p, void *stream) {
   std::vector<uint64_t> words;
   ma_status st = plan_fetch_host_view(p, items, ents, words);
   if (st != MA_OK) return st;
-  // Bucket every non-SKIP tile by (sequence, k-tile); q-tiles ascending.
+  // Bucket every non-SKIP tile by (sequence, k-tile).
   std::vector<int64_t> kbase(p->batch + 1, 0);
   for (int b = 0; b < p->batch; ++b) kbase[b + 1] = kbase[b] + p->nkt[b];
   const int64_t nk = kbase[p->batch];
@@ -533,8 +533,11 @@ ma_status plan_build_kmajor(ma_plan *p, void *stream) {
   for (int b = 0; b < p->batch; ++b)
     for (int32_t kt = 0; kt < p->nkt[b]; ++kt) {
       std::vector<Entry> &bk = bucket[(size_t)(kbase[b] + kt)];
+      // Descending q-tiles: under causal-like masks the key tiles of a head
+      // all end at the last q-tiles, so workgroups started together walk the
+      // same query blocks at the same time and share them in L2.
       std::sort(bk.begin(), bk.end(), [](const Entry &x, const Entry &y) {
-        return entry_kt(x.kt_cls) < entry_kt(y.kt_cls);
+        return entry_kt(x.kt_cls) > entry_kt(y.kt_cls);
       });
       if (kents.size() + bk.size() > (size_t)INT32_MAX)
         return set_error(MA_ERR_UNSUPPORTED, "plan has too many tiles for the backward");
