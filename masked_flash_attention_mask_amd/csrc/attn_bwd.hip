@@ -86,160 +86,6 @@ struct BwdParams {
   float scale, scale_log2;
 };
 
-// ---------------------------------------------------------------------------
-// D[t, h] = <dO[t, h], O[t, h]>, L2[t, h] = LSE[t, h] log2 e (+inf for a row
-// with no visible key, so that its probabilities come out exactly 0).
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep(BwdParams p) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (token, head)
-  const int lane = threadIdx.x & 63;
-  if (row >= p.total_q * p.hq) return;
-  float acc = 0.f;
-  for (int c = lane; c < D; c += 64) {
-    const float o = p.o_f32 ? ((const float *)p.o)[row * D + c]
-                            : __uint_as_float((uint32_t)((const uint16_t *)p.o)[row * D + c] << 16);
-    const float g = __uint_as_float((uint32_t)p.dout[row * D + c] << 16);
-    acc += o * g;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) {
-    p.dd[row] = acc;
-    const float lse = p.lse[row];
-    p.l2[row] = lse == neg_inf() ? __builtin_inff() : lse * kLog2e;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dQ: one workgroup per (q-tile, query head), BQ / 32 waves x 32 query rows.
-// ---------------------------------------------------------------------------
-template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq(BwdParams p) {
-  constexpr int NT = BQ * 2, S = BwdStage<D>::S;
-  extern __shared__ __align__(16) uint16_t lds[];   // [2 stages][K tile, V tile]
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int item_idx = blockIdx.x / p.hq, h = blockIdx.x - item_idx * p.hq;
-  const Item it = p.items[item_idx];
-  const SeqInfo sq = p.seqs[it.seq];
-  const int g = h / p.group;
-  const int wrow = wave * 32 + l32;
-  const int row_local = it.qt * BQ + wrow;
-  const bool row_ok = row_local < sq.q_len;
-  const int64_t tok = (int64_t)sq.q_start + row_local;
-  const int kv_len = sq.kv_len;
-
-  bf16x8 qf[D / 16], dof[D / 16];
-  load_q<D>(qf, p.q + (tok * p.hq + h) * D, row_ok, hi);
-  load_q<D>(dof, p.dout + (tok * p.hq + h) * D, row_ok, hi);
-  const float l2 = row_ok ? p.l2[tok * p.hq + h] : __builtin_inff();
-  const float dd = row_ok ? p.dd[tok * p.hq + h] : 0.f;
-  const float c = p.scale_log2;
-
-  const uint16_t *kbase = p.k + (int64_t)g * p.s_head;
-  const uint16_t *vbase = p.v + (int64_t)g * p.s_head;
-  const int32_t *pt = p.page_table + (int64_t)it.seq * p.max_pages;
-  using KV = staged::KvTile<D, NT>;
-  KV kv;
-  typename KV::Pages pg_nxt;
-  auto store_kv = [&](uint16_t *stage) {
-#pragma unroll
-    for (int i = 0; i < KV::PPT; ++i) {
-      const int pair = tid + i * NT;
-      if (KV::PAIRS % NT == 0 || pair < KV::PAIRS) {
-        const int kg = pair / KV::CH, cc = pair % KV::CH;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          *(u32x4 *)(stage + (4 * kg + j) * S + 8 * cc) = kv.kreg[i][j];
-          *(u32x4 *)(stage + 64 * S + (4 * kg + j) * S + 8 * cc) = kv.vreg[i][j];
-        }
-      }
-    }
-  };
-
-  f32x16 dqacc[D / 32];
-#pragma unroll
-  for (int n = 0; n < D / 32; ++n) dqacc[n] = f32x16{};
-
-  const int eb = it.ent_begin, ee = it.ent_end;
-  uint64_t word_nxt = 0;
-  auto load_word = [&](Entry e) -> uint64_t {
-    return entry_cls(e.kt_cls) == MA_TILE_PARTIAL ? p.words[(int64_t)e.wblk * BQ + wrow] : 0ull;
-  };
-  if (eb < ee) {
-    const Entry e0 = p.entries[eb];
-    const int kt0 = entry_kt(e0.kt_cls);
-    const typename KV::Pages pg0 = kv.pages(pt, p.page_shift, kt0, kv_len, tid);
-    kv.load(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv_len, tid);
-    word_nxt = load_word(e0);
-    if (eb + 1 < ee) pg_nxt = kv.pages(pt, p.page_shift, entry_kt(p.entries[eb + 1].kt_cls), kv_len, tid);
-    store_kv(lds);
-    __syncthreads();
-  }
-  for (int e = eb; e < ee; ++e) {
-    const int cur = (e - eb) & 1;
-    const Entry ec = p.entries[e];
-    const uint64_t wcur = word_nxt;
-    const bool has_next = e + 1 < ee;
-    if (has_next) {
-      const Entry en = p.entries[e + 1];
-      kv.load(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, entry_kt(en.kt_cls), kv_len, tid);
-      word_nxt = load_word(en);
-      if (e + 2 < ee) pg_nxt = kv.pages(pt, p.page_shift, entry_kt(p.entries[e + 2].kt_cls), kv_len, tid);
-    }
-    const uint16_t *ks = lds + cur * 2 * 64 * S;
-    const uint16_t *vs = ks + 64 * S;
-    // S^T = K Q^T and dP^T = V dO^T (keys x this wave's 32 query rows)
-    f32x16 sacc[2], dpacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-      dpacc[kb] = f32x16{};
-#pragma unroll
-      for (int k = 0; k < D / 16; ++k) {
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<D>(ks + 32 * kb * S, l32, hi, k), qf[k], sacc[kb], 0, 0, 0);
-        dpacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_op<D>(vs + 32 * kb * S, l32, hi, k), dof[k], dpacc[kb], 0, 0, 0);
-      }
-    }
-    const int kt = entry_kt(ec.kt_cls), cls = entry_cls(ec.kt_cls);
-    const int kin = kv_len - kt * 64;
-    if (cls == MA_TILE_PARTIAL || kin < 64)
-      apply_word(sacc, (cls == MA_TILE_PARTIAL ? wcur : ~0ull) & low_bits(kin), hi);
-    // P = exp2(S c - L2); dS = P (dP - D)
-    bf16x8 dsb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(__builtin_fmaf(sacc[kb][r], c, -l2));
-        dpacc[kb][r] = pr * (dpacc[kb][r] - dd);
-      }
-      dsb[2 * kb] = to_bf16x8(dpacc[kb], 0);
-      dsb[2 * kb + 1] = to_bf16x8(dpacc[kb], 1);
-    }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int n = 0; n < D / 32; ++n)
-        dqacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_op<D>(ks + 32 * (u >> 1) * S, lane, u & 1, n), dsb[u],
-                                                           dqacc[n], 0, 0, 0);
-    if (has_next) store_kv(lds + (cur ^ 1) * 2 * 64 * S);
-    __syncthreads();
-  }
-  if (row_ok) store_row<D, float>(p.dq + (tok * p.hq + h) * D, dqacc, p.scale, hi);
-}
-
-// ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (k-tile, K/V head), 4 waves.  Wave w owns keys
-// 32 (w % 2) .. + 31 of the tile (K and V rows held as B operands) and query
-// rows 32 (w / 2) .. + 31 of every 64-row block; the two waves of a key half
-// add their partial sums at the end.  Query blocks (Q, dO, and per row L2, D
-// and the tile word) are gathered straight into LDS (global_load_lds) one
-// block ahead, into two alternating stages.
-// ---------------------------------------------------------------------------
-
 // One 64-row block of Q or dO in LDS: dense rows of D bf16, 16-byte chunks
 // XOR swizzled by the row so that both the row reads (ds_read_b128 over 16
 // rows, one chunk each) and the transposed reads (ds_read_b64_tr_b16 over 4
@@ -266,6 +112,235 @@ __device__ __forceinline__ Entry load_entry(const Entry *e, int i) {
   const __attribute__((address_space(4))) Entry *c = (const __attribute__((address_space(4))) Entry *)e;
   return Entry{c[i].kt_cls, c[i].wblk};
 }
+
+typedef const __attribute__((address_space(1))) void *gptr_t;
+
+// Direct global -> LDS loads with a scalar base and a 32-bit per-lane byte
+// offset (the SGPR-base form of the instruction): lane l writes LDS address
+// m0 + 16 l (4 l).  See dma::lds_load16 for how the kernels order them.
+__device__ __forceinline__ void lds_load16_s(gptr_t base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void lds_load4_s(gptr_t base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+}
+
+// ---------------------------------------------------------------------------
+// D[t, h] = <dO[t, h], O[t, h]>, L2[t, h] = LSE[t, h] log2 e (+inf for a row
+// with no visible key, so that its probabilities come out exactly 0).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep(BwdParams p) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (token, head)
+  const int lane = threadIdx.x & 63;
+  if (row >= p.total_q * p.hq) return;
+  float acc = 0.f;
+  for (int c = lane; c < D; c += 64) {
+    const float o = p.o_f32 ? ((const float *)p.o)[row * D + c]
+                            : __uint_as_float((uint32_t)((const uint16_t *)p.o)[row * D + c] << 16);
+    const float g = __uint_as_float((uint32_t)p.dout[row * D + c] << 16);
+    acc += o * g;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) {
+    p.dd[row] = acc;
+    const float lse = p.lse[row];
+    p.l2[row] = lse == neg_inf() ? __builtin_inff() : lse * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (q-tile, query head), BQ / 32 waves x 32 query rows
+// (Q and dO rows held as B operands).  The K / V tiles of the plan's row are
+// gathered straight into LDS (global_load_lds) one tile ahead into two
+// alternating stages, both swizzled like a query block, so the row reads of
+// K and V (the A operands of S^T and dP^T) and the transposed reads of K (the
+// A operand of dQ^T) are free of bank conflicts.
+// ---------------------------------------------------------------------------
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq(BwdParams p) {
+  using QB = QBlk<D>;
+  constexpr int NW = BQ / 32, CH = D / 8, NI = CH / NW;   // gather instructions per wave per matrix
+  constexpr int TILE = 64 * D;                             // elements of one 64-key matrix
+  extern __shared__ __align__(16) uint16_t lds[];          // [2 stages][K tile, V tile]
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int item_idx = blockIdx.x / p.hq, h = blockIdx.x - item_idx * p.hq;
+  const Item it = p.items[item_idx];
+  const SeqInfo sq = p.seqs[it.seq];
+  const int g = h / p.group;
+  const int wrow = wave * 32 + l32;
+  const int row_local = it.qt * BQ + wrow;
+  const bool row_ok = row_local < sq.q_len;
+  const int64_t tok = (int64_t)sq.q_start + row_local;
+  const int kv_len = sq.kv_len;
+
+  bf16x8 qf[D / 16], dof[D / 16];
+  load_q<D>(qf, p.q + (tok * p.hq + h) * D, row_ok, hi);
+  load_q<D>(dof, p.dout + (tok * p.hq + h) * D, row_ok, hi);
+  const float l2 = row_ok ? p.l2[tok * p.hq + h] : __builtin_inff();
+  const float dd = row_ok ? p.dd[tok * p.hq + h] : 0.f;
+  const float c = p.scale_log2;
+
+  const uint16_t *kbase = p.k + (int64_t)g * p.s_head;
+  const uint16_t *vbase = p.v + (int64_t)g * p.s_head;
+  const int32_t *pt = p.page_table + (int64_t)it.seq * p.max_pages;
+  const int pmask = (1 << p.page_shift) - 1;
+  // Gather: instruction t of a matrix fills LDS chunks [64 t, 64 t + 64);
+  // lane l of it loads key row (64 t + l) / CH, logical chunk ((64 t + l) %
+  // CH) ^ f(row).  Keys past kv_len repeat the last key (masked to 0).
+  int32_t pg[NI];
+  auto pages = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (64 * (wave * NI + i) + lane) / CH;
+      pg[i] = pt[min(kt * 64 + r, kv_len - 1) >> p.page_shift];
+    }
+  };
+  auto issue = [&](int kt, int sl) {
+    uint16_t *st = lds + sl * 2 * TILE;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int t = wave * NI + i;
+      const int pos = 64 * t + lane, r = pos / CH, pc = pos % CH;
+      const int key = min(kt * 64 + r, kv_len - 1);
+      const int64_t off = (int64_t)pg[i] * p.s_page + (int64_t)(key & pmask) * p.s_slot + 8 * (pc ^ QB::f(r));
+      dma::lds_load16(kbase + off, dma::lds_addr(st + 512 * t));
+      dma::lds_load16(vbase + off, dma::lds_addr(st + TILE + 512 * t));
+    }
+  };
+  // Row reads (K, V rows 32 kb + l32, chunk 2 k + hi) and transposed reads
+  // (K rows 16 u + j (+ 8), columns 32 n + ...) in the swizzled layout.
+  const int rx = 8 * (hi ^ QB::f(l32));
+  const int j = 4 * hi + ((lane & 15) >> 2);
+  const int cb = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tax = 8 * (cb ^ QB::f(j)) + 4 * (lane & 1);
+  const int tbx = 8 * (cb ^ QB::f(j + 8)) + 4 * (lane & 1);
+  auto tr_read = [&](const uint16_t *m, int u, int n) -> bf16x8 {
+    const uint16_t *b = m + (j + 16 * u) * D;
+    const i16x4 r0 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(b + ((32 * n) ^ tax)));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(b + 8 * D + ((32 * n) ^ tbx)));
+    const i16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  f32x16 dqacc[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) dqacc[n] = f32x16{};
+
+  const int eb = it.ent_begin, ee = it.ent_end;
+  auto load_word = [&](Entry e) -> uint64_t {
+    return entry_cls(e.kt_cls) == MA_TILE_PARTIAL ? p.words[(int64_t)e.wblk * BQ + wrow] : 0ull;
+  };
+  if (eb < ee) {
+    const Entry e0 = load_entry(p.entries, eb);
+    pages(entry_kt(e0.kt_cls));
+    issue(entry_kt(e0.kt_cls), 0);
+    uint64_t word_nxt = load_word(e0);
+    if (eb + 1 < ee) pages(entry_kt(load_entry(p.entries, eb + 1).kt_cls));
+    for (int e = eb; e < ee; ++e) {
+      const int cur = (e - eb) & 1;
+      dma::wait_vmem();
+      __syncthreads();   // tile e is in stage cur; every wave is done with stage cur ^ 1
+      const Entry ec = load_entry(p.entries, e);
+      const uint64_t wcur = word_nxt;
+      if (e + 1 < ee) {
+        const Entry en = load_entry(p.entries, e + 1);
+        issue(entry_kt(en.kt_cls), cur ^ 1);
+        word_nxt = load_word(en);
+        if (e + 2 < ee) pages(entry_kt(load_entry(p.entries, e + 2).kt_cls));
+      }
+      const uint16_t *ks = lds + cur * 2 * TILE;
+      const uint16_t *vs = ks + TILE;
+      // S^T = K Q^T (64 keys x this wave's 32 query rows), then dP^T = V dO^T
+      // with P = exp2(S c - L2) computed beside it; operands of step k + 1
+      // are read while step k's products run.
+      const int kt = entry_kt(ec.kt_cls), cls = entry_cls(ec.kt_cls);
+      const int kin = kv_len - kt * 64;
+      f32x16 sacc[2], dpacc[2];
+      {
+        bf16x8 ka[2][2];
+        auto read_k = [&](int k, int sl) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            ka[sl][kb] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(ks + (32 * kb + l32) * D + ((16 * k) ^ rx)));
+        };
+        read_k(0, 0);
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) {
+          if (k + 1 < D / 16) read_k(k + 1, (k + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            sacc[kb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[k & 1][kb], qf[k], k == 0 ? f32x16{} : sacc[kb], 0, 0, 0);
+        }
+      }
+      if (cls == MA_TILE_PARTIAL || kin < 64)
+        apply_word(sacc, (cls == MA_TILE_PARTIAL ? wcur : ~0ull) & low_bits(kin), hi);
+      {
+        constexpr int KS = D / 16, RPS = 32 / KS;   // P elements finished per dP step
+        bf16x8 va[2][2];
+        auto read_v = [&](int k, int sl) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            va[sl][kb] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(vs + (32 * kb + l32) * D + ((16 * k) ^ rx)));
+        };
+        read_v(0, 0);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          if (k + 1 < KS) read_v(k + 1, (k + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            dpacc[kb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[k & 1][kb], dof[k], k == 0 ? f32x16{} : dpacc[kb], 0, 0, 0);
+#pragma unroll
+          for (int x = 0; x < RPS; ++x) {
+            const int el = RPS * k + x, kb = el >> 4, r = el & 15;
+            sacc[kb][r] = fast_exp2(__builtin_fmaf(sacc[kb][r], c, -l2));
+          }
+        }
+      }
+      // dS = P (dP - D), rounded to bf16
+      bf16x8 dsb[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dpacc[kb][r] = sacc[kb][r] * (dpacc[kb][r] - dd);
+        dsb[2 * kb] = to_bf16x8(dpacc[kb], 0);
+        dsb[2 * kb + 1] = to_bf16x8(dpacc[kb], 1);
+      }
+      // dQ^T += K^T dS^T (keys 16 u .. of the tile); transposed operands read one step ahead
+      {
+        constexpr int NS = 4 * (D / 32);
+        bf16x8 ta[2];
+        auto read_t = [&](int x, int sl) { ta[sl] = tr_read(ks, x / (D / 32), x % (D / 32)); };
+        read_t(0, 0);
+#pragma unroll
+        for (int x = 0; x < NS; ++x) {
+          if (x + 1 < NS) read_t(x + 1, (x + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          const int u = x / (D / 32), n = x % (D / 32);
+          dqacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[x & 1], dsb[u], dqacc[n], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (row_ok) store_row<D, float>(p.dq + (tok * p.hq + h) * D, dqacc, p.scale, hi);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (k-tile, K/V head), 4 waves.  Wave w owns keys
+// 32 (w % 2) .. + 31 of the tile (K and V rows held as B operands) and query
+// rows 32 (w / 2) .. + 31 of every 64-row block; the two waves of a key half
+// add their partial sums at the end.  Query blocks (Q, dO, and per row L2, D
+// and the tile word) are gathered straight into LDS (global_load_lds) one
+// block ahead, into two alternating stages.
+// ---------------------------------------------------------------------------
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv(BwdParams p) {
@@ -493,18 +568,6 @@ struct QBlkW {
   static constexpr int K1_OFF = V_OFF + 64 * D;      // K rows of keys 32..63, 32 x D, swizzled likewise
   static constexpr size_t LDS = (size_t)(K1_OFF + 32 * D) * sizeof(uint16_t);
 };
-
-typedef const __attribute__((address_space(1))) void *gptr_t;
-
-// Direct global -> LDS loads with a scalar base and a 32-bit per-lane byte
-// offset (the SGPR-base form of the instruction): lane l writes LDS address
-// m0 + 16 l (4 l).  See dma::lds_load16 for how the kernels order them.
-__device__ __forceinline__ void lds_load16_s(gptr_t base, uint32_t voff, uint32_t m0) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
-}
-__device__ __forceinline__ void lds_load4_s(gptr_t base, uint32_t voff, uint32_t m0) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
-}
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide(BwdParams p) {
@@ -834,7 +897,7 @@ ma_status run(const BackwardArgs &a, const BwdParams &prm) {
   const int64_t rows = a.total_q * a.hq;
   ma_status st = launch(bwd_prep<D>, (int)((rows + 3) / 4), 256, 0, prm, a.stream, "backward prep");
   if (st != MA_OK) return st;
-  const size_t dq_lds = 2 * 2 * 64 * BwdStage<D>::S * sizeof(uint16_t);
+  const size_t dq_lds = 2 * 2 * 64 * D * sizeof(uint16_t);
   if (prm.tile_q == 128)
     st = launch(bwd_dq<D, 128>, prm.num_items * a.hq, 256, dq_lds, prm, a.stream, "backward dQ");
   else
