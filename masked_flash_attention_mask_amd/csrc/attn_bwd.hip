@@ -706,8 +706,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide(BwdParams p) {
         //   dK^T += Q^T dS.
         // Register r of a lane holds query row 8 (r / 4) + 4 hi + r % 4 and
         // key 32 kb + l32; its visibility is bit l32 of half kb of the row's
-        // tile word (all ones for a FULL tile).  Operands of step k + 1 are
-        // read while step k's products run.
+        // tile word.  Operands of step k + 1 are read while step k's products
+        // run.
         constexpr int KS = D / 16;              // k-steps of S and dP
         constexpr int RPS = 16 / KS;            // rows of P finished per dP step
         const uint32_t *wd = (const uint32_t *)(qs + QW::META + 256);
@@ -733,7 +733,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide(BwdParams p) {
             sb[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[sl], kb1[sl], k == 0 ? f32x16{} : sb[1], 0, 0, 0);
           }
         }
-        // dP, and beside it P = exp2(S c - L2) on visible entries
+        // Masked entries (PARTIAL tiles, keys past kv_len) get S = -inf, so
+        // exp2 gives them exactly 0; FULL interior tiles skip this.
+        if (cls == MA_TILE_PARTIAL || kin < 64) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * hi + (r & 3);
+            const uint32_t wlo = wd[2 * row], whi = wd[2 * row + 1];
+            if (!((wlo | full) & kbit0)) sb[0][r] = neg_inf();
+            if (!((whi | full) & kbit1)) sb[1][r] = neg_inf();
+          }
+        }
+        // dP, and beside it P = exp2(S c - L2)
         f32x16 dpb[2];
         f32x8 pv[2][2];   // P as fp32 (for dS), [kb][u]
         bf16x8 pb[2][2];
@@ -756,13 +767,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_wide(BwdParams p) {
 #pragma unroll
             for (int rr = 0; rr < RPS; ++rr) {
               const int r = RPS * k + rr, a4 = r >> 2, b = r & 3;
-              const int row = 8 * a4 + 4 * hi + b;
-              const float l2 = meta[row];
-              const uint32_t wlo = wd[2 * row], whi = wd[2 * row + 1];
-              const float e0 = fast_exp2(__builtin_fmaf(sb[0][r], c, -l2));
-              const float e1 = fast_exp2(__builtin_fmaf(sb[1][r], c, -l2));
-              pv[0][r >> 3][r & 7] = ((wlo | full) & kbit0) ? e0 : 0.f;
-              pv[1][r >> 3][r & 7] = ((whi | full) & kbit1) ? e1 : 0.f;
+              const float l2 = meta[8 * a4 + 4 * hi + b];
+              pv[0][r >> 3][r & 7] = fast_exp2(__builtin_fmaf(sb[0][r], c, -l2));
+              pv[1][r >> 3][r & 7] = fast_exp2(__builtin_fmaf(sb[1][r], c, -l2));
             }
           }
 #pragma unroll
