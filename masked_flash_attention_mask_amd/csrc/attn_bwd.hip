@@ -113,14 +113,12 @@ __device__ __forceinline__ Entry load_entry(const Entry *e, int i) {
   return Entry{c[i].kt_cls, c[i].wblk};
 }
 
-typedef const __attribute__((address_space(1))) void *gptr_t;
+using dma::gptr_t;
 
-// Direct global -> LDS loads with a scalar base and a 32-bit per-lane byte
-// offset (the SGPR-base form of the instruction): lane l writes LDS address
-// m0 + 16 l (4 l).  See dma::lds_load16 for how the kernels order them.
-__device__ __forceinline__ void lds_load16_s(gptr_t base, uint32_t voff, uint32_t m0) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
-}
+// Direct global -> LDS load of 4 bytes per lane with a scalar base and a
+// 32-bit per-lane byte offset: lane l writes LDS address m0 + 4 l.  See
+// dma::lds_load16 for how the kernels order them.
+using dma::lds_load16_s;
 __device__ __forceinline__ void lds_load4_s(gptr_t base, uint32_t voff, uint32_t m0) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
 }

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
   using C = Bf16Cfg<D, BQ, DMA>;
   extern __shared__ __align__(16) uint16_t lds[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   int item_idx, h;
   map_block(blockIdx.x, p.num_items, p.hq, item_idx, h);
@@ -143,12 +143,13 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
   if constexpr (DMA) {
     using KV = dma::KvDma<D, C::NW>;
     const dma::LaneOffsets<D> lo(lane);
+    const uint32_t lds0 = dma::lds_addr(lds);
     typename KV::Pages pg_nxt;
     if (eb < ee) {
       const Entry e0 = load_entry(p.entries, eb);
       const int kt0 = entry_kt(e0.kt_cls);
       const typename KV::Pages pg0 = KV::pages_uniform(pt, p.page_shift, kt0, kv_len, wave);
-      KV::issue(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv_len, lds, wave, lane);
+      KV::issue(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv_len, lds0, wave, lane);
       word_nxt = load_word(e0);
       if (eb + 1 < ee)
         pg_nxt = KV::pages_uniform(pt, p.page_shift, entry_kt(load_entry(p.entries, eb + 1).kt_cls), kv_len, wave);
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
       if (e + 1 < ee) {
         const Entry en = load_entry(p.entries, e + 1);
         KV::issue(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, entry_kt(en.kt_cls), kv_len,
-                  lds + (cur ^ 1) * dma::Stage<D>::ELEMS, wave, lane);
+                  lds0 + (uint32_t)((cur ^ 1) * dma::Stage<D>::BYTES), wave, lane);
         word_nxt = load_word(en);
         if (e + 2 < ee)
           pg_nxt = KV::pages_uniform(pt, p.page_shift, entry_kt(load_entry(p.entries, e + 2).kt_cls), kv_len, wave);
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(BQ * 2, 1) void prefill_f32_kernel(PrefillParams p)
   float *Ks = ldsf;
   float *Vs = ldsf + 64 * C::KS;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   int item_idx, h;
   map_block(blockIdx.x, p.num_items, p.hq, item_idx, h);
@@ -381,10 +382,11 @@ ma_status dispatch_bf16_mode(const PrefillArgs &a, const PrefillParams &prm, int
 }
 
 // The direct gather needs the key rows of one gather instruction (512 / d of
-// them) inside one page.
+// them) inside one page, and a page's bytes addressable by a 32-bit offset.
 template <int D, int BQ>
 ma_status dispatch_bf16(const PrefillArgs &a, const PrefillParams &prm, int grid) {
-  if ((1 << a.page_shift) >= dma::KvDma<D, BQ / 32>::RPI) return dispatch_bf16_mode<D, BQ, true>(a, prm, grid);
+  const bool fits = ((int64_t)1 << a.page_shift) * a.s_slot * 2 < ((int64_t)1 << 31);
+  if ((1 << a.page_shift) >= dma::KvDma<D, BQ / 32>::RPI && fits) return dispatch_bf16_mode<D, BQ, true>(a, prm, grid);
   return dispatch_bf16_mode<D, BQ, false>(a, prm, grid);
 }
 

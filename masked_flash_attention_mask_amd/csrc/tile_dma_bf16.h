@@ -39,6 +39,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 __device__ __forceinline__ void lds_load16(const void *src, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
+// The same with a scalar (SGPR) base and a 32-bit per-lane byte offset.
+typedef const __attribute__((address_space(1))) void *gptr_t;
+__device__ __forceinline__ void lds_load16_s(gptr_t base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
 
 // Direct global -> LDS gather of one tile by NW waves: wave instruction t
 // fills LDS chunks [64 t, 64 t + 64) of K (and of V); lane l of it loads the
@@ -84,7 +89,14 @@ struct KvDma {
     return pg;
   }
 
-  __device__ __forceinline__ static void issue(const uint16_t *kbase, const uint16_t *vbase, const Pages &pg,
+  // Issues this wave's gathers of tile kt into the stage at LDS byte address
+  // stage (scalar), with page ids from pages_uniform: each instruction's RPI
+  // rows share one page,
+  // so its source is a scalar page base plus a 32-bit per-lane offset (the
+  // SGPR-base form of the instruction), and M0 is scalar arithmetic: no
+  // 64-bit per-lane address math.  Needs page_size * s_slot * 2 < 2^31.
+  // Per-lane page ids (any page size): a 64-bit address per lane.
+  __device__ __forceinline__ static void issue_lanes(const uint16_t *kbase, const uint16_t *vbase, const Pages &pg,
                                                int page_shift, int64_t s_page, int64_t s_slot, int kt,
                                                int kv_len, uint16_t *stage, int wave, int lane) {
     const int pmask = (1 << page_shift) - 1;
@@ -97,6 +109,23 @@ struct KvDma {
       const int64_t off = (int64_t)pg.id[i] * s_page + (int64_t)(key & pmask) * s_slot;
       lds_load16(kbase + off + 8 * (pc ^ Stage<D>::fk(r)), lds_addr(stage + 512 * t));
       lds_load16(vbase + off + 8 * (pc ^ Stage<D>::fv(r)), lds_addr(stage + Stage<D>::V_OFF + 512 * t));
+    }
+  }
+
+  __device__ __forceinline__ static void issue(const uint16_t *kbase, const uint16_t *vbase, const Pages &pg,
+                                               int page_shift, int64_t s_page, int64_t s_slot, int kt,
+                                               int kv_len, uint32_t stage, int wave, int lane) {
+    const int pmask = (1 << page_shift) - 1;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int t = wave * IPW + i;
+      const int pos = 64 * t + lane;
+      const int r = pos / CH, pc = pos % CH;
+      const int key = min(kt * 64 + r, kv_len - 1);
+      const int64_t pb = (int64_t)pg.id[i] * s_page;
+      const uint32_t slot = (uint32_t)((key & pmask) * (int)s_slot) * 2;
+      lds_load16_s((gptr_t)(kbase + pb), slot + 16 * (pc ^ Stage<D>::fk(r)), stage + 1024 * t);
+      lds_load16_s((gptr_t)(vbase + pb), slot + 16 * (pc ^ Stage<D>::fv(r)), stage + 2 * Stage<D>::V_OFF + 1024 * t);
     }
   }
 };

@@ -198,7 +198,7 @@ __device__ __forceinline__ uint64_t fetch_word(const VerifyParams &p, int64_t mo
 template <int D, int NW, typename OutT, bool UP>
 __global__ __launch_bounds__(NW * 64, 1) void verify_kernel(VerifyParams p) {
   extern __shared__ __align__(16) uint16_t lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int split = blockIdx.x, b = blockIdx.z;
   const int q0 = p.cu_seqlens_q[b], q_len = p.cu_seqlens_q[b + 1] - q0;
@@ -229,6 +229,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_kernel(VerifyParams p) {
   const int32_t *pt = p.page_table + (int64_t)b * p.max_pages;
   using KV = KvDma<D, NW>;
   const LaneOffsets<D> lo(lane);
+  const uint32_t lds0 = lds_addr(lds);
   typename KV::Pages pg_nxt;
   auto pages = [&](int kt) {
     if constexpr (UP)
@@ -247,7 +248,10 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_kernel(VerifyParams p) {
   uint64_t word_nxt = 0;
   if (kt0 < kt1) {
     const typename KV::Pages pg0 = pages(kt0);
-    KV::issue(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv, lds, wave, lane);
+    if constexpr (UP)
+      KV::issue(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv, lds0, wave, lane);
+    else
+      KV::issue_lanes(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv, lds, wave, lane);
     word_nxt = fetch_word(p, moff, plen, t, row_ok, r0, q_len, kv, kt0, lane);
     if (kt0 + 1 < kt1) pg_nxt = pages(kt0 + 1);
     wait_vmem();
@@ -260,8 +264,12 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_kernel(VerifyParams p) {
       // The mask word first: a dense mask's ballots wait for its loads, and
       // that wait would otherwise include the gather.
       word_nxt = fetch_word(p, moff, plen, t, row_ok, r0, q_len, kv, kt + 1, lane);
-      KV::issue(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, kt + 1, kv,
-                lds + (cur ^ 1) * Stage<D>::ELEMS, wave, lane);
+      if constexpr (UP)
+        KV::issue(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, kt + 1, kv,
+                  lds0 + (uint32_t)((cur ^ 1) * Stage<D>::BYTES), wave, lane);
+      else
+        KV::issue_lanes(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, kt + 1, kv,
+                        lds + (cur ^ 1) * Stage<D>::ELEMS, wave, lane);
       if (kt + 2 < kt1) pg_nxt = pages(kt + 2);
     }
     const uint16_t *stage = lds + cur * Stage<D>::ELEMS;
@@ -335,8 +343,11 @@ __global__ __launch_bounds__(256) void verify_combine(VerifyParams p) {
 template <int D, int NW, typename OutT>
 ma_status run(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh) {
   const size_t lds = 2 * Stage<D>::BYTES;
-  auto kern = (1 << a.page_shift) >= KvDma<D, NW>::RPI ? verify_kernel<D, NW, OutT, true>
-                                                       : verify_kernel<D, NW, OutT, false>;
+  // Uniform pages: the rows of one gather instruction share a page whose
+  // bytes a 32-bit offset reaches.
+  const bool up = (1 << a.page_shift) >= KvDma<D, NW>::RPI &&
+                  ((int64_t)1 << a.page_shift) * a.s_slot * 2 < ((int64_t)1 << 31);
+  auto kern = up ? verify_kernel<D, NW, OutT, true> : verify_kernel<D, NW, OutT, false>;
   hipError_t e = hipSuccess;
   if (lds > 64 * 1024) e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
