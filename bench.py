@@ -35,6 +35,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "masked-attn prefill effective TFLOP/s (unmasked FLOPs) and % of bf16 MFMA peak"
 KERNEL_SOURCES = ["masked_flash_attention_mask_amd/csrc/attn_fwd.hip",
                   "masked_flash_attention_mask_amd/csrc/tile_bf16.h",
+                  "masked_flash_attention_mask_amd/csrc/tile_dma_bf16.h",
                   "masked_flash_attention_mask_amd/csrc/kernels_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_d128_chunk_causal_16k_traffic.txt")
 
