@@ -1,4 +1,5 @@
-"""CPU oracle for masked flash-attention prefill and tree verify.
+"""CPU oracle for masked flash-attention prefill, its gradients, and tree
+verify.
 
 TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, fp64 statement of
 what the GPU path computes.  Only the test-suite, the package smoke check and
@@ -24,6 +25,8 @@ Sources (the web pages this method is taken from):
 Modules:
   masks      dense boolean masks for every mask kind (definitions written out)
   attention  fp64 softmax(Q K^T * scale + mask) V over ragged, paged K/V
+  backward   fp64 dQ, dK, dV of the same attention for an upstream dO (whole
+             sequences, or sampled rows and keys of one head)
   tiles      per-(q-tile, k-tile) FULL / SKIP / PARTIAL classes and words
 
 Parity pins: every function here is pinned by the tests under tests/ that
@@ -33,4 +36,4 @@ BI_CAUSAL semantics, the sliding-window boundary) are pinned only against
 their own written definition: parity unpinned for those two points.
 """
 
-from . import masks, attention, tiles  # noqa: F401
+from . import masks, attention, backward, tiles  # noqa: F401

@@ -50,6 +50,45 @@ def attend_backward(q, k, v, mask, scale, do):
     return dq, dk, dv
 
 
+def attend_backward_sampled(q, k, v, mask, scale, do, rows, keys, chunk=1024):
+    """attend_backward evaluated only where asked: dq for the query rows
+    `rows` and dk, dv for the keys `keys` of one head (q, do [n, d]; k, v
+    [m, d]; mask bool [n, m] or a callable (r0, r1) -> mask rows r0..r1-1).
+    The same definition, taken over row chunks so that no n x m matrix is
+    held: per chunk S, P (with the chunk's own row normaliser), dP and
+    D = rowsum(P dP) are exact row by row, and the dk / dv sums over rows are
+    accumulated chunk by chunk.  Returns (dq [len(rows), d], dk [len(keys),
+    d], dv [len(keys), d]) in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    n = q.shape[0]
+    dq = np.zeros((len(rows), k.shape[1]))
+    dk = np.zeros((len(keys), q.shape[1]))
+    dv = np.zeros((len(keys), do.shape[1]))
+    for r0 in range(0, n, chunk):
+        r1 = min(n, r0 + chunk)
+        mk = mask(r0, r1) if callable(mask) else np.asarray(mask[r0:r1], dtype=bool)
+        has = mk.any(axis=1)
+        s = np.where(mk, scale * (q[r0:r1] @ k.T), -np.inf)
+        m = np.where(has, s.max(axis=1, initial=-np.inf), 0.0)
+        e = np.where(mk, np.exp(s - m[:, None]), 0.0)
+        l = e.sum(axis=1)
+        p = np.where(has[:, None], e / np.where(has, l, 1.0)[:, None], 0.0)
+        dp = do[r0:r1] @ v.T
+        dd = (p * dp).sum(axis=1)
+        ds = p * (dp - dd[:, None])
+        dv += p[:, keys].T @ do[r0:r1]
+        dk += scale * (ds[:, keys].T @ q[r0:r1])
+        sel = (rows >= r0) & (rows < r1)
+        if sel.any():
+            dq[sel] = scale * (ds[rows[sel] - r0] @ k)
+    return dq, dk, dv
+
+
 def attention_backward(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, masks, scale, do,
                        kv_heads=None):
     """Gradients of the ragged, paged, masked attention of oracle.attention.

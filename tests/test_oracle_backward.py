@@ -158,3 +158,24 @@ def test_gqa_sums_query_heads():
         dks, dvs = dks + b, dvs + c
     assert np.allclose(A.gather_paged(dk, table[0], 9, 0), dks)
     assert np.allclose(A.gather_paged(dv, table[0], 9, 0), dvs)
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 64])
+def test_sampled_equals_whole(chunk):
+    """The sampled, row-chunked evaluation returns exactly the whole-matrix
+    gradients at the sampled rows and keys (a mask given as a matrix and as
+    a row-block callable), empty rows included."""
+    rng = np.random.default_rng(16)
+    n, m, d = 37, 53, 8
+    q, k, v, do = (rng.standard_normal((x, d)) for x in (n, m, m, n))
+    mask = rng.random((n, m)) < 0.4
+    mask[5] = False
+    mask[:, 0] |= M.causal(n, m)[:, 0]
+    dq, dk, dv = B.attend_backward(q, k, v, mask, 0.3, do)
+    rows = np.array([0, 5, 17, 36])
+    keys = np.array([0, 1, 26, 52])
+    for mk in (mask, lambda r0, r1: mask[r0:r1]):
+        sq, sk, sv = B.attend_backward_sampled(q, k, v, mk, 0.3, do, rows, keys, chunk=chunk)
+        assert np.allclose(sq, dq[rows], rtol=1e-12, atol=1e-13)
+        assert np.allclose(sk, dk[keys], rtol=1e-12, atol=1e-13)
+        assert np.allclose(sv, dv[keys], rtol=1e-12, atol=1e-13)
