@@ -138,3 +138,44 @@ def test_backward_rejects_unsupported():
     with pytest.raises(ma.MaskAttnError):
         ma.attn_backward_masked(plan, dev["q"], dev["k"], dev["v"], dev["pt"], out, lse, dev["do"], w.scale,
                                 workspace=torch.empty(8, dtype=torch.uint8, device="cuda"))
+
+
+def test_backward_full_size_sampled():
+    """The benchmark's backward at full size: one 16384-token sequence,
+    chunk-causal (chunk 2 after a 1024-token causal prefix, one CHUNK_CAUSAL
+    range), 16 heads, d 128; the library's forward (fp32 output) feeds it.
+    The oracle computes exact gradients for two heads at sampled query rows
+    and keys (tile and range boundaries, the ends, random picks)."""
+    from oracle import masks as OM
+    from oracle import attention as OA
+    w = W.config4(chunk_sizes=(2,))
+    dev = device_inputs(w)
+    do = W.upstream_grad(w, 4001)
+    dev["do"] = torch.from_numpy(do).cuda().to(torch.bfloat16).contiguous()
+    name = "chunk2"
+    _say("backward full size", name)
+    out, lse, plan = run_prefill(w, dev, name, out_dtype=torch.float32)
+    dq, dk, dv = ma.attn_backward_masked(plan, dev["q"], dev["k"], dev["v"], dev["pt"], out, lse, dev["do"], w.scale)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+    n = int(w.kv_lens[0])
+    rng = np.random.default_rng(44)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 1023, 1024, 1025, 8191, n - 2, n - 1],
+                                     rng.integers(0, n, 22)]))
+    keys = np.unique(np.concatenate([[0, 63, 64, 1023, 1024, 1025, 8192, n - 64, n - 1], rng.integers(0, n, 23)]))
+    mask = OM.ranges(n, n, w.masks[name].ranges[0])
+    page = w.page_size
+    slots = (w.page_table[0, keys // page], keys % page)
+    for h in (0, 9):
+        _say("oracle head", h)
+        k = OA.gather_paged(w.k_cache, w.page_table[0], n, h)
+        v = OA.gather_paged(w.v_cache, w.page_table[0], n, h)
+        rq, rk, rv = OB.attend_backward_sampled(w.q[:, h], k, v, mask, w.scale, do[:, h], rows, keys)
+        gq = dq[rows, h]
+        errq = float(np.abs(gq - rq).max() / np.sqrt((rq ** 2).mean()))
+        _say("dq max err / rms", errq)
+        assert errq <= 2.0 ** -3, (h, errq)
+        for g, r, what in ((dk[slots[0], slots[1], h], rk, "dk"), (dv[slots[0], slots[1], h], rv, "dv")):
+            err = grad_err(torch.from_numpy(g), r)
+            _say(what, "row metric", err)
+            assert err <= TOL_GRAD, (h, what, err)
