@@ -19,11 +19,13 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I" + os.path.
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
 
 
-# Per-source flags.  The backward kernels keep their dK / dV sums in the
-# accumulation registers and the score blocks in vector registers; the
-# VGPR form of the matrix instructions lets the allocator do that with fewer
-# register copies.
-SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source flags.  The matrix-core kernels are compiled with the VGPR form
+# of the matrix instructions: the allocator then keeps score blocks in vector
+# registers and uses the accumulation registers as spill room, with fewer
+# copies than the default AGPR form (no spills at d = 256, -12% on the d = 256
+# prefill, -3.5% on the backward; d <= 128 prefill unchanged).
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+SOURCE_FLAGS = {"attn_bwd.hip": _VGPR_FORM, "attn_fwd.hip": _VGPR_FORM, "verify.hip": _VGPR_FORM}
 
 
 def _compile(src):
