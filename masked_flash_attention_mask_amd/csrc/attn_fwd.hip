@@ -135,7 +135,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
   float m_ref = neg_inf();
-  f32x16 lsum = f32x16{};
+  float lsum = 0.f;   // this lane's half of its row sum
   const float c = p.scale_log2;
 
   const int eb = it.ent_begin, ee = it.ent_end;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
       __syncthreads();
     }
   }
-  epilogue<D, OutT>(p, oacc, m_ref, lsum[0], tok, h, row_ok, hi);
+  epilogue<D, OutT>(p, oacc, m_ref, sum_halves(lsum), tok, h, row_ok, hi);
 }
 
 // ---------------------------------------------------------------------------

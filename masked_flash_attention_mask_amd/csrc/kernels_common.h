@@ -84,6 +84,19 @@ __device__ __forceinline__ void apply_word(f32x16 (&s)[2], uint64_t word, int hi
   }
 }
 
+// acc + the sum of the 8 bf16 values of x (v_dot2_f32_bf16 against (1, 1),
+// fp32 accumulation).
+__device__ __forceinline__ float row_sum_bf16(const bf16x8 &x, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {x[2 * i], x[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
+}
+
 // Both 32-lane halves of a wave hold the same 32 query rows (other keys):
 // combine a per-lane value with its partner lane l ^ 32.
 __device__ __forceinline__ float max_halves(float x) {

@@ -214,16 +214,15 @@ __device__ __forceinline__ void read_vt(const uint16_t *vlane, bf16x8 (&a)[D / 3
   }
 }
 
-// lsum accumulates, through one more product per 16 keys with an all-ones
-// A operand, the row sums of exactly the bf16 probabilities that enter P V
-// (every register of lsum holds the lane's query-row sum).
+// lsum accumulates the lane's share of its query-row sum over exactly the
+// bf16 probabilities that enter P V (see row_sum_bf16); the two halves of a
+// row are added at the end.
 template <int D>
 __device__ __forceinline__ void pv_tile(const uint16_t *stage, const f32x16 (&p)[2], f32x16 (&o)[D / 32],
-                                        f32x16 &lsum, int l32, int hi) {
+                                        float &lsum, int l32, int hi) {
   const int lane = 32 * hi + l32;
   const uint16_t *vlane = stage + Stage<D>::V_OFF + (4 * hi + ((lane & 15) >> 2)) * Stage<D>::VS +
                           16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   // V^T operands of product u + 1 are read while product u runs (d <= 128);
   // d = 256 reads each product's operands just before it (register budget).
   constexpr int NB = D <= 128 ? 2 : 1;
@@ -240,7 +239,7 @@ __device__ __forceinline__ void pv_tile(const uint16_t *stage, const f32x16 (&p)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u % NB][n], pb, o[n], 0, 0, 0);
-    lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb, lsum, 0, 0, 0);
+    lsum = row_sum_bf16(pb, lsum);
   }
 }
 

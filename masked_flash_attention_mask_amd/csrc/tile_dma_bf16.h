@@ -216,15 +216,16 @@ __device__ __forceinline__ void read_vt(const uint16_t *stage, const LaneOffsets
   }
 }
 
-// lsum accumulates, through one more product per 16 keys with an all-ones
-// A operand, the row sums of exactly the bf16 probabilities that enter P V
-// (every register of lsum holds the lane's query-row sum).  V^T operands of
+// lsum accumulates the lane's share of its query-row sum (the 32 keys of the
+// tile this lane's half holds), over exactly the bf16 probabilities that
+// enter P V: v_dot2_f32_bf16 against (1, 1) adds two of them per vector
+// instruction, which keeps the matrix cores for the products.  The two
+// halves of a row are added once, at the end.  V^T operands of
 // product u + 1 are read while product u runs (d <= 128); d = 256 reads each
 // product's operands just before it (register budget).
 template <int D>
 __device__ __forceinline__ void pv_tile(const uint16_t *stage, const LaneOffsets<D> &lo, const f32x16 (&p)[2],
-                                        f32x16 (&o)[D / 32], f32x16 &lsum) {
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+                                        f32x16 (&o)[D / 32], float &lsum) {
   constexpr int NB = D <= 128 ? 2 : 1;
   bf16x8 a[NB][D / 32];
   if (NB == 2) read_vt<D>(stage, lo, a[0], 0);
@@ -239,7 +240,7 @@ __device__ __forceinline__ void pv_tile(const uint16_t *stage, const LaneOffsets
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u % NB][n], pb, o[n], 0, 0, 0);
-    lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb, lsum, 0, 0, 0);
+    lsum = row_sum_bf16(pb, lsum);
   }
 }
 

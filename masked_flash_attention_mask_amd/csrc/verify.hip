@@ -242,7 +242,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_kernel(VerifyParams p) {
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
   float m_ref = neg_inf();
-  f32x16 lsum = f32x16{};
+  float lsum = 0.f;   // this lane's half of its row sum
   const float c = p.scale_log2;
 
   uint64_t word_nxt = 0;
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_kernel(VerifyParams p) {
     __syncthreads();
   }
 
-  const float lt = lsum[0];
+  const float lt = sum_halves(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse = lt > 0.f ? (m_ref + __log2f(lt)) * kLn2 : neg_inf();
   if (!row_ok) return;
