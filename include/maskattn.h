@@ -19,7 +19,8 @@
  *    after it (highlights).
  *  - flashinfer issue 724, "Custom mask slows down attention.": a float mask
  *    bit-packed before the kernel, the block-sparse alternative, tree
- *    attention for speculative decoding as a custom mask.
+ *    attention for speculative decoding as a custom mask, and the question
+ *    whether a sliding window and a custom mask can be used jointly.
  *  - MagiAttention issue 316, "Feature request: chunk-causal mask type for
  *    Flex Flash Attention": (q_range, k_range, attn_type) lists with types
  *    FULL, CAUSAL, INV_CAUSAL, BI_CAUSAL and the proposed CHUNK_CAUSAL with a
@@ -47,6 +48,10 @@
  *      PACKED_U64      per query row ceil(kv_len/64) uint64 words; key j is
  *                      bit (j % 64) of word j / 64; rows concatenated over
  *                      sequences; bits past kv_len are ignored
+ *      BLOCK_SPARSE    block (t / block_r, j / block_c) is listed in the
+ *                      sequence's block-row CSR (below)
+ *    DENSE_BOOL, PACKED_U64 and BLOCK_SPARSE accept window >= 1: the mask is
+ *    then intersected with the sliding-window band pos(t) - window < j <= pos(t).
  *  - Range descriptors are in per-sequence local coordinates (query rows and
  *    keys of that sequence).  Inside a range, i = t - q_start,
  *    jj = j - k_start, Lq = q_end - q_start, Lk = k_end - k_start:
@@ -96,7 +101,8 @@ typedef enum {
   MA_KIND_PREFIX_LM = 2,
   MA_KIND_RANGES = 3,
   MA_KIND_DENSE_BOOL = 4,
-  MA_KIND_PACKED_U64 = 5
+  MA_KIND_PACKED_U64 = 5,
+  MA_KIND_BLOCK_SPARSE = 6
 } ma_mask_kind;
 
 typedef enum { MA_F32 = 0, MA_BF16 = 1 } ma_dtype;
@@ -118,7 +124,8 @@ typedef struct {
   int32_t batch;                /* number of sequences, >= 1 */
   const int32_t *cu_seqlens_q;  /* host [batch+1], nondecreasing, starts at 0 */
   const int32_t *kv_lens;       /* host [batch], kv_len >= q_len of the sequence */
-  int32_t window;               /* SLIDING_WINDOW: >= 1 (other kinds: must be 0) */
+  int32_t window;               /* SLIDING_WINDOW: >= 1; DENSE_BOOL / PACKED_U64 / BLOCK_SPARSE:
+                                   0 or a window >= 1 intersected with the mask; others: 0 */
   const int32_t *prefix_len;    /* PREFIX_LM: host [batch], 0 <= prefix_len <= kv_len */
   const ma_range *ranges;       /* RANGES: host, range_indptr[batch] descriptors */
   const int32_t *range_indptr;  /* RANGES: host [batch+1] CSR offsets into ranges */
@@ -127,6 +134,15 @@ typedef struct {
   int32_t mask_on_device;       /* 1: `mask` is device memory (classified on the GPU, stream-ordered) */
   int32_t tile_q;               /* 64 or 128: query rows per tile */
   int32_t tile_k;               /* 64: keys per tile */
+  /* BLOCK_SPARSE: blocks of block_r query rows x block_c keys.  Sequence b
+   * has nrb_b = ceil(q_len_b / block_r) block rows; the block rows of all
+   * sequences are concatenated (sequence 0 first) into one CSR:
+   * bsr_indptr (host, [sum_b nrb_b + 1], starts at 0, nondecreasing) and
+   * bsr_indices (host, block-column indices local to the sequence, each in
+   * [0, ceil(kv_len_b / block_c)); repeats allowed). */
+  int32_t block_r, block_c;
+  const int32_t *bsr_indptr;
+  const int32_t *bsr_indices;
 } ma_mask_desc;
 
 /* A compiled plan: per (sequence, q-tile, k-tile) FULL/SKIP/PARTIAL, the

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libmaskattn.so")
 MA_OK, MA_ERR_INVALID, MA_ERR_CONFLICT, MA_ERR_SIZE = 0, -1, -2, -3
 MA_ERR_UNSUPPORTED, MA_ERR_PLAN_MISMATCH, MA_ERR_HIP, MA_ERR_NOMEM = -4, -5, -6, -7
 RANGE_FULL, RANGE_CAUSAL, RANGE_INV_CAUSAL, RANGE_BI_CAUSAL, RANGE_CHUNK_CAUSAL = 0, 1, 2, 3, 4
-KIND = {"causal": 0, "window": 1, "prefix_lm": 2, "ranges": 3, "dense": 4, "packed": 5}
+KIND = {"causal": 0, "window": 1, "prefix_lm": 2, "ranges": 3, "dense": 4, "packed": 5, "block_sparse": 6}
 F32, BF16 = 0, 1
 TILE_SKIP, TILE_FULL, TILE_PARTIAL = 0, 1, 2
 
@@ -39,7 +39,9 @@ class MaMaskDesc(ctypes.Structure):
                 ("window", ctypes.c_int32), ("prefix_len", ctypes.c_void_p),
                 ("ranges", ctypes.c_void_p), ("range_indptr", ctypes.c_void_p),
                 ("mask", ctypes.c_void_p), ("mask_numel", ctypes.c_int64),
-                ("mask_on_device", ctypes.c_int32), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32)]
+                ("mask_on_device", ctypes.c_int32), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
+                ("block_r", ctypes.c_int32), ("block_c", ctypes.c_int32),
+                ("bsr_indptr", ctypes.c_void_p), ("bsr_indices", ctypes.c_void_p)]
 
 
 class MaPlanInfo(ctypes.Structure):
@@ -156,8 +158,10 @@ class Plan:
 
 
 def make_desc(kind, cu_seqlens_q, kv_lens, window=0, prefix_len=None, ranges=None, mask=None,
-              tile_q=128, tile_k=64):
-    """Builds the C mask description; returns (desc, arrays to keep alive)."""
+              tile_q=128, tile_k=64, bsr=None):
+    """Builds the C mask description; returns (desc, arrays to keep alive).
+    bsr = (block_r, block_c, indptr, indices) for the block-sparse kind (the
+    block rows of all sequences concatenated, column indices per sequence)."""
     cu = _i32(cu_seqlens_q)
     kv = _i32(kv_lens)
     keep = [cu, kv]
@@ -180,6 +184,13 @@ def make_desc(kind, cu_seqlens_q, kv_lens, window=0, prefix_len=None, ranges=Non
         keep += [indptr, arr]
         d.ranges = ctypes.cast(arr, ctypes.c_void_p)
         d.range_indptr = _ptr(indptr)
+    if bsr is not None:
+        br, bc, indptr, indices = bsr
+        ip, ix = _i32(indptr), _i32(indices)
+        keep += [ip, ix]
+        d.block_r, d.block_c = int(br), int(bc)
+        d.bsr_indptr = _ptr(ip)
+        d.bsr_indices = _ptr(ix) if ix.size else None
     if mask is not None:
         if hasattr(mask, "is_cuda"):
             d.mask = ctypes.c_void_p(mask.data_ptr())

@@ -91,7 +91,7 @@ ma_status mask_compile(const ma_mask_desc *desc, void *stream, ma_plan **out) {
       (desc->kind == MA_KIND_DENSE_BOOL || desc->kind == MA_KIND_PACKED_U64) && desc->mask_on_device;
   if (st == MA_OK) {
     if (device_mask) {
-      st = launch_classify(p, desc->mask, desc->kind, desc->mask_numel, stream);
+      st = launch_classify(p, desc->mask, desc->kind, desc->mask_numel, desc->window, stream);
     } else {
       st = compile_host(desc, p);
       if (st == MA_OK) st = plan_upload(p, stream);

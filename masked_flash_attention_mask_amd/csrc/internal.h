@@ -98,7 +98,7 @@ ma_status plan_build_kmajor(ma_plan *p, void *stream);
 void plan_free_device(ma_plan *p);
 
 // mask_classify.hip
-ma_status launch_classify(ma_plan *p, const void *mask, int32_t kind, int64_t mask_numel,
+ma_status launch_classify(ma_plan *p, const void *mask, int32_t kind, int64_t mask_numel, int32_t window,
                           void *stream);
 
 // attn_fwd.hip

@@ -37,7 +37,20 @@ struct ClassifyParams {
   const void *mask;
   int64_t mask_numel;
   int32_t batch, num_rows, tile_q, packed;
+  int32_t window;   // > 0: the mask is ANDed with the band pos - window < j <= pos
 };
+
+// Bits of k-tile c (keys 64 c .. 64 c + 63) inside the sliding-window band of
+// local query row `row` (all ones without a window).
+__device__ __forceinline__ uint64_t band_bits(int row, int c, int q_len, int kv, int window) {
+  if (window <= 0) return ~0ull;
+  const int64_t pos = (int64_t)row + kv - q_len;
+  const int64_t lo = max((int64_t)0, pos - window + 1 - 64 * (int64_t)c);
+  const int64_t hi = min((int64_t)64, pos + 1 - 64 * (int64_t)c);
+  if (hi <= lo) return 0ull;
+  const uint64_t upper = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
+  return upper & ~((1ull << lo) - 1ull);
+}
 
 // Bits (LSB = lowest address) of the nonzero bytes of a dword: per byte the
 // high bit is set iff the byte is nonzero (SWAR), then one multiply moves the
@@ -107,7 +120,8 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p) {
         }
         if (lane < cn) {
 #pragma unroll
-          for (int i = 0; i < 32; ++i) wl[lane * ws + rg * 32 + i] = w[i] & inb;
+          for (int i = 0; i < 32; ++i)
+            wl[lane * ws + rg * 32 + i] = w[i] & inb & band_bits(row0 + i, c, sq.q_len, kv, p.window);
         }
       } else {
         const int i = lane >> 1, half = lane & 1;
@@ -155,7 +169,9 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p) {
           for (int u = 0; u < kDenseBatch; ++u) {
             const int src = 2 * (lane & 31);
             const uint32_t lo = __shfl(bits[u], src, 64), hi = __shfl(bits[u], src + 1, 64);
-            if (lane < 32 && ci0 + u < cn) wl[(ci0 + u) * ws + rg * 32 + lane] = ((uint64_t)hi << 32) | lo;
+            if (lane < 32 && ci0 + u < cn)
+              wl[(ci0 + u) * ws + rg * 32 + lane] =
+                  (((uint64_t)hi << 32) | lo) & band_bits(row0 + lane, c0 + ci0 + u, sq.q_len, kv, p.window);
           }
         }
       }
@@ -210,7 +226,8 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p) {
 
 }  // namespace
 
-ma_status launch_classify(ma_plan *p, const void *mask, int32_t kind, int64_t mask_numel, void *stream) {
+ma_status launch_classify(ma_plan *p, const void *mask, int32_t kind, int64_t mask_numel, int32_t window,
+                          void *stream) {
   if (p->num_tiles > INT32_MAX) return set_error(MA_ERR_UNSUPPORTED, "too many tiles for a device-built plan");
   ma_status st = plan_alloc_device(p, p->num_tiles, p->num_tiles);
   if (st != MA_OK) return st;
@@ -241,6 +258,7 @@ ma_status launch_classify(ma_plan *p, const void *mask, int32_t kind, int64_t ma
   prm.num_rows = p->num_rows;
   prm.tile_q = p->tile_q;
   prm.packed = kind == MA_KIND_PACKED_U64 ? 1 : 0;
+  prm.window = window;
   const size_t lds = (size_t)kTiles * (p->tile_q + 1) * sizeof(uint64_t);
   e = hipSuccess;
   if (lds > 64 * 1024)

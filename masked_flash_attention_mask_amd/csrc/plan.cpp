@@ -71,10 +71,67 @@ struct RowIntervals {
   std::vector<Iv> iv;
 };
 
+// Intersects every row's intervals with the sliding-window band
+// pos - window < j <= pos (a window given with a BLOCK_SPARSE mask).
+void clip_to_window(RowIntervals &R, int32_t q_len, int32_t kv_len, int32_t window) {
+  const int64_t delta = (int64_t)kv_len - q_len;
+  std::vector<Iv> iv;
+  std::vector<int32_t> ptr(q_len + 1, 0);
+  iv.reserve(R.iv.size());
+  for (int32_t t = 0; t < q_len; ++t) {
+    const int64_t pos = t + delta;
+    const int64_t lo = pos - window + 1, hi = pos + 1;
+    for (int32_t k = R.ptr[t]; k < R.ptr[t + 1]; ++k) {
+      const int64_t a = std::max<int64_t>(lo, R.iv[k].lo), z = std::min<int64_t>(hi, R.iv[k].hi);
+      if (z > a) iv.push_back(Iv{(int32_t)a, (int32_t)z});
+    }
+    ptr[t + 1] = (int32_t)iv.size();
+  }
+  R.iv.swap(iv);
+  R.ptr.swap(ptr);
+}
+
+// First block row of sequence b in the concatenated block-row CSR.
+int64_t bsr_row_base(const ma_mask_desc *d, int b) {
+  int64_t base = 0;
+  for (int s = 0; s < b; ++s)
+    base += ceil_div((int64_t)d->cu_seqlens_q[s + 1] - d->cu_seqlens_q[s], d->block_r);
+  return base;
+}
+
 void build_rows(const ma_mask_desc *d, int b, int32_t q_len, int32_t kv_len, RowIntervals &out) {
   out.ptr.assign(q_len + 1, 0);
   out.iv.clear();
   const int64_t delta = (int64_t)kv_len - q_len;
+  if (d->kind == MA_KIND_BLOCK_SPARSE) {
+    // Row t sees the listed blocks of its block row; adjacent or repeated
+    // blocks merge.  One sorted column list per block row.
+    const int64_t rb0 = bsr_row_base(d, b);
+    const int32_t nrb = (int32_t)ceil_div(q_len, d->block_r);
+    std::vector<Iv> blocks;
+    for (int32_t rb = 0; rb < nrb; ++rb) {
+      const int32_t k0 = d->bsr_indptr[rb0 + rb], k1 = d->bsr_indptr[rb0 + rb + 1];
+      std::vector<int32_t> cols(d->bsr_indices + k0, d->bsr_indices + k1);
+      std::sort(cols.begin(), cols.end());
+      blocks.clear();
+      for (int32_t c : cols) {
+        const int32_t lo = (int32_t)std::min<int64_t>(kv_len, (int64_t)c * d->block_c);
+        const int32_t hi = (int32_t)std::min<int64_t>(kv_len, (int64_t)(c + 1) * d->block_c);
+        if (hi <= lo) continue;
+        if (!blocks.empty() && blocks.back().hi >= lo)
+          blocks.back().hi = std::max(blocks.back().hi, hi);
+        else
+          blocks.push_back(Iv{lo, hi});
+      }
+      const int32_t t1 = std::min<int32_t>(q_len, (rb + 1) * d->block_r);
+      for (int32_t t = rb * d->block_r; t < t1; ++t) {
+        out.iv.insert(out.iv.end(), blocks.begin(), blocks.end());
+        out.ptr[t + 1] = (int32_t)out.iv.size();
+      }
+    }
+    if (d->window > 0) clip_to_window(out, q_len, kv_len, d->window);
+    return;
+  }
   if (d->kind == MA_KIND_CAUSAL || d->kind == MA_KIND_SLIDING_WINDOW ||
       d->kind == MA_KIND_PREFIX_LM) {
     out.iv.reserve(q_len);
@@ -186,11 +243,13 @@ void classify_qtile_intervals(const RowIntervals &R, int32_t r0, int32_t r1, int
   }
 }
 
-// Classify one q-tile row of a host-resident dense / packed mask.
+// Classify one q-tile row of a host-resident dense / packed mask (ANDed with
+// the sliding-window band when a window is given).
 void classify_qtile_matrix(const ma_mask_desc *d, int64_t moff, int32_t r0, int32_t r1,
-                           int32_t kv_len, int32_t tile_q, int32_t nkt, RowPlan &rp) {
+                           int32_t q_len, int32_t kv_len, int32_t tile_q, int32_t nkt, RowPlan &rp) {
   const int32_t BK = 64;
   const int64_t nw = ceil_div(kv_len, 64);
+  const int64_t delta = (int64_t)kv_len - q_len;
   std::vector<uint64_t> tw(tile_q);
   for (int32_t c = 0; c < nkt; ++c) {
     const int32_t keys = std::min<int32_t>(BK, kv_len - c * BK);
@@ -205,6 +264,12 @@ void classify_qtile_matrix(const ma_mask_desc *d, int64_t moff, int32_t r0, int3
         for (int32_t x = 0; x < keys; ++x) w |= (uint64_t)(row[x] != 0) << x;
       }
       w &= inb;
+      if (d->window > 0) {
+        const int64_t pos = t + delta;
+        const int64_t lo = std::max<int64_t>(0, pos - d->window + 1 - (int64_t)c * BK);
+        const int64_t hi = std::min<int64_t>(64, pos + 1 - (int64_t)c * BK);
+        w &= hi > lo ? bits_between((int32_t)lo, (int32_t)hi) : 0ull;
+      }
       tw[t - r0] = w;
       all_full &= (w == inb);
       all_zero &= (w == 0);
@@ -256,14 +321,20 @@ ma_status validate_desc(const ma_mask_desc *d) {
       return set_error(MA_ERR_UNSUPPORTED, "kv_lens[%d] too large", b);
   }
   const int kind = d->kind;
-  if (kind < MA_KIND_CAUSAL || kind > MA_KIND_PACKED_U64)
+  if (kind < MA_KIND_CAUSAL || kind > MA_KIND_BLOCK_SPARSE)
     return set_error(MA_ERR_INVALID, "unknown mask kind %d", kind);
-  // A sliding window is a restriction of causal masking (sglang-jax review):
-  // any other kind with a window is a conflict, as is a custom mask or range
-  // list supplied to a closed-form kind.
-  if (kind != MA_KIND_SLIDING_WINDOW && d->window != 0)
-    return set_error(MA_ERR_CONFLICT, "window is only valid with the sliding-window (causal) kind");
+  // A sliding window is a restriction of causal masking (sglang-jax review);
+  // with a custom or block-sparse mask it is an intersection (the joint use
+  // asked about in flashinfer issue 724).  With PrefixLM or a range list it
+  // is a conflict, as is a custom mask or range list supplied to a
+  // closed-form kind.
   const bool custom = kind == MA_KIND_DENSE_BOOL || kind == MA_KIND_PACKED_U64;
+  const bool window_ok = kind == MA_KIND_SLIDING_WINDOW || custom || kind == MA_KIND_BLOCK_SPARSE;
+  if (!window_ok && d->window != 0)
+    return set_error(MA_ERR_CONFLICT, "window is only valid with sliding-window, custom or block-sparse kinds");
+  if (d->window < 0) return set_error(MA_ERR_INVALID, "window must be >= 0 (got %d)", d->window);
+  if (kind != MA_KIND_BLOCK_SPARSE && (d->bsr_indptr || d->bsr_indices))
+    return set_error(MA_ERR_CONFLICT, "block-sparse arrays were given with another kind");
   if (!custom && d->mask)
     return set_error(MA_ERR_CONFLICT, "a custom mask buffer was given with a non-custom kind");
   if (kind != MA_KIND_RANGES && (d->ranges || d->range_indptr))
@@ -301,6 +372,27 @@ ma_status validate_desc(const ma_mask_desc *d) {
         if (r.type == MA_RANGE_CHUNK_CAUSAL && r.chunk_size < 1)
           return set_error(MA_ERR_INVALID, "chunk_size must be >= 1 (range %d of sequence %d)",
                            k - d->range_indptr[b], b);
+      }
+    }
+  }
+  if (kind == MA_KIND_BLOCK_SPARSE) {
+    if (d->block_r < 1 || d->block_c < 1)
+      return set_error(MA_ERR_INVALID, "block_r and block_c must be >= 1 (got %d, %d)", d->block_r, d->block_c);
+    if (!d->bsr_indptr) return set_error(MA_ERR_INVALID, "bsr_indptr is required for block-sparse masks");
+    if (d->bsr_indptr[0] != 0) return set_error(MA_ERR_INVALID, "bsr_indptr[0] must be 0");
+    int64_t rb = 0;
+    for (int b = 0; b < d->batch; ++b) {
+      const int64_t ql = d->cu_seqlens_q[b + 1] - d->cu_seqlens_q[b];
+      const int64_t ncb = ceil_div(d->kv_lens[b], d->block_c);
+      for (int64_t r = 0; r < ceil_div(ql, d->block_r); ++r, ++rb) {
+        if (d->bsr_indptr[rb + 1] < d->bsr_indptr[rb])
+          return set_error(MA_ERR_INVALID, "bsr_indptr decreases at block row %lld", (long long)rb);
+        if (d->bsr_indptr[rb + 1] > d->bsr_indptr[rb] && !d->bsr_indices)
+          return set_error(MA_ERR_INVALID, "bsr_indices is NULL");
+        for (int32_t k = d->bsr_indptr[rb]; k < d->bsr_indptr[rb + 1]; ++k)
+          if (d->bsr_indices[k] < 0 || d->bsr_indices[k] >= ncb)
+            return set_error(MA_ERR_INVALID, "block column %d of block row %lld (sequence %d) outside [0, %lld)",
+                             d->bsr_indices[k], (long long)r, b, (long long)ncb);
       }
     }
   }
@@ -363,7 +455,7 @@ ma_status compile_host(const ma_mask_desc *d, ma_plan *p) {
       const int32_t r0 = a * p->tile_q, r1 = std::min(ql, r0 + p->tile_q);
       RowPlan &rp = rps[p->row_base[b] + a];
       if (matrix)
-        classify_qtile_matrix(d, moff, r0, r1, kl, p->tile_q, p->nkt[b], rp);
+        classify_qtile_matrix(d, moff, r0, r1, ql, kl, p->tile_q, p->nkt[b], rp);
       else
         classify_qtile_intervals(R, r0, r1, kl, p->tile_q, p->nkt[b], cnt, diff, rp);
     }

@@ -25,6 +25,12 @@ Readings taken where the pages are silent (each is listed in the design notes):
     causal mask and that W >= the sequence length changes nothing.  Parity
     unpinned beyond that.
   * Overlapping range descriptors are OR-ed.
+  * Block-sparse masks ([flashinfer#724] recommends its block-sparse API for
+    long sequences; the page gives no layout): blocks of block_r rows x
+    block_c keys listed per block row in CSR form; a key is visible when its
+    block is listed.  The last block row / column is cut at q_len / kv_len.
+  * A sliding window given with a custom or block-sparse mask is ANDed with
+    it (the joint use [flashinfer#724] asks about), using the band above.
 """
 
 import numpy as np
@@ -179,3 +185,27 @@ def packed_from_flat(flat, q_lens, kv_lens):
         out.append(unpack_rows(flat[off:off + n], int(ql), int(kl)))
         off += n
     return out
+
+
+def block_sparse(q_len, kv_len, block_r, block_c, indptr, indices):
+    """Block-sparse mask of one sequence: indptr [ceil(q_len / block_r) + 1]
+    and indices (block columns) in CSR form over block rows; row t sees key
+    j when block (t // block_r, j // block_c) is listed.  Written out entry
+    by block entry, no blocking beyond the definition."""
+    m = np.zeros((q_len, kv_len), dtype=bool)
+    nrb = -(-q_len // block_r)
+    for rb in range(nrb):
+        r0, r1 = rb * block_r, min(q_len, (rb + 1) * block_r)
+        for k in range(int(indptr[rb]), int(indptr[rb + 1])):
+            c = int(indices[k])
+            m[r0:r1, c * block_c:min(kv_len, (c + 1) * block_c)] = True
+    return m
+
+
+def window_band(q_len, kv_len, window):
+    """The sliding-window band alone: pos - window < j <= pos (the set that a
+    window intersects a custom or block-sparse mask with)."""
+    if window < 1:
+        raise ValueError("window must be >= 1")
+    pos, j = _grid(q_len, kv_len)
+    return (j > pos - window) & (j <= pos)

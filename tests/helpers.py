@@ -43,12 +43,22 @@ def oracle_masks(w, mask_name):
         return lambda b: OM.prefix_lm(int(ql[b]), int(kl[b]), int(mi.prefix_len[b]))
     if mi.kind == "ranges":
         return lambda b: OM.ranges(int(ql[b]), int(kl[b]), mi.ranges[b])
+    band = (lambda b: OM.window_band(int(ql[b]), int(kl[b]), mi.window)) if mi.window else None
     if mi.kind == "dense":
         lst = OM.dense_from_flat(mi.data, ql, kl)
-        return lambda b: lst[b]
+        return (lambda b: lst[b] & band(b)) if band else (lambda b: lst[b])
     if mi.kind == "packed":
         lst = OM.packed_from_flat(mi.data, ql, kl)
-        return lambda b: lst[b]
+        return (lambda b: lst[b] & band(b)) if band else (lambda b: lst[b])
+    if mi.kind == "block_sparse":
+        br, bc, indptr, indices = mi.bsr
+        starts = np.concatenate([[0], np.cumsum([-(-int(q) // br) for q in ql])])
+
+        def bsr(b):
+            ip = indptr[starts[b]:starts[b + 1] + 1]
+            m = OM.block_sparse(int(ql[b]), int(kl[b]), br, bc, ip, indices)
+            return m & band(b) if band else m
+        return bsr
     raise ValueError(mi.kind)
 
 

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 import masked_flash_attention_mask_amd as ma
+import masked_flash_attention_mask_amd._lib as L
 import workloads as W
 from oracle import masks as M
 from oracle import tiles as T
@@ -137,3 +138,81 @@ def test_execution_order_most_work_first():
     assert data[4 + 1] == 7
     info = p.info()
     assert info.num_qtiles == 8 and info.num_tiles == 8 * 16 and info.host_valid == 1
+
+
+def _bsr_arrays(rng, q_lens, kv_lens, br, bc, p):
+    indptr, indices, dense = [0], [], []
+    for q, k in zip(q_lens, kv_lens):
+        nrb, ncb = -(-q // br), -(-k // bc)
+        blocks = rng.random((nrb, ncb)) < p
+        blocks[0, :] = True if ncb else blocks[0, :]   # a dense block row (FULL tiles)
+        for rb in range(nrb):
+            cols = list(np.flatnonzero(blocks[rb]))
+            rng.shuffle(cols)
+            indices += cols
+            indptr.append(len(indices))
+        dense.append(np.kron(blocks, np.ones((br, bc), dtype=bool))[:q, :k])
+    return np.array(indptr), np.array(indices), dense
+
+
+@pytest.mark.parametrize("br,bc", [(16, 32), (64, 64), (128, 64), (7, 100), (1, 1)])
+def test_block_sparse_host(br, bc):
+    """Block-sparse descriptions compile to the oracle's classes and words,
+    and to the same plan bytes as the equal dense mask."""
+    rng = np.random.default_rng(br * 131 + bc)
+    q_lens, kv_lens = [300, 5, 130], [900, 70, 130]
+    indptr, indices, dense = _bsr_arrays(rng, q_lens, kv_lens, br, bc, 0.3)
+    flat = np.concatenate([d.astype(np.uint8).reshape(-1) for d in dense])
+    for tq in (64, 128):
+        pb = ma.mask_compile_host("block_sparse", _cu(q_lens), kv_lens, bsr=(br, bc, indptr, indices), tile_q=tq)
+        _check(pb, dense, tq)
+        pd = ma.mask_compile_host("dense", _cu(q_lens), kv_lens, mask=flat, tile_q=tq)
+        assert pb.serialize() == pd.serialize()
+
+
+def test_window_intersections_host():
+    """A window with a custom (dense / packed) or block-sparse mask is the
+    intersection with the window band: same plan bytes as the intersected
+    dense mask, and the oracle's classes and words."""
+    rng = np.random.default_rng(77)
+    q_lens, kv_lens = [300, 5, 130], [900, 70, 130]
+    indptr, indices, bdense = _bsr_arrays(rng, q_lens, kv_lens, 32, 64, 0.5)
+    custom = [rng.random((q, k)) < 0.6 for q, k in zip(q_lens, kv_lens)]
+    flat = np.concatenate([d.astype(np.uint8).reshape(-1) for d in custom])
+    packed = np.concatenate([W.pack_rows(d).reshape(-1) for d in custom])
+    for win in (1, 37, 200, 5000):
+        band = [M.window_band(q, k, win) for q, k in zip(q_lens, kv_lens)]
+        want_c = [c & b for c, b in zip(custom, band)]
+        want_b = [c & b for c, b in zip(bdense, band)]
+        ref_c = ma.mask_compile_host("dense", _cu(q_lens), kv_lens,
+                                     mask=np.concatenate([d.astype(np.uint8).reshape(-1) for d in want_c]))
+        for kind, mk in (("dense", flat), ("packed", packed)):
+            p = ma.mask_compile_host(kind, _cu(q_lens), kv_lens, mask=mk, window=win)
+            _check(p, want_c, 128)
+            assert p.serialize() == ref_c.serialize()
+        pb = ma.mask_compile_host("block_sparse", _cu(q_lens), kv_lens, bsr=(32, 64, indptr, indices), window=win)
+        _check(pb, want_b, 128)
+
+
+def test_block_sparse_and_window_validation():
+    cu, kv = [0, 10], [20]
+    ok = (4, 8, [0, 1, 1, 2], [0, 2])
+    ma.mask_compile_host("block_sparse", cu, kv, bsr=ok)
+    bad = [
+        ((0, 8, [0, 1, 1, 2], [0, 2]), ma.MaskAttnError),      # block_r 0
+        ((4, 8, [0, 2, 1, 2], [0, 2]), ma.MaskAttnError),      # indptr decreases
+        ((4, 8, [0, 1, 1, 2], [0, 3]), ma.MaskAttnError),      # column 3 >= ceil(20 / 8)
+        ((4, 8, [1, 1, 1, 2], [0, 2]), ma.MaskAttnError),      # indptr[0] != 0
+    ]
+    for bsr, exc in bad:
+        with pytest.raises(exc):
+            ma.mask_compile_host("block_sparse", cu, kv, bsr=bsr)
+    with pytest.raises(ma.MaskAttnError) as e:                 # block-sparse arrays with another kind
+        ma.mask_compile_host("causal", cu, kv, bsr=ok)
+    assert e.value.status == L.MA_ERR_CONFLICT
+    for kind, kw in (("prefix_lm", {"prefix_len": [3]}), ("ranges", {"ranges": [[(0, 10, 0, 20, 0, 0)]]}),
+                     ("causal", {})):
+        with pytest.raises(ma.MaskAttnError):
+            ma.mask_compile_host(kind, cu, kv, window=4, **kw)
+    with pytest.raises(ma.MaskAttnError):
+        ma.mask_compile_host("dense", cu, kv, mask=np.ones(200, np.uint8), window=-1)

@@ -217,3 +217,57 @@ def test_flat_layouts():
     a, b = M.packed_from_flat(words, [2, 1], [3, 2])
     assert np.array_equal(a, np.array([[1, 0, 1], [1, 1, 0]], bool))
     assert np.array_equal(b, np.array([[0, 1]], bool))
+
+
+# --------------------------------------------------------------------------
+# Block-sparse masks and the window band
+
+
+def _random_bsr(rng, q_len, kv_len, br, bc, p=0.4, repeat=True):
+    nrb, ncb = -(-q_len // br), -(-kv_len // bc)
+    blocks = rng.random((nrb, ncb)) < p
+    indptr, indices = [0], []
+    for rb in range(nrb):
+        cols = list(np.flatnonzero(blocks[rb]))
+        if repeat and cols:
+            cols.append(cols[0])                 # a repeated block is the same block
+        rng.shuffle(cols)
+        indices += cols
+        indptr.append(len(indices))
+    return blocks, np.array(indptr), np.array(indices, dtype=np.int64)
+
+
+@pytest.mark.parametrize("q_len,kv_len,br,bc", [(37, 53, 8, 16), (64, 64, 64, 64), (5, 130, 3, 7), (1, 1, 1, 1)])
+def test_block_sparse_is_kron_of_blocks(q_len, kv_len, br, bc):
+    """Library routine: the mask is the block matrix expanded by np.kron with
+    a block of ones, cut to [q_len, kv_len]."""
+    rng = np.random.default_rng(q_len * 1000 + kv_len)
+    blocks, indptr, indices = _random_bsr(rng, q_len, kv_len, br, bc)
+    want = np.kron(blocks, np.ones((br, bc), dtype=bool))[:q_len, :kv_len]
+    assert np.array_equal(M.block_sparse(q_len, kv_len, br, bc, indptr, indices), want)
+
+
+def test_block_sparse_special_cases():
+    rng = np.random.default_rng(3)
+    q_len, kv_len = 23, 41
+    # 1 x 1 blocks list exactly the visible entries: any dense mask round-trips
+    dense = rng.random((q_len, kv_len)) < 0.3
+    indptr = np.concatenate([[0], np.cumsum(dense.sum(1))])
+    indices = np.concatenate([np.flatnonzero(r) for r in dense])
+    assert np.array_equal(M.block_sparse(q_len, kv_len, 1, 1, indptr, indices), dense)
+    # every block listed: all true; none: all false
+    nrb, ncb = -(-q_len // 5), -(-kv_len // 6)
+    full = M.block_sparse(q_len, kv_len, 5, 6, np.arange(nrb + 1) * ncb, np.tile(np.arange(ncb), nrb))
+    assert full.all()
+    assert not M.block_sparse(q_len, kv_len, 5, 6, np.zeros(nrb + 1, int), np.zeros(0, int)).any()
+
+
+def test_window_band():
+    """The band alone is the sliding-window kind's set; a window at least as
+    long as the keys leaves the causal mask; window 1 is the diagonal."""
+    for q_len, kv_len in [(30, 30), (7, 50)]:
+        for w in (1, 5, 29, 60):
+            assert np.array_equal(M.window_band(q_len, kv_len, w), M.sliding_window(q_len, kv_len, w))
+        assert np.array_equal(M.window_band(q_len, kv_len, kv_len), M.causal(q_len, kv_len))
+        band = M.window_band(q_len, kv_len, 1)
+        assert (band.sum(1) == 1).all() and (np.argmax(band, 1) == M.positions(q_len, kv_len)).all()

@@ -28,7 +28,13 @@ def plan_kwargs(w, mask_name, host=False):
         kw["prefix_len"] = mi.prefix_len
     elif mi.kind == "ranges":
         kw["ranges"] = mi.ranges
+    elif mi.kind == "block_sparse":
+        kw["bsr"] = mi.bsr
+        if mi.window:
+            kw["window"] = mi.window
     elif mi.kind in ("dense", "packed"):
+        if mi.window:
+            kw["window"] = mi.window
         if host:
             kw["mask"] = mi.data
         else:

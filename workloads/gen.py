@@ -31,13 +31,17 @@ R_FULL, R_CAUSAL, R_INV_CAUSAL, R_BI_CAUSAL, R_CHUNK_CAUSAL = 0, 1, 2, 3, 4
 class MaskInput:
     """One mask as handed to the library.
 
-    kind: 'causal' | 'window' | 'prefix_lm' | 'ranges' | 'dense' | 'packed'
+    kind: 'causal' | 'window' | 'prefix_lm' | 'ranges' | 'dense' | 'packed' |
+          'block_sparse'
+    window: the window of 'window', or one ANDed with 'dense' / 'packed' /
+            'block_sparse' (0: none)
     """
     kind: str
     window: int = 0
     prefix_len: np.ndarray = None          # int32 [B]
     ranges: list = None                    # per sequence: list of 6-tuples
     data: np.ndarray = None                # dense uint8 flat / packed uint64 flat
+    bsr: tuple = None                      # (block_r, block_c, indptr, indices), block rows of all sequences
 
 
 @dataclass
@@ -365,4 +369,47 @@ def backward_small(seed=7, d=128, hq=4, hkv=2, q_lens=(300, 5, 130, 64, 1, 200),
     w.masks["ranges"] = MaskInput("ranges", ranges=ranges)
     w.masks["dense"] = MaskInput("dense", data=np.concatenate([m.astype(np.uint8).reshape(-1) for m in dense]))
     w.masks["packed"] = MaskInput("packed", data=np.concatenate([pack_rows(m).reshape(-1) for m in dense]))
+    return w
+
+
+# ---------------------------------------------------------- more mask inputs --
+def block_sparse_csr(rng, q_lens, kv_lens, block_r, block_c, p):
+    """Bernoulli(p) block structure per sequence (the first block row forced
+    full), as one CSR over the block rows of all sequences (columns local to
+    each sequence, in shuffled order).  Returns (indptr, indices)."""
+    indptr, indices = [0], []
+    for q, k in zip(q_lens, kv_lens):
+        nrb, ncb = -(-int(q) // block_r), -(-int(k) // block_c)
+        blocks = rng.random((nrb, ncb)) < p
+        blocks[0, :] = True
+        for rb in range(nrb):
+            cols = list(np.flatnonzero(blocks[rb]))
+            rng.shuffle(cols)
+            indices += cols
+            indptr.append(len(indices))
+    return np.array(indptr, dtype=np.int32), np.array(indices, dtype=np.int32)
+
+
+def mask_inputs(seed=9, d=128, hq=8, hkv=2, q_lens=(300, 5, 130, 700, 1), kv_lens=(900, 70, 130, 2000, 64)):
+    """Ragged batch (bf16, GQA, random page order) for the block-sparse and
+    window-intersected mask inputs: block-sparse masks at block sizes 64 x 64,
+    128 x 128 and 16 x 48 (Bernoulli(0.35) blocks), the 64 x 64 one also with
+    a 300-key window, and a Bernoulli(0.5) custom mask with a 111-key window
+    (dense bytes and packed words) and without."""
+    rng = rng_for(seed)
+    q_lens, kv_lens = list(q_lens), list(kv_lens)
+    bs = {}
+    for br, bc in ((64, 64), (128, 128), (16, 48)):
+        bs[(br, bc)] = block_sparse_csr(rng, q_lens, kv_lens, br, bc, 0.35)
+    custom = [rng.random((q, k)) < 0.5 for q, k in zip(q_lens, kv_lens)]
+    w = _build(f"maskin{seed}", rng, "bf16", q_lens, kv_lens, hq, hkv, d, permute=True)
+    for (br, bc), (ip, ix) in bs.items():
+        w.masks[f"bsr{br}x{bc}"] = MaskInput("block_sparse", bsr=(br, bc, ip, ix))
+    ip, ix = bs[(64, 64)]
+    w.masks["bsr64x64_window"] = MaskInput("block_sparse", bsr=(64, 64, ip, ix), window=300)
+    flat = np.concatenate([m.astype(np.uint8).reshape(-1) for m in custom])
+    packed = np.concatenate([pack_rows(m).reshape(-1) for m in custom])
+    w.masks["dense"] = MaskInput("dense", data=flat)
+    w.masks["dense_window"] = MaskInput("dense", data=flat, window=111)
+    w.masks["packed_window"] = MaskInput("packed", data=packed, window=111)
     return w
