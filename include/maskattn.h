@@ -218,6 +218,26 @@ ma_status attn_prefill_masked(const ma_plan *plan, const void *q, int64_t total_
                               const int32_t *page_table, int32_t max_pages, int32_t in_dtype,
                               int32_t out_dtype, float scale, void *out, float *lse, void *stream);
 
+/* Masked prefill with fp8 inputs (OCP e4m3: 1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, subnormals, no infinities, 0x7F / 0xFF NaN;
+ * largest 448) — the fp8 path asked about in flashinfer issue 724 (closing
+ * questions).  q, k_cache, v_cache hold e4m3 bytes in the layouts of
+ * attn_prefill_masked (strides in elements = bytes).  Per-tensor descale
+ * factors: the attention is softmax(scale * q_descale * k_descale * Q8 K8^T
+ * + mask) (v_descale * V8), Q8 / K8 / V8 the decoded bytes.
+ *  out_dtype BF16 or F32; d in {64, 128}; plans with tile 128 x 64; page
+ *  size at least 1024 / d keys (one gather instruction's rows in one page).
+ * Arithmetic: both products on fp8 matrix cores with fp32 accumulation; the
+ * probabilities are rounded to e4m3 (round to nearest even) for P V and the
+ * row sums add those rounded values.  Deterministic; stream-ordered.
+ * Errors as attn_prefill_masked, plus INVALID for descale factors that are
+ * not positive and finite, UNSUPPORTED for small pages. */
+ma_status attn_prefill_masked_fp8(const ma_plan *plan, const void *q, int64_t total_q, int32_t hq,
+                                  const void *k_cache, const void *v_cache, int32_t hkv, int32_t d,
+                                  int32_t page_size, const int64_t kv_strides[3], const int32_t *page_table,
+                                  int32_t max_pages, float q_descale, float k_descale, float v_descale,
+                                  int32_t out_dtype, float scale, void *out, float *lse, void *stream);
+
 /* Workspace bytes attn_backward_masked needs for this plan and Hq (two fp32
  * values per (query, head)); 0 for a NULL plan or hq < 1. */
 size_t attn_backward_workspace(const ma_plan *plan, int32_t hq);

@@ -23,7 +23,7 @@ TILE_SKIP, TILE_FULL, TILE_PARTIAL = 0, 1, 2
 
 EXPORTS = ["mask_compile", "mask_compile_host", "mask_plan_upload", "mask_plan_destroy",
            "mask_plan_info_get", "mask_plan_export", "mask_plan_serialize", "attn_prefill_masked",
-           "attn_backward_workspace", "attn_backward_masked", "attn_verify_tree_workspace", "attn_verify_tree",
+           "attn_prefill_masked_fp8", "attn_backward_workspace", "attn_backward_masked", "attn_verify_tree_workspace", "attn_verify_tree",
            "attn_decode_workspace", "attn_decode",
            "ma_status_string", "ma_last_error"]
 
@@ -72,6 +72,8 @@ def _load():
         "mask_plan_serialize": (i32, [vp, vp, ctypes.POINTER(sz)]),
         "attn_prefill_masked": (i32, [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, i32, i32, f32,
                                       vp, vp, vp]),
+        "attn_prefill_masked_fp8": (i32, [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, f32, f32, f32, i32,
+                                          f32, vp, vp, vp]),
         "attn_backward_workspace": (sz, [vp, i32]),
         "attn_backward_masked": (i32, [vp, vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, vp, i32, vp, vp, f32,
                                        vp, vp, vp, vp, sz, vp]),
@@ -258,6 +260,34 @@ def attn_prefill_masked(plan, q, k_cache, v_cache, page_table, scale, out=None, 
         strides, page_table.data_ptr(), page_table.shape[1], _dtype_code(q.dtype), _dtype_code(out.dtype),
         float(scale), out.data_ptr(), lse.data_ptr() if lse is not False else None, _stream(stream))
     check(st, "attn_prefill_masked")
+    return out, lse
+
+
+def attn_prefill_masked_fp8(plan, q8, k8, v8, page_table, scale, q_descale, k_descale, v_descale, out=None,
+                            lse=None, out_dtype=None, stream=None):
+    """fp8 (e4m3) prefill: q8 [total_q, Hq, d], k8 / v8 [pages, page_size, Hkv, d]
+    as uint8 (or float8_e4m3fn) device tensors; per-tensor descale factors.
+    Returns (out, lse); out is bf16 unless out_dtype says otherwise."""
+    import torch
+    if not q8.is_contiguous() or not page_table.is_contiguous() or page_table.dtype != torch.int32:
+        raise ValueError("q must be contiguous and page_table a contiguous int32 tensor")
+    for t in (q8, k8, v8):
+        if t.element_size() != 1:
+            raise ValueError("fp8 inputs must be one-byte tensors")
+    total_q, hq, d = q8.shape
+    hkv, page_size = k8.shape[2], k8.shape[1]
+    strides = _cache_args(k8, v8)
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((total_q, hq, d), dtype=out_dtype, device=q8.device)
+    if lse is None:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=q8.device)
+    st = LIB.attn_prefill_masked_fp8(
+        plan.handle, q8.data_ptr(), total_q, hq, k8.data_ptr(), v8.data_ptr(), hkv, d, page_size, strides,
+        page_table.data_ptr(), page_table.shape[1], float(q_descale), float(k_descale), float(v_descale),
+        _dtype_code(out.dtype), float(scale), out.data_ptr(), lse.data_ptr() if lse is not False else None,
+        _stream(stream))
+    check(st, "attn_prefill_masked_fp8")
     return out, lse
 
 

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmaskattn.so")
-SOURCES = ["abi.cpp", "plan.cpp", "attn_fwd.hip", "mask_classify.hip", "verify.hip", "attn_bwd.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "attn_fwd.hip", "mask_classify.hip", "verify.hip", "attn_bwd.hip", "attn_fp8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are disabled on purpose: plain scalar fp32 code
@@ -25,7 +25,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I" + os.path.
 # copies than the default AGPR form (no spills at d = 256, -12% on the d = 256
 # prefill, -3.5% on the backward; d <= 128 prefill unchanged).
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-SOURCE_FLAGS = {"attn_bwd.hip": _VGPR_FORM, "attn_fwd.hip": _VGPR_FORM, "verify.hip": _VGPR_FORM}
+SOURCE_FLAGS = {"attn_bwd.hip": _VGPR_FORM, "attn_fwd.hip": _VGPR_FORM, "verify.hip": _VGPR_FORM,
+                "attn_fp8.hip": _VGPR_FORM}
 
 
 def _compile(src):

@@ -264,6 +264,66 @@ ma_status attn_prefill_masked(const ma_plan *plan, const void *q, int64_t total_
   return launch_prefill(a);
 }
 
+ma_status attn_prefill_masked_fp8(const ma_plan *plan, const void *q, int64_t total_q, int32_t hq,
+                                  const void *k_cache, const void *v_cache, int32_t hkv, int32_t d,
+                                  int32_t page_size, const int64_t kv_strides[3], const int32_t *page_table,
+                                  int32_t max_pages, float q_descale, float k_descale, float v_descale,
+                                  int32_t out_dtype, float scale, void *out, float *lse, void *stream) {
+  clear_error();
+  if (!plan) return set_error(MA_ERR_INVALID, "plan is NULL");
+  ma_status st = check_paged(q, k_cache, v_cache, out, page_table, hq, hkv, page_size, kv_strides,
+                             max_pages, scale);
+  if (st != MA_OK) return st;
+  for (float f : {q_descale, k_descale, v_descale})
+    if (!std::isfinite(f) || !(f > 0.f)) return set_error(MA_ERR_INVALID, "descale factors must be positive and finite");
+  if (total_q != plan->total_q)
+    return set_error(MA_ERR_PLAN_MISMATCH, "total_q %lld differs from the plan's %lld",
+                     (long long)total_q, (long long)plan->total_q);
+  if (plan->tile_k != 64 || plan->tile_q != 128)
+    return set_error(MA_ERR_PLAN_MISMATCH, "fp8 prefill needs a 128 x 64 tile plan (got %d x %d)", plan->tile_q,
+                     plan->tile_k);
+  for (int b = 0; b < plan->batch; ++b)
+    if ((int64_t)max_pages * page_size < plan->kv_len[b])
+      return set_error(MA_ERR_INVALID, "page table (max_pages %d x page_size %d) shorter than kv_len %d",
+                       max_pages, page_size, plan->kv_len[b]);
+  if (d != 64 && d != 128) return set_error(MA_ERR_UNSUPPORTED, "fp8 head_dim %d (supported: 64, 128)", d);
+  if (out_dtype != MA_BF16 && out_dtype != MA_F32) return set_error(MA_ERR_UNSUPPORTED, "out dtype %d", out_dtype);
+  if (kv_strides[2] < d) return set_error(MA_ERR_INVALID, "head stride %lld < head_dim", (long long)kv_strides[2]);
+  if (page_size < fp8_rows_per_gather(d))
+    return set_error(MA_ERR_UNSUPPORTED, "fp8 prefill needs pages of at least %d keys at head_dim %d",
+                     fp8_rows_per_gather(d), d);
+  if ((int64_t)page_size * kv_strides[1] >= ((int64_t)1 << 31))
+    return set_error(MA_ERR_UNSUPPORTED, "a page's bytes exceed a 32-bit offset");
+  if (total_q == 0 || plan->num_rows == 0) return MA_OK;
+  if (!plan->on_device) {
+    st = plan_upload(const_cast<ma_plan *>(plan), stream);
+    if (st != MA_OK) return st;
+  }
+  Fp8Args a{};
+  a.plan = plan;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.page_shift = log2i(page_size);
+  a.s_page = kv_strides[0];
+  a.s_slot = kv_strides[1];
+  a.s_head = kv_strides[2];
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.out_dtype = out_dtype;
+  a.scale = scale;
+  a.q_descale = q_descale;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
+  a.out = out;
+  a.lse = lse;
+  a.stream = stream;
+  return launch_prefill_fp8(a);
+}
+
 size_t attn_backward_workspace(const ma_plan *plan, int32_t hq) {
   if (!plan || hq < 1) return 0;
   return backward_workspace(plan->total_q, hq);

@@ -117,6 +117,23 @@ struct PrefillArgs {
 };
 ma_status launch_prefill(const PrefillArgs &a);
 
+// attn_fp8.hip
+struct Fp8Args {
+  const ma_plan *plan;
+  const void *q, *k, *v;
+  int32_t hq, hkv, d, page_shift;
+  int64_t s_page, s_slot, s_head;
+  const int32_t *page_table;
+  int32_t max_pages;
+  int32_t out_dtype;
+  float scale, q_descale, k_descale, v_descale;
+  void *out;
+  float *lse;
+  void *stream;
+};
+int32_t fp8_rows_per_gather(int32_t d);
+ma_status launch_prefill_fp8(const Fp8Args &a);
+
 // attn_bwd.hip
 struct BackwardArgs {
   ma_plan *plan;

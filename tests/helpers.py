@@ -108,3 +108,45 @@ def bf16_out_err(gpu_bf16, ref):
     r = ref[sel]
     ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - 7)
     return float((np.abs(g[sel] - r) - ulp).max())
+
+
+# ------------------------------------------------------------------- fp8 --
+def fp8_dequantized(w, f8):
+    """The workload with Q / K / V replaced by the exact values of their e4m3
+    bytes times the descale factors (what the fp8 kernel computes with)."""
+    import copy
+    from oracle import fp8 as OF
+    w2 = copy.copy(w)
+    w2.q = OF.e4m3_decode(f8["q8"]) * f8["q_s"]
+    w2.k_cache = OF.e4m3_decode(f8["k8"]) * f8["k_s"]
+    w2.v_cache = OF.e4m3_decode(f8["v8"]) * f8["v_s"]
+    return w2
+
+
+def fp8_bound(q_rows, k, v, mask_rows, scale, o_ref):
+    """Error bounds of the fp8 kernel for the given query rows of one head,
+    returned as (per-element bound on O, per-row bound on LSE).
+
+    The kernel's probabilities are rounded to e4m3: relative half-ulp 2^-4,
+    absolute 2^-10 below the normal range, in units of the kernel's running
+    reference maximum, which never exceeds the row's true maximum, so in units
+    where the row's largest probability is 1 each rounding error is at most
+    e_k = max(2^-4 p_k, 2^-10).  Then O moves by exactly
+    sum_k eps_k (V_k - O) / sum_k p~_k; the bound is six standard deviations
+    of that sum for independent errors (variance at most e_k^2 / 3), plus
+    1e-3 for fp32 accumulation.  The row sum moves by at most sum_k e_k, which
+    bounds the LSE error by that over sum_k p_k (with 5% slack) plus 1e-4."""
+    s = scale * (q_rows @ k.T)
+    s = np.where(mask_rows, s, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    has = np.isfinite(mx)
+    p = np.where(mask_rows & has, np.exp(np.where(mask_rows & has, s - np.where(has, mx, 0.0), 0.0)), 0.0)
+    e = np.where(mask_rows & has, np.maximum(2.0 ** -4 * p, 2.0 ** -10), 0.0)
+    e2 = e ** 2
+    # sum_k e_k^2 (V_kx - O_tx)^2, expanded into products
+    var = (e2 @ v ** 2) - 2.0 * o_ref * (e2 @ v) + o_ref ** 2 * e2.sum(axis=1, keepdims=True)
+    var = np.maximum(var, 0.0) / 3.0
+    tot = np.maximum(p.sum(axis=1, keepdims=True), 1e-300)
+    o_bound = 6.0 * np.sqrt(var) / tot + 1e-3
+    lse_bound = 1.05 * e.sum(axis=1) / tot[:, 0] + 1e-4
+    return o_bound, lse_bound

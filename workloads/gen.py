@@ -12,6 +12,10 @@ Recipe (the same for tests, benchmark and oracle checks):
     random permutation of all pages otherwise.  Unused slots of the last page,
     two spare pages and every page-table entry past a sequence's last page
     hold / point at NaN, so a read past kv_len shows up in the output.
+  * fp8 inputs (fp8_inputs): per-tensor descale = max |x| / 448 over the
+    finite values of Q, of the K cache and of the V cache; each value x is
+    stored as the e4m3 byte of x / descale, rounded to nearest even
+    (torch's float8_e4m3fn conversion); NaN slots stay NaN bytes.
   * Mask buffers are laid out as the caller hands them over: a dense mask is
     one row-major q_len x kv_len uint8 block per sequence, concatenated; a
     packed mask is one row of ceil(kv_len / 64) uint64 words per query, key j
@@ -413,3 +417,22 @@ def mask_inputs(seed=9, d=128, hq=8, hkv=2, q_lens=(300, 5, 130, 700, 1), kv_len
     w.masks["dense_window"] = MaskInput("dense", data=flat, window=111)
     w.masks["packed_window"] = MaskInput("packed", data=packed, window=111)
     return w
+
+
+# --------------------------------------------------------------------- fp8 --
+def _e4m3_bytes(x, descale):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32) / np.float32(descale))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def fp8_inputs(w):
+    """e4m3 bytes and per-tensor descale factors of a workload's Q, K cache
+    and V cache: dict q8, k8, v8 (uint8, same shapes) and q_s, k_s, v_s."""
+    out = {}
+    for name, x in (("q", w.q), ("k", w.k_cache), ("v", w.v_cache)):
+        amax = float(np.nanmax(np.abs(x)))
+        ds = amax / 448.0 if amax > 0 else 1.0
+        out[name + "8"] = _e4m3_bytes(x, ds)
+        out[name + "_s"] = ds
+    return out
