@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X published dense bf16 matrix-core peak
+PEAK_FP8_TFLOPS = 5000.0      # MI355X published dense fp8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 METRIC = "masked-attn prefill effective TFLOP/s (unmasked FLOPs) and % of bf16 MFMA peak"
 KERNEL_SOURCES = ["masked_flash_attention_mask_amd/csrc/attn_fwd.hip",
@@ -157,12 +158,15 @@ def main():
     ap.add_argument("--classify", action="store_true",
                     help="print only the device mask-classify lines (block mask, packed and dense)")
     ap.add_argument("--backward", action="store_true", help="print only the backward lines")
+    ap.add_argument("--fp8", action="store_true", help="print only the fp8 (e4m3) prefill lines")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
-    if args.decode or args.classify or args.backward:
+    if args.decode or args.classify or args.backward or args.fp8:
+        if args.fp8:
+            fp8_lines(args.steps, args.warmup)
         if args.decode:
             decode_lines(args.steps, args.warmup)
         if args.classify:
@@ -240,6 +244,7 @@ def main():
         extra(args)
         decode_lines(args.steps, args.warmup)
         backward_lines(args.steps, args.warmup)
+        fp8_lines(args.steps, args.warmup)
 
 
 def extra(args):
@@ -378,6 +383,39 @@ def backward_lines(steps, warmup):
                           "tflops": round(tf, 2), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
                           "flops_per_step": 10.0 * d * hq * n_unmasked,
                           "kernels": "bwd_prep, bwd_dq<128,128>, bwd_dkdv<128>"}), flush=True)
+        del plan
+
+
+def fp8_lines(steps, warmup):
+    """fp8 (e4m3) prefill of the headline workload and of causal at the same
+    shape: the bf16 inputs quantized per tensor, bf16 output."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import masked_flash_attention_mask_amd as ma
+    from workloads.device import plan_kwargs
+    seq, prefix, cs, hq, d = 16384, 1024, 2, 16, 128
+    w = W.config4(seq=seq, prefix=prefix, hq=hq, d=d, chunk_sizes=(cs,))
+    f8 = W.fp8_inputs(w)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(f8[k])).cuda() for k in ("q8", "k8", "v8")}
+    pt = torch.from_numpy(w.page_table).cuda().contiguous()
+    out = torch.empty(dev["q8"].shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(dev["q8"].shape[:2], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for name, n_unmasked in ((f"chunk{cs}", chunk_unmasked(seq, prefix, cs)), ("causal", seq * (seq + 1) // 2)):
+        kind, kw = plan_kwargs(w, name)
+        plan = ma.mask_compile(kind, w.cu_seqlens_q, w.kv_lens, **kw)
+
+        def step():
+            ma.attn_prefill_masked_fp8(plan, dev["q8"], dev["k8"], dev["v8"], pt, w.scale, f8["q_s"], f8["k_s"],
+                                       f8["v_s"], out=out, lse=lse)
+        ms = time_steps(step, steps, warmup, stream)
+        tf = 4.0 * d * hq * n_unmasked / (ms * 1e-3) / 1e12
+        print(json.dumps({"workload": f"prefill_fp8_{name}_16k", "mask": name, "ms": round(ms, 4),
+                          "tflops": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                          "pct_of_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+                          "flops_per_step": 4.0 * d * hq * n_unmasked,
+                          "kernel": "prefill_fp8_kernel<128,bf16>"}), flush=True)
         del plan
 
 
