@@ -260,6 +260,12 @@ def test_block_sparse_special_cases():
     full = M.block_sparse(q_len, kv_len, 5, 6, np.arange(nrb + 1) * ncb, np.tile(np.arange(ncb), nrb))
     assert full.all()
     assert not M.block_sparse(q_len, kv_len, 5, 6, np.zeros(nrb + 1, int), np.zeros(0, int)).any()
+    # a column listed twice in a block row is the same as listed once
+    ip1 = np.arange(nrb + 1)
+    ix1 = np.arange(nrb) % ncb
+    ip2 = 2 * np.arange(nrb + 1)
+    ix2 = np.repeat(ix1, 2)
+    assert np.array_equal(M.block_sparse(q_len, kv_len, 5, 6, ip1, ix1), M.block_sparse(q_len, kv_len, 5, 6, ip2, ix2))
 
 
 def test_window_band():
