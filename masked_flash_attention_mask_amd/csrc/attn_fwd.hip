@@ -19,6 +19,8 @@
 // stage.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "internal.h"
 #include "kernels_common.h"
 #include "tile_bf16.h"
@@ -92,6 +94,7 @@ struct Bf16Cfg {
   static constexpr int NT = NW * 64;
   static constexpr size_t STAGE_ELEMS = DMA ? (size_t)dma::Stage<D>::ELEMS : (size_t)Stage<D>::ELEMS;
   static constexpr size_t LDS_BYTES = 2 * STAGE_ELEMS * sizeof(uint16_t);
+  static constexpr bool PIPE = DMA && D <= 128 && BQ == 128;
 };
 
 // Plan entries are read through the constant address space: uniform reads
@@ -140,7 +143,105 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
 
   const int eb = it.ent_begin, ee = it.ent_end;
   uint64_t word_nxt = 0;
-  if constexpr (DMA) {
+  if constexpr (C::PIPE) {
+    // Software-pipelined over tiles: step j issues the products S^T of tile
+    // j + 1 and, beside them, the masking and softmax of tile j, then
+    // O^T += V^T P^T of tile j, so the vector work of one tile runs while the
+    // matrix cores take the next tile's scores.  K of tile t is gathered at
+    // step t - 2 and V at step t - 1: step j reads K(j + 1) from stage
+    // (j + 1) % 2 and V(j) from stage j % 2 while the gathers write K(j + 2)
+    // into stage j % 2 and V(j + 1) into stage (j + 1) % 2.
+    using KV = dma::KvDma<D, C::NW>;
+    constexpr uint32_t SB = (uint32_t)dma::Stage<D>::BYTES, VB = 2u * dma::Stage<D>::V_OFF;
+    constexpr int SE = dma::Stage<D>::ELEMS;
+    const dma::LaneOffsets<D> lo(lane);
+    const uint32_t lds0 = dma::lds_addr(lds);
+    const int n = ee - eb;
+    auto pages_of = [&](int j) { return KV::pages_uniform(pt, p.page_shift, entry_kt(load_entry(p.entries, eb + j).kt_cls), kv_len, wave); };
+    using IsK = std::integral_constant<bool, false>;
+    using IsV = std::integral_constant<bool, true>;
+    const dma::LaneGather<D, C::NW, false> lgk(wave, lane, p.s_slot);
+    const dma::LaneGather<D, C::NW, true> lgv(wave, lane, p.s_slot);
+    const uint32_t page_bytes = (uint32_t)(p.s_page * 2), slot_bytes = (uint32_t)(p.s_slot * 2);
+    auto gather = [&](auto is_v, const typename KV::Pages &pg, int j, uint32_t dst) {
+      constexpr bool V = decltype(is_v)::value;
+      const int kt = entry_kt(load_entry(p.entries, eb + j).kt_cls);
+      auto go = [&](auto clamp) {
+        constexpr bool CL = decltype(clamp)::value;
+        if constexpr (V)
+          dma::issue_mat_fast<D, C::NW, true, CL>(vbase, pg, lgv, p.page_shift, page_bytes, slot_bytes, kt, kv_len,
+                                                  dst, wave, lane);
+        else
+          dma::issue_mat_fast<D, C::NW, false, CL>(kbase, pg, lgk, p.page_shift, page_bytes, slot_bytes, kt, kv_len,
+                                                   dst, wave, lane);
+      };
+      if (kt * 64 + 64 <= kv_len)
+        go(std::integral_constant<bool, false>{});
+      else
+        go(std::integral_constant<bool, true>{});
+    };
+    typename KV::Pages pg_a, pg_b;   // pages of tiles j + 2 and j + 1 at the start of step j
+    uint64_t word_cur = 0;
+    f32x16 sa[2], sb[2];
+    if (n > 0) {
+      const typename KV::Pages pg0 = pages_of(0);
+      gather(IsK{}, pg0, 0, lds0);
+      gather(IsV{}, pg0, 0, lds0 + VB);
+      word_cur = load_word(load_entry(p.entries, eb));
+      if (n > 1) {
+        pg_b = pages_of(1);
+        gather(IsK{}, pg_b, 1, lds0 + SB);
+        word_nxt = load_word(load_entry(p.entries, eb + 1));
+        if (n > 2) pg_a = pages_of(2);
+      }
+      dma::wait_vmem();
+      __syncthreads();
+      dma::qk_tile<D, (D > 64 ? 4 : D / 16)>(lds, lo, qf, sa);
+      if (n > 2) __syncthreads();   // every wave has read K(0) before K(2) replaces it
+    }
+    auto step = [&](f32x16 (&scur)[2], f32x16 (&snxt)[2], int j) {
+      const int cur = j & 1;
+      const Entry ec = load_entry(p.entries, eb + j);
+      const uint64_t wcur = word_cur;
+      if (j + 2 < n) gather(IsK{}, pg_a, j + 2, lds0 + (uint32_t)cur * SB);
+      if (j + 1 < n) gather(IsV{}, pg_b, j + 1, lds0 + (uint32_t)(cur ^ 1) * SB + VB);
+      word_cur = word_nxt;
+      if (j + 2 < n) {
+        word_nxt = load_word(load_entry(p.entries, eb + j + 2));
+        pg_b = pg_a;
+        if (j + 3 < n) pg_a = pages_of(j + 3);
+      }
+      const int kt = entry_kt(ec.kt_cls);
+      const int cls = entry_cls(ec.kt_cls);
+      const int kin = kv_len - kt * 64;
+      if (cls == MA_TILE_PARTIAL || kin < 64)
+        apply_word(scur, (cls == MA_TILE_PARTIAL ? wcur : ~0ull) & low_bits(kin), hi);
+      // unconditional (at the last step the result is unused): a branch here
+      // would split the products from the softmax they are to overlap
+      dma::qk_tile_free<D>(lds + (cur ^ 1) * SE, lo, qf, snxt);
+      float alpha, ps;
+      const bool any = softmax_tile(scur, m_ref, c, alpha);
+      bf16x8 pb[4];
+      dma::pack_p(scur, pb, ps);
+      // P is complete here, in the same block as the products above: without
+      // this the exponentials sink past the rescale branch below and run
+      // after the products instead of beside them
+      asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(ps));
+      if (any) {
+#pragma unroll
+        for (int x = 0; x < D / 32; ++x) oacc[x] *= alpha;
+        lsum *= alpha;
+      }
+      lsum += ps;
+      dma::pv_tile_packed<D>(lds + cur * SE, lo, pb, oacc);
+      dma::wait_vmem();
+      __syncthreads();
+    };
+    for (int j = 0; j < n; j += 2) {
+      step(sa, sb, j);
+      if (j + 1 < n) step(sb, sa, j + 1);
+    }
+  } else if constexpr (DMA) {
     using KV = dma::KvDma<D, C::NW>;
     const dma::LaneOffsets<D> lo(lane);
     const uint32_t lds0 = dma::lds_addr(lds);
@@ -385,7 +486,8 @@ ma_status dispatch_bf16_mode(const PrefillArgs &a, const PrefillParams &prm, int
 // them) inside one page, and a page's bytes addressable by a 32-bit offset.
 template <int D, int BQ>
 ma_status dispatch_bf16(const PrefillArgs &a, const PrefillParams &prm, int grid) {
-  const bool fits = ((int64_t)1 << a.page_shift) * a.s_slot * 2 < ((int64_t)1 << 31);
+  const bool fits = ((int64_t)1 << a.page_shift) * a.s_slot * 2 < ((int64_t)1 << 31) &&
+                    a.s_page * 2 < ((int64_t)1 << 32);
   if ((1 << a.page_shift) >= dma::KvDma<D, BQ / 32>::RPI && fits) return dispatch_bf16_mode<D, BQ, true>(a, prm, grid);
   return dispatch_bf16_mode<D, BQ, false>(a, prm, grid);
 }

@@ -125,11 +125,10 @@ __device__ __forceinline__ bool softmax_tile(f32x16 (&s)[2], float &m_ref, float
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
   const float mxc = max_halves(mx) * c;
   const bool raise = mxc > m_ref + kRescaleSlack;
-  alpha = 1.f;
-  if (raise) {
-    alpha = fast_exp2(m_ref - mxc);   // 0 when m_ref is still -inf
-    m_ref = mxc;
-  }
+  // selects, not a branch: the kernels schedule matrix products across this
+  const float a = fast_exp2(m_ref - mxc);   // 0 when m_ref is still -inf
+  alpha = raise ? a : 1.f;
+  m_ref = raise ? mxc : m_ref;
   const bool any = __builtin_amdgcn_ballot_w64(raise) != 0ull;
   const float mu = m_ref == neg_inf() ? 0.f : m_ref;
 #pragma unroll

@@ -130,6 +130,81 @@ struct KvDma {
   }
 };
 
+// One matrix (K when !IS_V, V when IS_V) of issue(), into the LDS byte address
+// dst of that matrix's half of a stage: the software-pipelined kernel
+// gathers a tile's K one step before its V.
+template <int D, int NW, bool IS_V>
+__device__ __forceinline__ void issue_mat(const uint16_t *base, const typename KvDma<D, NW>::Pages &pg,
+                                          int page_shift, int64_t s_page, int64_t s_slot, int kt, int kv_len,
+                                          uint32_t dst, int wave, int lane) {
+  constexpr int CH = KvDma<D, NW>::CH, IPW = KvDma<D, NW>::IPW;
+  const int pmask = (1 << page_shift) - 1;
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int t = wave * IPW + i;
+    const int pos = 64 * t + lane;
+    const int r = pos / CH, pc = pos % CH;
+    const int key = min(kt * 64 + r, kv_len - 1);
+    const int64_t pb = (int64_t)pg.id[i] * s_page;
+    const uint32_t slot = (uint32_t)((key & pmask) * (int)s_slot) * 2;
+    const int sw = IS_V ? Stage<D>::fv(r) : Stage<D>::fk(r);
+    lds_load16_s((gptr_t)(base + pb), slot + 16 * (pc ^ sw), dst + 1024 * t);
+  }
+}
+
+// issue_mat for a tile that lies wholly below kv_len (no key is clamped):
+// an instruction's RPI rows are then consecutive slots of one page, so the
+// lane's source offset splits into a scalar part (page base and the first
+// row's slot, folded into the SGPR base) and a per-lane constant (the row
+// inside the group and the swizzled chunk), computed once per kernel.  No
+// vector instruction per gather.  Needs page bytes (2 s_page) < 2^32 and page
+// ids >= 0.
+template <int D, int NW, bool IS_V>
+struct LaneGather {
+  static constexpr int CH = KvDma<D, NW>::CH, IPW = KvDma<D, NW>::IPW, RPI = KvDma<D, NW>::RPI;
+  uint32_t off[IPW];
+  __device__ __forceinline__ LaneGather(int wave, int lane, int64_t s_slot) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int t = wave * IPW + i;
+      const int r = RPI * t + lane / CH, pc = lane % CH;
+      const int sw = IS_V ? Stage<D>::fv(r) : Stage<D>::fk(r);
+      off[i] = (uint32_t)((lane / CH) * (int)s_slot) * 2 + 16 * (pc ^ sw);
+    }
+  }
+};
+
+// CLAMP: the tile may reach past kv_len; keys past it are clamped to the last
+// key, which lies in the page of the instruction's first row (pages hold a
+// multiple of RPI keys, and a group is clamped only where it starts at or
+// before the last key or lies wholly past it, when pages_uniform took the
+// last key's page), so only the lane's slot moves: by (clamped key -
+// unclamped key) slots, a few vector instructions on the last tile only.
+template <int D, int NW, bool IS_V, bool CLAMP>
+__device__ __forceinline__ void issue_mat_fast(const uint16_t *base, const typename KvDma<D, NW>::Pages &pg,
+                                               const LaneGather<D, NW, IS_V> &lg, int page_shift,
+                                               uint32_t page_bytes, uint32_t slot_bytes, int kt, int kv_len,
+                                               uint32_t dst, int wave, int lane) {
+  constexpr int IPW = KvDma<D, NW>::IPW, RPI = KvDma<D, NW>::RPI, CH = KvDma<D, NW>::CH;
+  const int pmask = (1 << page_shift) - 1;
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int t = wave * IPW + i;
+    const int key0 = kt * 64 + RPI * t;
+    uint32_t voff = lg.off[i];
+    int k0 = key0;
+    if constexpr (CLAMP) {
+      // rows of a group wholly past the last key all read the last key
+      k0 = min(key0, kv_len - 1);
+      const int key = min(key0 + lane / CH, kv_len - 1);
+      voff += (uint32_t)((key - k0 - lane / CH) * (int)slot_bytes);
+    }
+    const uint32_t row0 = (uint32_t)(k0 & pmask);
+    const uint64_t off = (uint64_t)(uint32_t)pg.id[i] * page_bytes + row0 * slot_bytes;
+    lds_load16_s((gptr_t)((const char *)base + off), voff, dst + 1024 * t);
+  }
+}
+
 // Waits for this wave's outstanding global loads (the LDS gathers among them).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -168,10 +243,9 @@ struct LaneOffsets {
 // rows.  Operands are read in register-budget-sized groups before their
 // products (sched_barrier keeps the compiler from sinking each read onto its
 // use): both 32-key blocks for d <= 128, half a block for d = 256.
-template <int D>
+template <int D, int GROUP = (D <= 128 ? 2 * (D / 16) : 8)>
 __device__ __forceinline__ void qk_tile(const uint16_t *stage, const LaneOffsets<D> &lo, const bf16x8 (&qf)[D / 16],
                                         f32x16 (&s)[2]) {
-  constexpr int GROUP = D <= 128 ? 2 * (D / 16) : 8;
   constexpr int NG = 2 * (D / 16) / GROUP;
   const uint16_t *kl = stage + lo.krow;
 #pragma unroll
@@ -241,6 +315,56 @@ __device__ __forceinline__ void pv_tile(const uint16_t *stage, const LaneOffsets
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u % NB][n], pb, o[n], 0, 0, 0);
     lsum = row_sum_bf16(pb, lsum);
+  }
+}
+
+// S^T = K Q^T as qk_tile, without scheduling fences: the software-pipelined
+// kernel lets the compiler interleave these products with the previous
+// tile's softmax.
+template <int D>
+__device__ __forceinline__ void qk_tile_free(const uint16_t *stage, const LaneOffsets<D> &lo,
+                                             const bf16x8 (&qf)[D / 16], f32x16 (&s)[2]) {
+  const uint16_t *kl = stage + lo.krow;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    s[kb] = f32x16{};
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4 *)(kl + 32 * kb * D + lo.kop(k)));
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k], s[kb], 0, 0, 0);
+    }
+  }
+}
+
+// P (the exponentiated S^T accumulators) as the four bf16 B operands of
+// O^T += V^T P^T (operand u: registers 8 (u % 2) .. + 7 of block u / 2), and
+// ps = the lane's sum of exactly those bf16 values (v_dot2_f32_bf16).
+__device__ __forceinline__ void pack_p(const f32x16 (&p)[2], bf16x8 (&pb)[4], float &ps) {
+  ps = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    f32x8 pv;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) pv[x] = p[u >> 1][8 * (u & 1) + x];
+    pb[u] = __builtin_convertvector(pv, bf16x8);
+    ps = row_sum_bf16(pb[u], ps);
+  }
+}
+
+// O^T += V^T P^T from packed operands (pack_p); the V^T operands of product
+// u + 1 are read while product u runs.
+template <int D>
+__device__ __forceinline__ void pv_tile_packed(const uint16_t *stage, const LaneOffsets<D> &lo,
+                                               const bf16x8 (&pb)[4], f32x16 (&o)[D / 32]) {
+  static_assert(D <= 128, "packed P V reads two products' operands ahead");
+  bf16x8 a[2][D / 32];
+  read_vt<D>(stage, lo, a[0], 0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (u + 1 < 4) read_vt<D>(stage, lo, a[(u + 1) & 1], u + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u & 1][n], pb[u], o[n], 0, 0, 0);
   }
 }
 
