@@ -150,7 +150,8 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
     // matrix cores take the next tile's scores.  K of tile t is gathered at
     // step t - 2 and V at step t - 1: step j reads K(j + 1) from stage
     // (j + 1) % 2 and V(j) from stage j % 2 while the gathers write K(j + 2)
-    // into stage j % 2 and V(j + 1) into stage (j + 1) % 2.
+    // into stage j % 2 and V(j + 1) into stage (j + 1) % 2.  Each step ends
+    // with a wait for this wave's gathers and a workgroup barrier.
     using KV = dma::KvDma<D, C::NW>;
     constexpr uint32_t SB = (uint32_t)dma::Stage<D>::BYTES, VB = 2u * dma::Stage<D>::V_OFF;
     constexpr int SE = dma::Stage<D>::ELEMS;
@@ -163,6 +164,8 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
     const dma::LaneGather<D, C::NW, false> lgk(wave, lane, p.s_slot);
     const dma::LaneGather<D, C::NW, true> lgv(wave, lane, p.s_slot);
     const uint32_t page_bytes = (uint32_t)(p.s_page * 2), slot_bytes = (uint32_t)(p.s_slot * 2);
+    // log2 of the keys one wave gathers per matrix and tile (RPI * IPW)
+    constexpr int kPageRunShift = __builtin_ctz(KV::RPI * KV::IPW);
     auto gather = [&](auto is_v, const typename KV::Pages &pg, int j, uint32_t dst) {
       constexpr bool V = decltype(is_v)::value;
       const int kt = entry_kt(load_entry(p.entries, eb + j).kt_cls);
@@ -175,10 +178,20 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
           dma::issue_mat_fast<D, C::NW, false, CL>(kbase, pg, lgk, p.page_shift, page_bytes, slot_bytes, kt, kv_len,
                                                    dst, wave, lane);
       };
-      if (kt * 64 + 64 <= kv_len)
-        go(std::integral_constant<bool, false>{});
-      else
+      if (kt * 64 + 64 <= kv_len) {
+        if (p.page_shift >= kPageRunShift) {
+          if constexpr (V)
+            dma::issue_mat_page<D, C::NW, true>(vbase, pg.id[0], lgv, p.page_shift, page_bytes, slot_bytes, kt, dst,
+                                                wave);
+          else
+            dma::issue_mat_page<D, C::NW, false>(kbase, pg.id[0], lgk, p.page_shift, page_bytes, slot_bytes, kt, dst,
+                                                 wave);
+        } else {
+          go(std::integral_constant<bool, false>{});
+        }
+      } else {
         go(std::integral_constant<bool, true>{});
+      }
     };
     typename KV::Pages pg_a, pg_b;   // pages of tiles j + 2 and j + 1 at the start of step j
     uint64_t word_cur = 0;

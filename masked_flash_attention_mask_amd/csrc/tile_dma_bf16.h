@@ -205,6 +205,25 @@ __device__ __forceinline__ void issue_mat_fast(const uint16_t *base, const typen
   }
 }
 
+// issue_mat_fast without clamping for pages of at least RPI * IPW keys: the
+// rows of this wave's IPW instructions then lie in one page (an aligned run
+// of RPI * IPW keys), so one page id and one scalar base serve all of them
+// and each further instruction adds a constant: two scalar adds and the M0
+// write per gather.
+template <int D, int NW, bool IS_V>
+__device__ __forceinline__ void issue_mat_page(const uint16_t *base, int32_t page_id,
+                                               const LaneGather<D, NW, IS_V> &lg, int page_shift,
+                                               uint32_t page_bytes, uint32_t slot_bytes, int kt, uint32_t dst,
+                                               int wave) {
+  constexpr int IPW = KvDma<D, NW>::IPW, RPI = KvDma<D, NW>::RPI;
+  const int pmask = (1 << page_shift) - 1;
+  const uint32_t row0 = (uint32_t)((kt * 64 + RPI * IPW * wave) & pmask);
+  const char *b0 = (const char *)base + ((uint64_t)(uint32_t)page_id * page_bytes + row0 * slot_bytes);
+#pragma unroll
+  for (int i = 0; i < IPW; ++i)
+    lds_load16_s((gptr_t)(b0 + (uint64_t)(i * RPI) * slot_bytes), lg.off[i], dst + 1024 * (wave * IPW + i));
+}
+
 // Waits for this wave's outstanding global loads (the LDS gathers among them).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
