@@ -226,12 +226,14 @@ ma_status attn_prefill_masked(const ma_plan *plan, const void *q, int64_t total_
  * factors: the attention is softmax(scale * q_descale * k_descale * Q8 K8^T
  * + mask) (v_descale * V8), Q8 / K8 / V8 the decoded bytes.
  *  out_dtype BF16 or F32; d in {64, 128}; plans with tile 128 x 64; page
- *  size at least 1024 / d keys (one gather instruction's rows in one page).
+ *  size at least 1024 / d keys (one gather instruction's rows in one page);
+ *  a page's bytes (page stride) below 2^32 and page_size * slot stride below
+ *  2^31.
  * Arithmetic: both products on fp8 matrix cores with fp32 accumulation; the
  * probabilities are rounded to e4m3 (round to nearest even) for P V and the
  * row sums add those rounded values.  Deterministic; stream-ordered.
  * Errors as attn_prefill_masked, plus INVALID for descale factors that are
- * not positive and finite, UNSUPPORTED for small pages. */
+ * not positive and finite, UNSUPPORTED for small or too large pages. */
 ma_status attn_prefill_masked_fp8(const ma_plan *plan, const void *q, int64_t total_q, int32_t hq,
                                   const void *k_cache, const void *v_cache, int32_t hkv, int32_t d,
                                   int32_t page_size, const int64_t kv_strides[3], const int32_t *page_table,

@@ -292,7 +292,7 @@ ma_status attn_prefill_masked_fp8(const ma_plan *plan, const void *q, int64_t to
   if (page_size < fp8_rows_per_gather(d))
     return set_error(MA_ERR_UNSUPPORTED, "fp8 prefill needs pages of at least %d keys at head_dim %d",
                      fp8_rows_per_gather(d), d);
-  if ((int64_t)page_size * kv_strides[1] >= ((int64_t)1 << 31))
+  if ((int64_t)page_size * kv_strides[1] >= ((int64_t)1 << 31) || kv_strides[0] >= ((int64_t)1 << 32))
     return set_error(MA_ERR_UNSUPPORTED, "a page's bytes exceed a 32-bit offset");
   if (total_q == 0 || plan->num_rows == 0) return MA_OK;
   if (!plan->on_device) {

@@ -80,15 +80,30 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8 &a, const i32x8 &b, const
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
 }
 
-// Gather of one tile by NW waves into the stage at LDS byte address `stage`:
-// instruction t of a matrix fills LDS chunks [64 t, 64 t + 64); its RPI key
-// rows share one page (a scalar page id), so the source is a scalar page
-// base plus a 32-bit lane offset.  Keys past kv_len repeat the last key.
-template <int D, int NW>
-struct Fp8Dma {
+// Gather of one 64-key tile's K or V by NW waves into an LDS slot: wave
+// instruction t fills LDS chunks [64 t, 64 t + 64), lane l the chunk of row
+// RPI t + l / CH, chunk l % CH (source side swizzled).  The RPI rows of an
+// instruction lie in one page (a scalar page id), so the source is a scalar
+// base plus a 32-bit lane offset; for tiles inside kv_len that offset is a
+// per-lane constant (off[i], the row inside the group and the swizzled
+// chunk) and the page and first row go into the scalar base.  Keys past
+// kv_len (the last tile) repeat the last key: they lie in the page of the
+// group's first row, so only the lane's slot moves.
+template <int D, int NW, bool IS_V>
+struct Fp8Gather {
   using St = Fp8Stage<D>;
-  static constexpr int IPW = St::CH / NW;  // instructions per wave per matrix
+  static constexpr int IPW = St::CH / NW;   // instructions per wave
+  static constexpr int RUN = St::RPI * IPW; // keys one wave gathers
   static_assert(St::CH % NW == 0, "gather needs CH to be a multiple of the wave count");
+  uint32_t off[IPW];
+  __device__ __forceinline__ Fp8Gather(int wave, int lane, uint32_t slot_bytes) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int t = wave * IPW + i;
+      const int r = St::RPI * t + lane / St::CH, pc = lane % St::CH;
+      off[i] = (uint32_t)(lane / St::CH) * slot_bytes + 16 * (pc ^ (IS_V ? St::fv(r) : St::fk(r)));
+    }
+  }
   struct Pages {
     int32_t id[IPW];
   };
@@ -99,29 +114,49 @@ struct Fp8Dma {
     for (int i = 0; i < IPW; ++i) pg.id[i] = cpt[min(kt * 64 + St::RPI * (wave * IPW + i), kv_len - 1) >> page_shift];
     return pg;
   }
-  __device__ __forceinline__ static void issue(const uint8_t *kbase, const uint8_t *vbase, const Pages &pg,
-                                               int page_shift, int64_t s_page, int64_t s_slot, int kt, int kv_len,
-                                               uint32_t stage, int wave, int lane) {
+  __device__ __forceinline__ void issue(const uint8_t *base, const Pages &pg, int page_shift, uint32_t page_bytes,
+                                        uint32_t slot_bytes, int kt, int kv_len, uint32_t dst, int wave,
+                                        int lane) const {
     const int pmask = (1 << page_shift) - 1;
+    if (kt * 64 + 64 <= kv_len && page_shift >= __builtin_ctz(RUN)) {
+      // one page for the wave's whole run of keys
+      const uint32_t row0 = (uint32_t)((kt * 64 + RUN * wave) & pmask);
+      const uint8_t *b0 = base + ((uint64_t)(uint32_t)pg.id[0] * page_bytes + row0 * slot_bytes);
+#pragma unroll
+      for (int i = 0; i < IPW; ++i)
+        dma::lds_load16_s((dma::gptr_t)(b0 + (uint64_t)(i * St::RPI) * slot_bytes), off[i],
+                          dst + 1024 * (wave * IPW + i));
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int t = wave * IPW + i;
-      const int pos = 64 * t + lane;
-      const int r = pos / St::CH, pc = pos % St::CH;
-      const int key = min(kt * 64 + r, kv_len - 1);
-      const int64_t pb = (int64_t)pg.id[i] * s_page;
-      const uint32_t slot = (uint32_t)((key & pmask) * (int)s_slot);
-      dma::lds_load16_s((dma::gptr_t)(kbase + pb), slot + 16 * (pc ^ St::fk(r)), stage + 1024 * t);
-      dma::lds_load16_s((dma::gptr_t)(vbase + pb), slot + 16 * (pc ^ St::fv(r)), stage + St::V_OFF + 1024 * t);
+      const int key0 = kt * 64 + St::RPI * t;
+      const int k0 = min(key0, kv_len - 1);
+      const int key = min(key0 + lane / St::CH, kv_len - 1);
+      const uint32_t voff = off[i] + (uint32_t)((key - k0 - lane / St::CH) * (int)slot_bytes);
+      const uint32_t row0 = (uint32_t)(k0 & pmask);
+      const uint8_t *b = base + ((uint64_t)(uint32_t)pg.id[i] * page_bytes + row0 * slot_bytes);
+      dma::lds_load16_s((dma::gptr_t)b, voff, dst + 1024 * t);
     }
   }
+};
+
+// LDS: K slots 0 and 1, then V slots 0 and 1, each [64 keys][D bytes].
+template <int D>
+struct Fp8Lds {
+  static constexpr int SLOT = 64 * D;
+  static constexpr int V0 = 2 * SLOT;
+  static constexpr int BYTES = 4 * SLOT;
 };
 
 template <int D, typename OutT>
 __global__ __launch_bounds__(256, 2) void prefill_fp8_kernel(Fp8Params p) {
   constexpr int BQ = 128, NW = 4;
   using St = Fp8Stage<D>;
-  using KV = Fp8Dma<D, NW>;
+  using L = Fp8Lds<D>;
+  using GK = Fp8Gather<D, NW, false>;
+  using GV = Fp8Gather<D, NW, true>;
   constexpr int KS = D / 64;                 // k-steps of S^T
   extern __shared__ __align__(16) uint8_t lds8[];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -150,8 +185,11 @@ __global__ __launch_bounds__(256, 2) void prefill_fp8_kernel(Fp8Params p) {
   const uint8_t *kbase = p.k + (int64_t)g * p.s_head;
   const uint8_t *vbase = p.v + (int64_t)g * p.s_head;
   const int32_t *pt = p.page_table + (int64_t)it.seq * p.max_pages;
+  const uint32_t page_bytes = (uint32_t)p.s_page, slot_bytes = (uint32_t)p.s_slot;
+  const GK gk(wave, lane, slot_bytes);
+  const GV gv(wave, lane, slot_bytes);
 
-  // Per-lane LDS byte offsets.  K rows 32 kb + l32, chunks 4 s + 2 hi (+1).
+  // Per-lane LDS offsets.  K rows 32 kb + l32, chunks 4 s + 2 hi (+1).
   const int krow = l32 * D;
   const int kf = St::fk(l32);   // the same for rows l32 and l32 + 32
   // V^T: source lane s16 = lane % 16 of group G = lane / 16 loads row
@@ -166,87 +204,31 @@ __global__ __launch_bounds__(256, 2) void prefill_fp8_kernel(Fp8Params p) {
     if (entry_cls(e.kt_cls) != MA_TILE_PARTIAL) return 0ull;
     return p.words[(int64_t)e.wblk * BQ + wrow];
   };
-
+  // S^T = K Q^T of the K tile at LDS byte offset kslot
+  auto qk = [&](int kslot, f32x16 (&sacc)[2]) {
+    const uint8_t *ks = lds8 + kslot;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint8_t *row = ks + 32 * kb * D + krow;
+        const u32x4 a = *(const u32x4 *)(row + 16 * ((4 * s + 2 * hi) ^ kf));
+        const u32x4 b = *(const u32x4 *)(row + 16 * ((4 * s + 2 * hi + 1) ^ kf));
+        const i32x8 ka = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+        sacc[kb] = mfma_fp8(ka, qf[s], sacc[kb]);
+      }
+    }
+  };
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
   f32x16 lacc = f32x16{};
-  float m_ref = neg_inf();
-  const float c = p.c;
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};
-
-  const uint32_t lds0 = dma::lds_addr(lds8);
-  const int eb = it.ent_begin, ee = it.ent_end;
-  uint64_t word_nxt = 0;
-  typename KV::Pages pg_nxt;
-  if (eb < ee) {
-    const Entry e0 = load_entry(p.entries, eb);
-    const int kt0 = entry_kt(e0.kt_cls);
-    const typename KV::Pages pg0 = KV::pages(pt, p.page_shift, kt0, kv_len, wave);
-    KV::issue(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv_len, lds0, wave, lane);
-    word_nxt = load_word(e0);
-    if (eb + 1 < ee) pg_nxt = KV::pages(pt, p.page_shift, entry_kt(load_entry(p.entries, eb + 1).kt_cls), kv_len, wave);
-    dma::wait_vmem();
-    __syncthreads();
-  }
-  for (int e = eb; e < ee; ++e) {
-    const int cur = (e - eb) & 1;
-    const Entry ec = load_entry(p.entries, e);
-    const uint64_t wcur = word_nxt;
-    if (e + 1 < ee) {
-      const Entry en = load_entry(p.entries, e + 1);
-      KV::issue(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, entry_kt(en.kt_cls), kv_len,
-                lds0 + (uint32_t)((cur ^ 1) * St::BYTES), wave, lane);
-      word_nxt = load_word(en);
-      if (e + 2 < ee) pg_nxt = KV::pages(pt, p.page_shift, entry_kt(load_entry(p.entries, e + 2).kt_cls), kv_len, wave);
-    }
-    const uint8_t *ks = lds8 + cur * St::BYTES;
-    const uint8_t *vs = ks + St::V_OFF;
-    // S^T = K Q^T
-    f32x16 sacc[2];
-    {
-      i32x8 ka[2][KS];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const uint8_t *row = ks + 32 * kb * D + krow;
-          const u32x4 a = *(const u32x4 *)(row + 16 * ((4 * s + 2 * hi) ^ kf));
-          const u32x4 b = *(const u32x4 *)(row + 16 * ((4 * s + 2 * hi + 1) ^ kf));
-          ka[kb][s] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
-        }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = mfma_fp8(ka[kb][0], qf[0], f32x16{});
-#pragma unroll
-        for (int s = 1; s < KS; ++s) sacc[kb] = mfma_fp8(ka[kb][s], qf[s], sacc[kb]);
-      }
-    }
-    {
-      const int kt = entry_kt(ec.kt_cls);
-      const int cls = entry_cls(ec.kt_cls);
-      const int kin = kv_len - kt * 64;
-      if (cls == MA_TILE_PARTIAL || kin < 64)
-        apply_word(sacc, (cls == MA_TILE_PARTIAL ? wcur : ~0ull) & low_bits(kin), hi);
-      float alpha;
-      if (softmax_tile(sacc, m_ref, c, alpha)) {
-#pragma unroll
-        for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
-        lacc *= alpha;
-      }
-    }
-    // P -> e4m3 B operand: byte 16 kb + r holds register r of key block kb
-    i32x8 pb;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int kb = w >> 2, r = 4 * (w & 3);
-      int x = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kb][r], sacc[kb][r + 1], 0, false);
-      x = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kb][r + 2], sacc[kb][r + 3], x, true);
-      pb[w] = x;
-    }
-    // O^T += V^T P^T, row sums += ones P^T
+  // O^T += V^T P^T and the row sums += ones P^T, V from LDS byte offset vslot
+  auto pv = [&](int vslot, const i32x8 &pb) {
+    const uint8_t *vs = lds8 + vslot;
 #pragma unroll
     for (int n = 0; n < D / 32; ++n) {
       i32x8 va;
@@ -261,9 +243,89 @@ __global__ __launch_bounds__(256, 2) void prefill_fp8_kernel(Fp8Params p) {
       oacc[n] = mfma_fp8(va, pb, oacc[n]);
     }
     lacc = mfma_fp8(ones, pb, lacc);
+  };
+  float m_ref = neg_inf();
+  const float c = p.c;
+
+  // Software pipeline over the item's tiles: step j runs the softmax of tile
+  // j beside the products S^T of tile j + 1 and O^T += V^T P^T of tile j - 1
+  // (all independent of it), so the vector work of a tile sits between
+  // matrix instructions.  K(t) is gathered at step t - 2, V(t) at step t; step
+  // j reads K(j + 1) from K slot (j + 1) % 2 and V(j - 1) from V slot
+  // (j - 1) % 2 while K(j + 2) and V(j) are written to the other slots.  Each
+  // step ends with a wait for the wave's gathers and a workgroup barrier.
+  const uint32_t lds0 = dma::lds_addr(lds8);
+  const int eb = it.ent_begin, n = it.ent_end - it.ent_begin;
+  auto kt_of = [&](int j) { return entry_kt(load_entry(p.entries, eb + j).kt_cls); };
+  typename GK::Pages pk_a;                   // pages of K(j + 2) at the start of step j
+  typename GV::Pages pv_a;                   // pages of V(j)
+  uint64_t word_cur = 0, word_nxt = 0;
+  f32x16 sa[2], sb[2];
+  i32x8 p_prev = i32x8{};
+  if (n > 0) {
+    // V slot 1 is read (with P = 0) at step 0: clear it so that stale bytes
+    // (NaN codes) cannot reach the accumulators
+    for (int x = tid; x < L::SLOT / 16; x += 256) *(u32x4 *)(lds8 + L::V0 + L::SLOT + 16 * x) = u32x4{0, 0, 0, 0};
+    gk.issue(kbase, GK::pages(pt, p.page_shift, kt_of(0), kv_len, wave), p.page_shift, page_bytes, slot_bytes,
+             kt_of(0), kv_len, lds0, wave, lane);
+    if (n > 1)
+      gk.issue(kbase, GK::pages(pt, p.page_shift, kt_of(1), kv_len, wave), p.page_shift, page_bytes, slot_bytes,
+               kt_of(1), kv_len, lds0 + L::SLOT, wave, lane);
+    if (n > 2) pk_a = GK::pages(pt, p.page_shift, kt_of(2), kv_len, wave);
+    pv_a = GV::pages(pt, p.page_shift, kt_of(0), kv_len, wave);
+    word_cur = load_word(load_entry(p.entries, eb));
+    if (n > 1) word_nxt = load_word(load_entry(p.entries, eb + 1));
     dma::wait_vmem();
     __syncthreads();
+    qk(0, sa);
+    if (n > 2) __syncthreads();   // every wave has read K(0) before K(2) replaces it
   }
+  auto step = [&](f32x16 (&scur)[2], f32x16 (&snxt)[2], int j) {
+    const int cur = j & 1;
+    const Entry ec = load_entry(p.entries, eb + j);
+    const uint64_t wcur = word_cur;
+    if (j + 2 < n)
+      gk.issue(kbase, pk_a, p.page_shift, page_bytes, slot_bytes, kt_of(j + 2), kv_len,
+               lds0 + (uint32_t)(cur * L::SLOT), wave, lane);
+    gv.issue(vbase, pv_a, p.page_shift, page_bytes, slot_bytes, kt_of(j), kv_len,
+             lds0 + (uint32_t)(L::V0 + cur * L::SLOT), wave, lane);
+    word_cur = word_nxt;
+    if (j + 2 < n) word_nxt = load_word(load_entry(p.entries, eb + j + 2));
+    if (j + 1 < n) pv_a = GV::pages(pt, p.page_shift, kt_of(j + 1), kv_len, wave);
+    if (j + 3 < n) pk_a = GK::pages(pt, p.page_shift, kt_of(j + 3), kv_len, wave);
+    const int kt = entry_kt(ec.kt_cls);
+    const int cls = entry_cls(ec.kt_cls);
+    const int kin = kv_len - kt * 64;
+    if (cls == MA_TILE_PARTIAL || kin < 64)
+      apply_word(scur, (cls == MA_TILE_PARTIAL ? wcur : ~0ull) & low_bits(kin), hi);
+    // unconditional: at the last step S^T of a tile past the end is unused
+    qk((cur ^ 1) * L::SLOT, snxt);
+    pv(L::V0 + (cur ^ 1) * L::SLOT, p_prev);
+    float alpha;
+    const bool any = softmax_tile(scur, m_ref, c, alpha);
+    // P -> e4m3 B operand: byte 16 kb + r holds register r of key block kb
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kb = w >> 2, r = 4 * (w & 3);
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(scur[kb][r], scur[kb][r + 1], 0, false);
+      x = __builtin_amdgcn_cvt_pk_fp8_f32(scur[kb][r + 2], scur[kb][r + 3], x, true);
+      p_prev[w] = x;
+    }
+    // keep the softmax in the block of the products above (see the bf16 kernel)
+    asm volatile("" : "+v"(p_prev));
+    if (any) {
+#pragma unroll
+      for (int x = 0; x < D / 32; ++x) oacc[x] *= alpha;
+      lacc *= alpha;
+    }
+    dma::wait_vmem();
+    __syncthreads();
+  };
+  for (int j = 0; j < n; j += 2) {
+    step(sa, sb, j);
+    if (j + 1 < n) step(sb, sa, j + 1);
+  }
+  if (n > 0) pv(L::V0 + ((n - 1) & 1) * L::SLOT, p_prev);
   const float lt = lacc[0];
   if (!row_ok) return;
   const float inv = lt > 0.f ? p.v_descale / lt : 0.f;
@@ -274,7 +336,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fp8_kernel(Fp8Params p) {
 template <int D, typename OutT>
 ma_status launch_d(const Fp8Params &prm, int grid, void *stream) {
   auto kern = prefill_fp8_kernel<D, OutT>;
-  constexpr size_t lds = 2 * Fp8Stage<D>::BYTES;
+  constexpr size_t lds = Fp8Lds<D>::BYTES;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, (hipStream_t)stream, prm);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "fp8 prefill launch: %s", hipGetErrorString(e));
