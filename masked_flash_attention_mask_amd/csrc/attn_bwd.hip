@@ -156,7 +156,16 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p) {
 // K and V (the A operands of S^T and dP^T) and the transposed reads of K (the
 // A operand of dQ^T) are free of bank conflicts.
 // ---------------------------------------------------------------------------
-template <int D, int BQ>
+// FAST (pages of at least 512 / D keys, a page's bytes below 2^32 and
+// page_size * slot stride below 2^31): page ids by scalar loads and, for
+// tiles inside kv_len, a scalar page-and-slot base with per-lane constant
+// offsets (the forward's gather); otherwise a 64-bit address per lane.
+template <int D>
+struct SwzQ {
+  __device__ static constexpr int f(int r) { return QBlk<D>::f(r); }
+};
+
+template <int D, int BQ, bool FAST>
 __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq(BwdParams p) {
   using QB = QBlk<D>;
   constexpr int NW = BQ / 32, CH = D / 8, NI = CH / NW;   // gather instructions per wave per matrix
@@ -188,24 +197,53 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq(BwdParams p)
   // Gather: instruction t of a matrix fills LDS chunks [64 t, 64 t + 64);
   // lane l of it loads key row (64 t + l) / CH, logical chunk ((64 t + l) %
   // CH) ^ f(row).  Keys past kv_len repeat the last key (masked to 0).
-  int32_t pg[NI];
+  using KV = dma::KvDma<D, NW>;
+  static_assert(KV::IPW == NI, "gather geometry");
+  typename KV::Pages pg;
+  [[maybe_unused]] const dma::LaneGather<D, NW, SwzQ<D>> lg(wave, lane, p.s_slot);
+  [[maybe_unused]] const uint32_t page_bytes = (uint32_t)(p.s_page * 2), slot_bytes = (uint32_t)(p.s_slot * 2);
+  [[maybe_unused]] const uint32_t lds_b = dma::lds_addr(lds);
   auto pages = [&](int kt) {
+    if constexpr (FAST) {
+      pg = KV::pages_uniform(pt, p.page_shift, kt, kv_len, wave);
+    } else {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r = (64 * (wave * NI + i) + lane) / CH;
-      pg[i] = pt[min(kt * 64 + r, kv_len - 1) >> p.page_shift];
+      for (int i = 0; i < NI; ++i) {
+        const int r = (64 * (wave * NI + i) + lane) / CH;
+        pg.id[i] = pt[min(kt * 64 + r, kv_len - 1) >> p.page_shift];
+      }
     }
   };
   auto issue = [&](int kt, int sl) {
     uint16_t *st = lds + sl * 2 * TILE;
+    if constexpr (FAST) {
+      const uint32_t sk = lds_b + (uint32_t)(sl * 2 * TILE * 2), sv = sk + (uint32_t)(TILE * 2);
+      if (kt * 64 + 64 <= kv_len) {
+        if (p.page_shift >= __builtin_ctz(KV::RPI * KV::IPW)) {
+          dma::issue_mat_page<D, NW, SwzQ<D>>(kbase, pg.id[0], lg, p.page_shift, page_bytes, slot_bytes, kt, sk, wave);
+          dma::issue_mat_page<D, NW, SwzQ<D>>(vbase, pg.id[0], lg, p.page_shift, page_bytes, slot_bytes, kt, sv, wave);
+        } else {
+          dma::issue_mat_fast<D, NW, SwzQ<D>, false>(kbase, pg, lg, p.page_shift, page_bytes, slot_bytes, kt, kv_len,
+                                                     sk, wave, lane);
+          dma::issue_mat_fast<D, NW, SwzQ<D>, false>(vbase, pg, lg, p.page_shift, page_bytes, slot_bytes, kt, kv_len,
+                                                     sv, wave, lane);
+        }
+      } else {
+        dma::issue_mat_fast<D, NW, SwzQ<D>, true>(kbase, pg, lg, p.page_shift, page_bytes, slot_bytes, kt, kv_len, sk,
+                                                  wave, lane);
+        dma::issue_mat_fast<D, NW, SwzQ<D>, true>(vbase, pg, lg, p.page_shift, page_bytes, slot_bytes, kt, kv_len, sv,
+                                                  wave, lane);
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int t = wave * NI + i;
-      const int pos = 64 * t + lane, r = pos / CH, pc = pos % CH;
-      const int key = min(kt * 64 + r, kv_len - 1);
-      const int64_t off = (int64_t)pg[i] * p.s_page + (int64_t)(key & pmask) * p.s_slot + 8 * (pc ^ QB::f(r));
-      dma::lds_load16(kbase + off, dma::lds_addr(st + 512 * t));
-      dma::lds_load16(vbase + off, dma::lds_addr(st + TILE + 512 * t));
+      for (int i = 0; i < NI; ++i) {
+        const int t = wave * NI + i;
+        const int pos = 64 * t + lane, r = pos / CH, pc = pos % CH;
+        const int key = min(kt * 64 + r, kv_len - 1);
+        const int64_t off = (int64_t)pg.id[i] * p.s_page + (int64_t)(key & pmask) * p.s_slot + 8 * (pc ^ QB::f(r));
+        dma::lds_load16(kbase + off, dma::lds_addr(st + 512 * t));
+        dma::lds_load16(vbase + off, dma::lds_addr(st + TILE + 512 * t));
+      }
     }
   };
   // Row reads (K, V rows 32 kb + l32, chunk 2 k + hi) and transposed reads
@@ -903,10 +941,14 @@ ma_status run(const BackwardArgs &a, const BwdParams &prm) {
   ma_status st = launch(bwd_prep<D>, (int)((rows + 3) / 4), 256, 0, prm, a.stream, "backward prep");
   if (st != MA_OK) return st;
   const size_t dq_lds = 2 * 2 * 64 * D * sizeof(uint16_t);
+  const bool fast = (1 << prm.page_shift) >= dma::KvDma<D, 2>::RPI && prm.s_page * 2 < ((int64_t)1 << 32) &&
+                    ((int64_t)1 << prm.page_shift) * prm.s_slot * 2 < ((int64_t)1 << 31);
   if (prm.tile_q == 128)
-    st = launch(bwd_dq<D, 128>, prm.num_items * a.hq, 256, dq_lds, prm, a.stream, "backward dQ");
+    st = fast ? launch(bwd_dq<D, 128, true>, prm.num_items * a.hq, 256, dq_lds, prm, a.stream, "backward dQ")
+              : launch(bwd_dq<D, 128, false>, prm.num_items * a.hq, 256, dq_lds, prm, a.stream, "backward dQ");
   else
-    st = launch(bwd_dq<D, 64>, prm.num_items * a.hq, 128, dq_lds, prm, a.stream, "backward dQ");
+    st = fast ? launch(bwd_dq<D, 64, true>, prm.num_items * a.hq, 128, dq_lds, prm, a.stream, "backward dQ")
+              : launch(bwd_dq<D, 64, false>, prm.num_items * a.hq, 128, dq_lds, prm, a.stream, "backward dQ");
   if (st != MA_OK) return st;
   if (prm.tile_q == 128)
     return launch(bwd_dkdv_wide<D>, prm.num_kitems * a.hkv, 256, QBlkW<D>::LDS, prm, a.stream, "backward dK dV");

@@ -161,8 +161,8 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
     auto pages_of = [&](int j) { return KV::pages_uniform(pt, p.page_shift, entry_kt(load_entry(p.entries, eb + j).kt_cls), kv_len, wave); };
     using IsK = std::integral_constant<bool, false>;
     using IsV = std::integral_constant<bool, true>;
-    const dma::LaneGather<D, C::NW, false> lgk(wave, lane, p.s_slot);
-    const dma::LaneGather<D, C::NW, true> lgv(wave, lane, p.s_slot);
+    const dma::LaneGather<D, C::NW, dma::SwzK<D>> lgk(wave, lane, p.s_slot);
+    const dma::LaneGather<D, C::NW, dma::SwzV<D>> lgv(wave, lane, p.s_slot);
     const uint32_t page_bytes = (uint32_t)(p.s_page * 2), slot_bytes = (uint32_t)(p.s_slot * 2);
     // log2 of the keys one wave gathers per matrix and tile (RPI * IPW)
     constexpr int kPageRunShift = __builtin_ctz(KV::RPI * KV::IPW);
@@ -172,19 +172,19 @@ __global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefil
       auto go = [&](auto clamp) {
         constexpr bool CL = decltype(clamp)::value;
         if constexpr (V)
-          dma::issue_mat_fast<D, C::NW, true, CL>(vbase, pg, lgv, p.page_shift, page_bytes, slot_bytes, kt, kv_len,
+          dma::issue_mat_fast<D, C::NW, dma::SwzV<D>, CL>(vbase, pg, lgv, p.page_shift, page_bytes, slot_bytes, kt, kv_len,
                                                   dst, wave, lane);
         else
-          dma::issue_mat_fast<D, C::NW, false, CL>(kbase, pg, lgk, p.page_shift, page_bytes, slot_bytes, kt, kv_len,
+          dma::issue_mat_fast<D, C::NW, dma::SwzK<D>, CL>(kbase, pg, lgk, p.page_shift, page_bytes, slot_bytes, kt, kv_len,
                                                    dst, wave, lane);
       };
       if (kt * 64 + 64 <= kv_len) {
         if (p.page_shift >= kPageRunShift) {
           if constexpr (V)
-            dma::issue_mat_page<D, C::NW, true>(vbase, pg.id[0], lgv, p.page_shift, page_bytes, slot_bytes, kt, dst,
+            dma::issue_mat_page<D, C::NW, dma::SwzV<D>>(vbase, pg.id[0], lgv, p.page_shift, page_bytes, slot_bytes, kt, dst,
                                                 wave);
           else
-            dma::issue_mat_page<D, C::NW, false>(kbase, pg.id[0], lgk, p.page_shift, page_bytes, slot_bytes, kt, dst,
+            dma::issue_mat_page<D, C::NW, dma::SwzK<D>>(kbase, pg.id[0], lgk, p.page_shift, page_bytes, slot_bytes, kt, dst,
                                                  wave);
         } else {
           go(std::integral_constant<bool, false>{});

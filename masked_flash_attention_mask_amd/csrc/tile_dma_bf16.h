@@ -159,7 +159,17 @@ __device__ __forceinline__ void issue_mat(const uint16_t *base, const typename K
 // inside the group and the swizzled chunk), computed once per kernel.  No
 // vector instruction per gather.  Needs page bytes (2 s_page) < 2^32 and page
 // ids >= 0.
-template <int D, int NW, bool IS_V>
+// Swz::f(r): the chunk swizzle of key row r in the destination layout.
+template <int D>
+struct SwzK {
+  __device__ static constexpr int f(int r) { return Stage<D>::fk(r); }
+};
+template <int D>
+struct SwzV {
+  __device__ static constexpr int f(int r) { return Stage<D>::fv(r); }
+};
+
+template <int D, int NW, typename Swz>
 struct LaneGather {
   static constexpr int CH = KvDma<D, NW>::CH, IPW = KvDma<D, NW>::IPW, RPI = KvDma<D, NW>::RPI;
   uint32_t off[IPW];
@@ -168,8 +178,7 @@ struct LaneGather {
     for (int i = 0; i < IPW; ++i) {
       const int t = wave * IPW + i;
       const int r = RPI * t + lane / CH, pc = lane % CH;
-      const int sw = IS_V ? Stage<D>::fv(r) : Stage<D>::fk(r);
-      off[i] = (uint32_t)((lane / CH) * (int)s_slot) * 2 + 16 * (pc ^ sw);
+      off[i] = (uint32_t)((lane / CH) * (int)s_slot) * 2 + 16 * (pc ^ Swz::f(r));
     }
   }
 };
@@ -180,9 +189,9 @@ struct LaneGather {
 // before the last key or lies wholly past it, when pages_uniform took the
 // last key's page), so only the lane's slot moves: by (clamped key -
 // unclamped key) slots, a few vector instructions on the last tile only.
-template <int D, int NW, bool IS_V, bool CLAMP>
+template <int D, int NW, typename Swz, bool CLAMP>
 __device__ __forceinline__ void issue_mat_fast(const uint16_t *base, const typename KvDma<D, NW>::Pages &pg,
-                                               const LaneGather<D, NW, IS_V> &lg, int page_shift,
+                                               const LaneGather<D, NW, Swz> &lg, int page_shift,
                                                uint32_t page_bytes, uint32_t slot_bytes, int kt, int kv_len,
                                                uint32_t dst, int wave, int lane) {
   constexpr int IPW = KvDma<D, NW>::IPW, RPI = KvDma<D, NW>::RPI, CH = KvDma<D, NW>::CH;
@@ -210,9 +219,9 @@ __device__ __forceinline__ void issue_mat_fast(const uint16_t *base, const typen
 // of RPI * IPW keys), so one page id and one scalar base serve all of them
 // and each further instruction adds a constant: two scalar adds and the M0
 // write per gather.
-template <int D, int NW, bool IS_V>
+template <int D, int NW, typename Swz>
 __device__ __forceinline__ void issue_mat_page(const uint16_t *base, int32_t page_id,
-                                               const LaneGather<D, NW, IS_V> &lg, int page_shift,
+                                               const LaneGather<D, NW, Swz> &lg, int page_shift,
                                                uint32_t page_bytes, uint32_t slot_bytes, int kt, uint32_t dst,
                                                int wave) {
   constexpr int IPW = KvDma<D, NW>::IPW, RPI = KvDma<D, NW>::RPI;

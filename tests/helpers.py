@@ -150,3 +150,28 @@ def fp8_bound(q_rows, k, v, mask_rows, scale, o_ref):
     o_bound = 6.0 * np.sqrt(var) / tot + 1e-3
     lse_bound = 1.05 * e.sum(axis=1) / tot[:, 0] + 1e-4
     return o_bound, lse_bound
+
+
+def repage(w, ps, seed):
+    """The same workload with its K/V laid out in pages of ps keys, in a
+    random page order (spare pages NaN)."""
+    import copy
+    c = copy.copy(w)
+    rng = np.random.default_rng(seed)
+    pages = [(int(k) + ps - 1) // ps for k in w.kv_lens]
+    total = sum(pages) + 2
+    perm = rng.permutation(total)
+    c.k_cache = np.full((total, ps) + w.k_cache.shape[2:], np.nan, np.float32)
+    c.v_cache = np.full_like(c.k_cache, np.nan)
+    c.page_table = np.full((len(pages), max(pages)), perm[-1], np.int32)
+    c.page_size = ps
+    off = 0
+    for b, kl in enumerate(w.kv_lens):
+        j = np.arange(int(kl))
+        src_p, src_s = w.page_table[b, j // w.page_size], j % w.page_size
+        dst = perm[off + j // ps]
+        c.k_cache[dst, j % ps] = w.k_cache[src_p, src_s]
+        c.v_cache[dst, j % ps] = w.v_cache[src_p, src_s]
+        c.page_table[b, :pages[b]] = perm[off:off + pages[b]]
+        off += pages[b]
+    return c

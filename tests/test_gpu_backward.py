@@ -8,7 +8,7 @@ import torch
 
 import masked_flash_attention_mask_amd as ma
 import workloads as W
-from helpers import TOL_GRAD, compile_plan, device_inputs, grad_err, oracle, oracle_masks, run_prefill
+from helpers import TOL_GRAD, compile_plan, device_inputs, grad_err, oracle, oracle_masks, repage, run_prefill
 from oracle import backward as OB
 
 pytestmark = pytest.mark.gpu
@@ -179,3 +179,34 @@ def test_backward_full_size_sampled():
             err = grad_err(torch.from_numpy(g), r)
             _say(what, "row metric", err)
             assert err <= TOL_GRAD, (h, what, err)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_page_sizes_bit_identical(d):
+    """Pages of 1 and 4 keys take the per-lane gather of the dQ pass, 16 the
+    per-instruction scalar base, 64 one base per wave; the page layout does not
+    enter the arithmetic, so dQ and every key's dK / dV are bit-identical."""
+    base, do, _ = _setup(d)
+    name = "ranges"
+    out, lse = _fwd_oracle(base, name)
+    res = {}
+    for ps in (1, 4, 16, 64):
+        w = base if ps == base.page_size else repage(base, ps, 900 + ps)
+        _say("backward page size", d, ps)
+        dev = device_inputs(w)
+        dev["do"] = torch.from_numpy(do).cuda().to(torch.bfloat16).contiguous()
+        dq, dk, dv = _bwd(w, dev, name, out, lse)
+        keys = []
+        dkc, dvc = dk.cpu().numpy(), dv.cpu().numpy()
+        for b, kl in enumerate(w.kv_lens):
+            j = np.arange(int(kl))
+            pg, sl = w.page_table[b, j // ps], j % ps
+            keys.append((dkc[pg, sl], dvc[pg, sl]))
+        res[ps] = (dq.cpu().numpy(), keys)
+    rq, rk, rv = _ref(base, do, name)
+    assert grad_err(torch.from_numpy(res[16][0]), rq) <= TOL_GRAD
+    for ps in (1, 4, 64):
+        assert np.array_equal(res[ps][0], res[16][0]), ("dq", ps)
+        for b in range(len(base.kv_lens)):
+            assert np.array_equal(res[ps][1][b][0], res[16][1][b][0]), ("dk", ps, b)
+            assert np.array_equal(res[ps][1][b][1], res[16][1][b][1]), ("dv", ps, b)

@@ -7,7 +7,7 @@ import torch
 
 import masked_flash_attention_mask_amd as ma
 import workloads as W
-from helpers import (TOL_BF16, TOL_F32, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle,
+from helpers import (TOL_BF16, TOL_F32, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle, repage,
                      run_prefill)
 
 pytestmark = pytest.mark.gpu
@@ -105,31 +105,6 @@ def test_bf16_ragged_kinds(d, tile_q):
     assert torch.all(out[200] == 0) and torch.all(torch.isneginf(lse[200]))
 
 
-def _repage(w, ps, seed):
-    """The same workload with its K/V laid out in pages of ps keys, in a
-    random page order (spare pages NaN)."""
-    import copy
-    c = copy.copy(w)
-    rng = np.random.default_rng(seed)
-    pages = [(int(k) + ps - 1) // ps for k in w.kv_lens]
-    total = sum(pages) + 2
-    perm = rng.permutation(total)
-    c.k_cache = np.full((total, ps) + w.k_cache.shape[2:], np.nan, np.float32)
-    c.v_cache = np.full_like(c.k_cache, np.nan)
-    c.page_table = np.full((len(pages), max(pages)), perm[-1], np.int32)
-    c.page_size = ps
-    off = 0
-    for b, kl in enumerate(w.kv_lens):
-        j = np.arange(int(kl))
-        src_p, src_s = w.page_table[b, j // w.page_size], j % w.page_size
-        dst = perm[off + j // ps]
-        c.k_cache[dst, j % ps] = w.k_cache[src_p, src_s]
-        c.v_cache[dst, j % ps] = w.v_cache[src_p, src_s]
-        c.page_table[b, :pages[b]] = perm[off:off + pages[b]]
-        off += pages[b]
-    return c
-
-
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_bf16_page_sizes_and_gather_modes(d):
     """Pages of 512 / d keys or more take the direct-to-LDS gather, smaller
@@ -139,7 +114,7 @@ def test_bf16_page_sizes_and_gather_modes(d):
     base.masks["prefix"] = W.MaskInput("prefix_lm", prefix_len=np.array([100, 7], np.int32))
     outs = {}
     for ps in (1, 2, 4, 8, 16, 64):
-        w = _repage(base, ps, 600 + ps)
+        w = repage(base, ps, 600 + ps)
         _say("page size", d, ps)
         outs[ps] = run_prefill(w, device_inputs(w), "prefix")[:2]
     ref_o, ref_l = oracle(base, "prefix")
