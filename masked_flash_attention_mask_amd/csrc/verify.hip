@@ -63,7 +63,7 @@ struct Shape {
 // a workgroup may have (8; 4 at d = 256, whose accumulators need a whole
 // SIMD's registers per wave).  Memory-bound decode loses nothing to the
 // padding rows of a wave.
-Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles) {
+Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles, bool positional = false) {
   const int group = hq / hkv;
   const int max_rows = 32 * (d == 256 ? 4 : 8);
   int gh = 1;
@@ -76,6 +76,10 @@ Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles) {
   // At d = 256 a workgroup keeps 4 waves even for a few rows: each wave's
   // share of the tile gather (addresses in registers) then stays small.
   int nw = d == 256 ? 4 : 1;
+  // Rows that fit one wave under a positional mask (decode): four waves share
+  // each tile's gather (the extra waves' rows are padding), which keeps more
+  // of it in flight per CU (measured -6% on 16 x 4k-16k decode).
+  if (positional && d <= 128 && need <= 1) nw = 4;
   while (nw < need) nw <<= 1;
   return Shape{gh, nw, split_shape(batch * (hq / gh), max_tiles)};
 }
@@ -411,7 +415,9 @@ size_t verify_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq
 
 ma_status launch_verify(const VerifyArgs &a) {
   const int mode = mode_of(a.mask_kind);
-  Shape sh = shape_for(a.batch, a.hq, a.hkv, a.d, a.max_q, max_walk_tiles(mode, a.window, a.max_q, a.max_kv));
+  const bool positional = mode == kCausal || mode == kWindow || mode == kPrefix;
+  Shape sh = shape_for(a.batch, a.hq, a.hkv, a.d, a.max_q, max_walk_tiles(mode, a.window, a.max_q, a.max_kv),
+                       positional);
   // Never more splits than the whole-context shape the workspace was sized for.
   const Shape full = shape_for(a.batch, a.hq, a.hkv, a.d, a.max_q, max_walk_tiles(kDense, 0, a.max_q, a.max_kv));
   if (sh.sp.max_splits > full.sp.max_splits) sh.sp = full.sp;
