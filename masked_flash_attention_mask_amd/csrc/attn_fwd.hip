@@ -104,8 +104,16 @@ __device__ __forceinline__ Entry load_entry(const Entry *e, int i) {
   return Entry{c[i].kt_cls, c[i].wblk};
 }
 
+// Waves per SIMD: 2, or 3 for the pipelined d = 64 kernel (168 registers;
+// its two spilled values are reloaded only after the loop), 1 for d = 256
+// and 64-row tiles.
+template <int D, int BQ, bool DMA>
+constexpr int prefill_occupancy() {
+  return D == 256 || BQ == 64 ? 1 : (D == 64 && DMA ? 3 : 2);
+}
+
 template <int D, int BQ, typename OutT, bool DMA>
-__global__ __launch_bounds__(BQ * 2, (D == 256 || BQ == 64 ? 1 : 2)) void prefill_bf16_kernel(PrefillParams p) {
+__global__ __launch_bounds__(BQ * 2, (prefill_occupancy<D, BQ, DMA>())) void prefill_bf16_kernel(PrefillParams p) {
   using C = Bf16Cfg<D, BQ, DMA>;
   extern __shared__ __align__(16) uint16_t lds[];
 
