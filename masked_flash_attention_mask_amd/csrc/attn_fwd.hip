@@ -267,11 +267,36 @@ __global__ __launch_bounds__(BQ * 2, (prefill_occupancy<D, BQ, DMA>())) void pre
     const dma::LaneOffsets<D> lo(lane);
     const uint32_t lds0 = dma::lds_addr(lds);
     typename KV::Pages pg_nxt;
+    [[maybe_unused]] const dma::LaneGather<D, C::NW, dma::SwzK<D>> lgk(wave, lane, p.s_slot);
+    [[maybe_unused]] const dma::LaneGather<D, C::NW, dma::SwzV<D>> lgv(wave, lane, p.s_slot);
+    [[maybe_unused]] const uint32_t page_bytes = (uint32_t)(p.s_page * 2), slot_bytes = (uint32_t)(p.s_slot * 2);
+    constexpr int kPageRunShift = __builtin_ctz(KV::RPI * KV::IPW);
+    auto issue_tile = [&](const typename KV::Pages &pg, int kt, uint32_t st) {
+      const uint32_t sv = st + 2u * dma::Stage<D>::V_OFF;
+      if constexpr (D > 128) {
+        // d = 256 keeps the per-lane form: the constant offsets' registers
+        // cost it more than the vector arithmetic they save (measured +3%)
+        KV::issue(kbase, vbase, pg, p.page_shift, p.s_page, p.s_slot, kt, kv_len, st, wave, lane);
+        return;
+      }
+      if (kt * 64 + 64 <= kv_len) {
+        if (p.page_shift >= kPageRunShift) {
+          dma::issue_mat_page<D, C::NW, dma::SwzK<D>>(kbase, pg.id[0], lgk, p.page_shift, page_bytes, slot_bytes, kt, st, wave);
+          dma::issue_mat_page<D, C::NW, dma::SwzV<D>>(vbase, pg.id[0], lgv, p.page_shift, page_bytes, slot_bytes, kt, sv, wave);
+        } else {
+          dma::issue_mat_fast<D, C::NW, dma::SwzK<D>, false>(kbase, pg, lgk, p.page_shift, page_bytes, slot_bytes, kt, kv_len, st, wave, lane);
+          dma::issue_mat_fast<D, C::NW, dma::SwzV<D>, false>(vbase, pg, lgv, p.page_shift, page_bytes, slot_bytes, kt, kv_len, sv, wave, lane);
+        }
+      } else {
+        dma::issue_mat_fast<D, C::NW, dma::SwzK<D>, true>(kbase, pg, lgk, p.page_shift, page_bytes, slot_bytes, kt, kv_len, st, wave, lane);
+        dma::issue_mat_fast<D, C::NW, dma::SwzV<D>, true>(vbase, pg, lgv, p.page_shift, page_bytes, slot_bytes, kt, kv_len, sv, wave, lane);
+      }
+    };
     if (eb < ee) {
       const Entry e0 = load_entry(p.entries, eb);
       const int kt0 = entry_kt(e0.kt_cls);
       const typename KV::Pages pg0 = KV::pages_uniform(pt, p.page_shift, kt0, kv_len, wave);
-      KV::issue(kbase, vbase, pg0, p.page_shift, p.s_page, p.s_slot, kt0, kv_len, lds0, wave, lane);
+      issue_tile(pg0, kt0, lds0);
       word_nxt = load_word(e0);
       if (eb + 1 < ee)
         pg_nxt = KV::pages_uniform(pt, p.page_shift, entry_kt(load_entry(p.entries, eb + 1).kt_cls), kv_len, wave);
@@ -284,8 +309,7 @@ __global__ __launch_bounds__(BQ * 2, (prefill_occupancy<D, BQ, DMA>())) void pre
       const uint64_t wcur = word_nxt;
       if (e + 1 < ee) {
         const Entry en = load_entry(p.entries, e + 1);
-        KV::issue(kbase, vbase, pg_nxt, p.page_shift, p.s_page, p.s_slot, entry_kt(en.kt_cls), kv_len,
-                  lds0 + (uint32_t)((cur ^ 1) * dma::Stage<D>::BYTES), wave, lane);
+        issue_tile(pg_nxt, entry_kt(en.kt_cls), lds0 + (uint32_t)((cur ^ 1) * dma::Stage<D>::BYTES));
         word_nxt = load_word(en);
         if (e + 2 < ee)
           pg_nxt = KV::pages_uniform(pt, p.page_shift, entry_kt(load_entry(p.entries, e + 2).kt_cls), kv_len, wave);

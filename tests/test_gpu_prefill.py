@@ -107,21 +107,24 @@ def test_bf16_ragged_kinds(d, tile_q):
 
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_bf16_page_sizes_and_gather_modes(d):
-    """Pages of 512 / d keys or more take the direct-to-LDS gather, smaller
-    ones the register-staged gather.  Page layout does not enter the
-    arithmetic, so every page size gives bit-identical outputs."""
+    """Pages of 512 / d keys or more take the direct-to-LDS gather (one page
+    id per instruction, or per wave once pages hold a wave's whole run of
+    keys), smaller ones the register-staged gather; both tile heights.  Page
+    layout does not enter the arithmetic, so every page size gives
+    bit-identical outputs."""
     base = _ragged(500 + d, d, 4, 2, [150, 77], [230, 77])
     base.masks["prefix"] = W.MaskInput("prefix_lm", prefix_len=np.array([100, 7], np.int32))
-    outs = {}
-    for ps in (1, 2, 4, 8, 16, 64):
-        w = repage(base, ps, 600 + ps)
-        _say("page size", d, ps)
-        outs[ps] = run_prefill(w, device_inputs(w), "prefix")[:2]
     ref_o, ref_l = oracle(base, "prefix")
-    assert max_abs_err(outs[1][0], ref_o) <= TOL_BF16
-    assert lse_err(outs[1][1], ref_l) <= 1e-2
-    for ps in (2, 4, 8, 16, 64):
-        assert torch.equal(outs[ps][0], outs[1][0]) and torch.equal(outs[ps][1], outs[1][1]), ps
+    for tq in (128, 64):
+        outs = {}
+        for ps in (1, 2, 4, 8, 16, 64):
+            w = repage(base, ps, 600 + ps)
+            _say("page size", d, tq, ps)
+            outs[ps] = run_prefill(w, device_inputs(w), "prefix", tile_q=tq)[:2]
+        assert max_abs_err(outs[1][0], ref_o) <= TOL_BF16
+        assert lse_err(outs[1][1], ref_l) <= 1e-2
+        for ps in (2, 4, 8, 16, 64):
+            assert torch.equal(outs[ps][0], outs[1][0]) and torch.equal(outs[ps][1], outs[1][1]), (tq, ps)
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
