@@ -45,9 +45,9 @@ struct SplitShape {
 
 // Splits of a walk of at most max_tiles k-tiles so that about
 // kTargetWorkgroups workgroups run.
-SplitShape split_shape(int units, int max_tiles) {
+SplitShape split_shape(int units, int max_tiles, int target = kTargetWorkgroups) {
   if (max_tiles < 1) return SplitShape{1, 1};
-  int want = (kTargetWorkgroups + units - 1) / units;
+  int want = (target + units - 1) / units;
   want = want < 1 ? 1 : (want > max_tiles ? max_tiles : want);
   const int t = (max_tiles + want - 1) / want;
   return SplitShape{t, (max_tiles + t - 1) / t};
@@ -81,7 +81,9 @@ Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles, boo
   // of it in flight per CU (measured -6% on 16 x 4k-16k decode).
   if (positional && d <= 128 && need <= 1) nw = 4;
   while (nw < need) nw <<= 1;
-  return Shape{gh, nw, split_shape(batch * (hq / gh), max_tiles)};
+  // Eight-wave workgroups run one per CU: aim for one round of them (the
+  // split partials cost a write and a read per split).
+  return Shape{gh, nw, split_shape(batch * (hq / gh), max_tiles, nw >= 8 ? 256 : kTargetWorkgroups)};
 }
 
 // Tiles a sequence's walk can need: all of them, or for a sliding window the
@@ -321,7 +323,8 @@ __global__ __launch_bounds__(256) void verify_combine(VerifyParams p) {
   const int nsplit = (ntiles + p.tiles_per_split - 1) / p.tiles_per_split;
   if (nsplit <= 1) return;
   const int64_t sbase = (int64_t)b * p.max_splits;
-  for (int idx = threadIdx.x; idx < q_len * (D / 4); idx += blockDim.x) {
+  // one (row, 4 columns) item per thread; blockIdx.z picks the chunk of items
+  for (int idx = blockIdx.z * blockDim.x + threadIdx.x; idx < q_len * (D / 4); idx += blockDim.x * gridDim.z) {
     const int t = idx / (D / 4), c4 = idx % (D / 4);
     float mx = neg_inf();
     for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, p.ws_lse[((sbase + s) * p.hq + h) * p.qs + t]);
@@ -360,7 +363,8 @@ ma_status run(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh) {
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify launch: %s", hipGetErrorString(e));
   if (sh.sp.max_splits > 1) {
-    hipLaunchKernelGGL((verify_combine<D, OutT>), dim3(a.hq, a.batch), dim3(256), 0, s, prm);
+    const int chunks = (a.max_q * (D / 4) + 255) / 256;
+    hipLaunchKernelGGL((verify_combine<D, OutT>), dim3(a.hq, a.batch, chunks), dim3(256), 0, s, prm);
     e = hipGetLastError();
     if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify combine launch: %s", hipGetErrorString(e));
   }
