@@ -129,19 +129,40 @@ __device__ __forceinline__ void lds_load4_s(gptr_t base, uint32_t voff, uint32_t
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep(BwdParams p) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (token, head)
-  const int lane = threadIdx.x & 63;
-  if (row >= p.total_q * p.hq) return;
+  // D / 8 lanes per (token, head) row, 8 elements (16 bytes of dO) per lane;
+  // 256 / (D / 8) rows per workgroup
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int c = (threadIdx.x % LPR) * 8;
   float acc = 0.f;
-  for (int c = lane; c < D; c += 64) {
-    const float o = p.o_f32 ? ((const float *)p.o)[row * D + c]
-                            : __uint_as_float((uint32_t)((const uint16_t *)p.o)[row * D + c] << 16);
-    const float g = __uint_as_float((uint32_t)p.dout[row * D + c] << 16);
-    acc += o * g;
+  if (row < p.total_q * p.hq) {
+    const u32x4 g = *(const u32x4 *)(p.dout + row * D + c);
+    float o[8];
+    if (p.o_f32) {
+      const f32x4 a = *(const f32x4 *)((const float *)p.o + row * D + c);
+      const f32x4 b = *(const f32x4 *)((const float *)p.o + row * D + c + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[i] = a[i];
+        o[4 + i] = b[i];
+      }
+    } else {
+      const u32x4 ob = *(const u32x4 *)((const uint16_t *)p.o + row * D + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(ob[i] << 16);
+        o[2 * i + 1] = __uint_as_float(ob[i] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc += o[2 * i] * __uint_as_float(g[i] << 16);
+      acc += o[2 * i + 1] * __uint_as_float(g[i] & 0xFFFF0000u);
+    }
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) {
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (row < p.total_q * p.hq && threadIdx.x % LPR == 0) {
     p.dd[row] = acc;
     const float lse = p.lse[row];
     p.l2[row] = lse == neg_inf() ? __builtin_inff() : lse * kLog2e;
@@ -938,7 +959,9 @@ ma_status launch(K kern, int grid, int block, size_t lds, const BwdParams &prm, 
 template <int D>
 ma_status run(const BackwardArgs &a, const BwdParams &prm) {
   const int64_t rows = a.total_q * a.hq;
-  ma_status st = launch(bwd_prep<D>, (int)((rows + 3) / 4), 256, 0, prm, a.stream, "backward prep");
+  constexpr int prep_rows = 256 / (D / 8);
+  ma_status st = launch(bwd_prep<D>, (int)((rows + prep_rows - 1) / prep_rows), 256, 0, prm, a.stream,
+                        "backward prep");
   if (st != MA_OK) return st;
   const size_t dq_lds = 2 * 2 * 64 * D * sizeof(uint16_t);
   const bool fast = (1 << prm.page_shift) >= dma::KvDma<D, 2>::RPI && prm.s_page * 2 < ((int64_t)1 << 32) &&
