@@ -9,7 +9,7 @@ import torch
 
 import masked_flash_attention_mask_amd as ma
 import workloads as W
-from helpers import compile_plan, fp8_bound, fp8_dequantized, oracle, oracle_masks
+from helpers import compile_plan, fp8_bound, fp8_dequantized, oracle, oracle_masks, repage
 from oracle import attention as OA
 
 pytestmark = pytest.mark.gpu
@@ -120,3 +120,26 @@ def test_fp8_full_size_sampled():
     rows = {0: np.array([0, 1, 127, 128, 1023, 1024, 1025, 5000, 8191, n - 2, n - 1])}
     worst = _check(w, wd, "chunk2", out, lse, heads=[0, 11], rows=rows)
     _say("worst err / bound", worst)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_page_sizes_bit_identical(d):
+    """Pages of the minimum size (one gather instruction's rows: 8 keys at
+    d 128, 16 at d 64), 16, 32 and 64 keys (one page per wave's run from 16
+    keys on): the page layout does not enter the arithmetic, so the outputs
+    are bit-identical; the first is also held to the oracle bound."""
+    base = W.backward_small(seed=97 + d, d=d, hq=4, hkv=2)
+    f8 = W.fp8_inputs(base)
+    name = "ranges"
+    outs = {}
+    for ps in (1024 // d, 16, 32, 64):
+        w = base if ps == base.page_size else repage(base, ps, 700 + ps)
+        g8 = W.fp8_inputs(w)
+        assert g8["k_s"] == f8["k_s"] and g8["v_s"] == f8["v_s"]   # same values, other layout
+        _say("fp8 page size", d, ps)
+        out, lse = _run(w, g8, _dev8(w, g8), name)
+        outs[ps] = (out.cpu(), lse.cpu())
+    first = 1024 // d
+    for ps in outs:
+        assert torch.equal(outs[ps][0], outs[first][0]) and torch.equal(outs[ps][1], outs[first][1]), ps
+    _check(base, fp8_dequantized(base, f8), name, outs[16][0], outs[16][1])
