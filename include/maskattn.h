@@ -337,6 +337,29 @@ ma_status attn_decode(const void *q, int64_t total_q, int32_t hq, const void *k_
                       int32_t in_dtype, int32_t out_dtype, float scale, void *workspace,
                       size_t ws_bytes, void *out, float *lse, void *stream);
 
+/* attn_decode over e4m3 (fp8) K/V caches (flashinfer issue 724, the
+ * fp8 question after its benchmark table, for the decode side: the cache is
+ * the bytes decode reads).  k_cache / v_cache hold OCP e4m3 bytes in the
+ * layout of attn_decode (strides in elements = bytes); the attention is that
+ * of attn_decode with K = k_descale * decode(K8) and V = v_descale *
+ * decode(V8) and bf16 queries.  The kernel widens each gathered tile exactly
+ * to bf16 in LDS and runs the bf16 products; the descale factors enter the
+ * softmax constant and the normalisation, so the result equals attn_decode
+ * on the exactly decoded caches (up to the same fp32 summation order).
+ * Mask kinds, lengths, splits and workspace (attn_decode_workspace) as for
+ * attn_decode.  Requires d in {64, 128, 256}, pages of at least 1024 / d
+ * keys, page_size * slot stride below 2^31 and the page stride below 2^32
+ * (bytes).  Errors as attn_decode, plus INVALID for descale factors that are
+ * not positive and finite, UNSUPPORTED for small or too large pages. */
+ma_status attn_decode_kv8(const void *q, int64_t total_q, int32_t hq, const void *k_cache,
+                          const void *v_cache, int32_t hkv, int32_t d, int32_t page_size,
+                          const int64_t kv_strides[3], const int32_t *page_table, int32_t max_pages,
+                          const int32_t *cu_seqlens_q, const int32_t *kv_lens, int32_t batch,
+                          int32_t max_q, int32_t max_kv, int32_t mask_kind, int32_t window,
+                          const int32_t *prefix_len, const void *mask, int64_t mask_numel,
+                          int32_t out_dtype, float scale, float k_descale, float v_descale,
+                          void *workspace, size_t ws_bytes, void *out, float *lse, void *stream);
+
 const char *ma_status_string(int32_t status);
 const char *ma_last_error(void);
 

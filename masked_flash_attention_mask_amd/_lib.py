@@ -24,7 +24,7 @@ TILE_SKIP, TILE_FULL, TILE_PARTIAL = 0, 1, 2
 EXPORTS = ["mask_compile", "mask_compile_host", "mask_plan_upload", "mask_plan_destroy",
            "mask_plan_info_get", "mask_plan_export", "mask_plan_serialize", "attn_prefill_masked",
            "attn_prefill_masked_fp8", "attn_backward_workspace", "attn_backward_masked", "attn_verify_tree_workspace", "attn_verify_tree",
-           "attn_decode_workspace", "attn_decode",
+           "attn_decode_workspace", "attn_decode", "attn_decode_kv8",
            "ma_status_string", "ma_last_error"]
 
 
@@ -83,6 +83,8 @@ def _load():
         "attn_decode_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
         "attn_decode": (i32, [vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                               vp, vp, i64, i32, i32, f32, vp, sz, vp, vp, vp]),
+        "attn_decode_kv8": (i32, [vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32,
+                                  i32, vp, vp, i64, i32, f32, f32, f32, vp, sz, vp, vp, vp]),
         "ma_status_string": (ctypes.c_char_p, [i32]),
         "ma_last_error": (ctypes.c_char_p, []),
     }
@@ -408,4 +410,43 @@ def attn_decode(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, max_q, m
         _dtype_code(q.dtype), _dtype_code(out.dtype), float(scale), ws_ptr, ws_bytes, out.data_ptr(),
         lse.data_ptr() if lse is not False else None, _stream(stream))
     check(st, "attn_decode")
+    return out, lse
+
+
+def attn_decode_kv8(q, k8_cache, v8_cache, page_table, cu_seqlens_q, kv_lens, max_q, max_kv, scale, k_descale,
+                    v_descale, mask_kind="causal", window=0, prefix_len=None, mask=None, workspace=None, out=None,
+                    lse=None, out_dtype=None, stream=None):
+    """attn_decode with e4m3 K/V caches (uint8 tensors of the cache shape,
+    K = k_descale * decode(K8), likewise V) and bf16 queries."""
+    import torch
+    total_q, hq, d = q.shape
+    hkv, page_size = k8_cache.shape[2], k8_cache.shape[1]
+    batch = kv_lens.shape[0]
+    if k8_cache.dtype != torch.uint8 or v8_cache.dtype != torch.uint8:
+        raise ValueError("fp8 caches must be uint8 tensors of e4m3 bytes")
+    strides = _cache_args(k8_cache, v8_cache)
+    for t in (q, page_table, cu_seqlens_q, kv_lens) + tuple(x for x in (mask, prefix_len) if x is not None):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("decode tensors must be contiguous device tensors")
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((total_q, hq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_workspace(batch, max_q, max_kv, hq, hkv, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    kind = {"window": KIND["window"], "sliding_window": KIND["window"]}.get(mask_kind, KIND.get(mask_kind))
+    if kind is None:
+        raise ValueError(f"unknown mask kind {mask_kind!r}")
+    st = LIB.attn_decode_kv8(
+        q.data_ptr(), total_q, hq, k8_cache.data_ptr(), v8_cache.data_ptr(), hkv, d, page_size, strides,
+        page_table.data_ptr(), page_table.shape[1], cu_seqlens_q.data_ptr(), kv_lens.data_ptr(), batch,
+        int(max_q), int(max_kv), kind, int(window), prefix_len.data_ptr() if prefix_len is not None else None,
+        mask.data_ptr() if mask is not None else None, mask.numel() if mask is not None else 0,
+        _dtype_code(out.dtype), float(scale), float(k_descale), float(v_descale), ws_ptr, ws_bytes,
+        out.data_ptr(), lse.data_ptr() if lse is not False else None, _stream(stream))
+    check(st, "attn_decode_kv8")
     return out, lse

@@ -427,7 +427,7 @@ static ma_status run_small_q(const void *q, int32_t hq, const void *k_cache, con
                              int32_t batch, int32_t max_q, int32_t max_kv, int32_t mask_kind, int32_t window,
                              const int32_t *prefix_len, const void *mask, int64_t mask_numel, int32_t out_dtype,
                              float scale, void *workspace, size_t ws_bytes, void *out, float *lse,
-                             void *stream) {
+                             void *stream, int32_t kv8 = 0, float k_descale = 1.f, float v_descale = 1.f) {
   const size_t need = verify_workspace(batch, max_q, max_kv, hq, hkv, d);
   if (need > 0 && (!workspace || ws_bytes < need))
     return set_error(MA_ERR_SIZE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
@@ -461,6 +461,9 @@ static ma_status run_small_q(const void *q, int32_t hq, const void *k_cache, con
   a.out = out;
   a.lse = lse;
   a.stream = stream;
+  a.kv8 = kv8;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
   return launch_verify(a);
 }
 
@@ -501,6 +504,46 @@ ma_status attn_decode(const void *q, int64_t total_q, int32_t hq, const void *k_
   return run_small_q(q, hq, k_cache, v_cache, hkv, d, page_size, kv_strides, page_table, max_pages, cu_seqlens_q,
                      kv_lens, batch, max_q, max_kv, mask_kind, window, prefix_len, mask, mask_numel, out_dtype,
                      scale, workspace, ws_bytes, out, lse, stream);
+}
+
+ma_status attn_decode_kv8(const void *q, int64_t total_q, int32_t hq, const void *k_cache, const void *v_cache,
+                          int32_t hkv, int32_t d, int32_t page_size, const int64_t kv_strides[3],
+                          const int32_t *page_table, int32_t max_pages, const int32_t *cu_seqlens_q,
+                          const int32_t *kv_lens, int32_t batch, int32_t max_q, int32_t max_kv, int32_t mask_kind,
+                          int32_t window, const int32_t *prefix_len, const void *mask, int64_t mask_numel,
+                          int32_t out_dtype, float scale, float k_descale, float v_descale, void *workspace,
+                          size_t ws_bytes, void *out, float *lse, void *stream) {
+  clear_error();
+  ma_status st = check_small_q(q, k_cache, v_cache, out, page_table, hq, hkv, page_size, kv_strides, max_pages,
+                               scale, cu_seqlens_q, kv_lens, batch, max_q, max_kv, MA_BF16, out_dtype, d, total_q);
+  if (st != MA_OK) return st;
+  if (!(k_descale > 0.f) || !(v_descale > 0.f) || !std::isfinite(k_descale) || !std::isfinite(v_descale))
+    return set_error(MA_ERR_INVALID, "descale factors must be positive and finite");
+  if (page_size < 1024 / d)
+    return set_error(MA_ERR_UNSUPPORTED, "fp8 caches need pages of at least %d keys at head_dim %d", 1024 / d, d);
+  if ((int64_t)page_size * kv_strides[1] >= ((int64_t)1 << 31) || kv_strides[0] >= ((int64_t)1 << 32))
+    return set_error(MA_ERR_UNSUPPORTED, "a page's bytes exceed a 32-bit offset");
+  switch (mask_kind) {
+    case MA_KIND_CAUSAL:
+      break;
+    case MA_KIND_SLIDING_WINDOW:
+      if (window < 1) return set_error(MA_ERR_INVALID, "window must be >= 1 (got %d)", window);
+      break;
+    case MA_KIND_PREFIX_LM:
+      if (!prefix_len) return set_error(MA_ERR_INVALID, "prefix_len is required for PREFIX_LM");
+      break;
+    case MA_KIND_DENSE_BOOL:
+    case MA_KIND_PACKED_U64:
+      if (!mask || mask_numel < 1) return set_error(MA_ERR_INVALID, "mask is required");
+      break;
+    case MA_KIND_RANGES:
+      return set_error(MA_ERR_UNSUPPORTED, "decode takes RANGES masks as dense or packed rows");
+    default:
+      return set_error(MA_ERR_INVALID, "mask kind %d", mask_kind);
+  }
+  return run_small_q(q, hq, k_cache, v_cache, hkv, d, page_size, kv_strides, page_table, max_pages, cu_seqlens_q,
+                     kv_lens, batch, max_q, max_kv, mask_kind, window, prefix_len, mask, mask_numel, out_dtype,
+                     scale, workspace, ws_bytes, out, lse, stream, 1, k_descale, v_descale);
 }
 
 ma_status attn_verify_tree(const void *q, int64_t total_q, int32_t hq, const void *k_cache,

@@ -174,6 +174,8 @@ struct VerifyArgs {
   void *out;
   float *lse;
   void *stream;
+  int32_t kv8;                 // 1: k / v hold e4m3 bytes, scaled by k_descale / v_descale
+  float k_descale, v_descale;
 };
 size_t verify_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq, int32_t hkv,
                         int32_t d);

@@ -111,7 +111,8 @@ struct VerifyParams {
   int32_t hq, group, gh, qs;
   int32_t mode, window;
   int32_t tiles_per_split, max_splits, max_kv;
-  float scale, scale_log2;
+  float scale, scale_log2;   // scale_log2 includes the K descale factor (fp8 caches)
+  float v_scale;             // V descale factor (fp8 caches; 1 otherwise)
 };
 
 __device__ __forceinline__ int64_t mask_offset(const VerifyParams &p, int b) {
@@ -201,7 +202,12 @@ __device__ __forceinline__ uint64_t fetch_word(const VerifyParams &p, int64_t mo
 // UP: pages hold at least the key rows of one gather instruction, so page
 // ids are scalar loads (uniform per instruction) instead of one vector load
 // per lane and instruction.
-template <int D, int NW, typename OutT, bool UP>
+// KV8: the caches hold e4m3 bytes (K = k_descale * decode(K8), likewise V).
+// Each tile's bytes are gathered into an fp8 stage (two, one tile ahead),
+// widened exactly to bf16 into the swizzled bf16 stage by all threads, and
+// from there the bf16 products run unchanged; the descale factors fold into
+// the softmax constant and the epilogue.
+template <int D, int NW, typename OutT, bool UP, bool KV8 = false>
 __global__ __launch_bounds__(NW * 64, 1) void verify_kernel(VerifyParams p) {
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -251,6 +257,86 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_kernel(VerifyParams p) {
   float lsum = 0.f;   // this lane's half of its row sum
   const float c = p.scale_log2;
 
+  if constexpr (KV8) {
+    constexpr int CH8 = D / 16;        // 16-byte chunks of an fp8 row
+    constexpr int T8 = D / 16;         // 1 KB gather instructions per matrix and tile
+    constexpr int RPI8 = 1024 / D;     // key rows per gather instruction
+    constexpr uint32_t F8 = 2u * 64 * D;   // bytes of one fp8 stage (K, then V)
+    constexpr uint32_t BF = 2u * F8;       // byte offset of the bf16 stage
+    uint8_t *l8 = (uint8_t *)lds;
+    const int pmask = (1 << p.page_shift) - 1;
+    const __attribute__((address_space(4))) int32_t *cpt = (const __attribute__((address_space(4))) int32_t *)pt;
+    const uint8_t *k8 = (const uint8_t *)p.k + (int64_t)g * p.s_head;
+    const uint8_t *v8 = (const uint8_t *)p.v + (int64_t)g * p.s_head;
+    // Instruction t of a matrix fills LDS chunks [64 t, 64 t + 64) of the
+    // plain row-major [64][D] byte tile; its RPI8 rows lie in one page (the
+    // host requires pages of at least RPI8 keys), keys past kv_len repeat the
+    // last key (same page as the group's first row, or the last key's page).
+    auto gather8 = [&](int kt, int st) {
+      for (int t8 = wave; t8 < T8; t8 += NW) {
+        const int key0 = min(kt * 64 + RPI8 * t8, kv - 1);
+        const int32_t pg = cpt[key0 >> p.page_shift];
+        const int r = RPI8 * t8 + lane / CH8, pc = lane % CH8;
+        const int key = min(kt * 64 + r, kv - 1);
+        const uint32_t off = (uint32_t)((key & pmask) * (int)p.s_slot) + 16 * pc;
+        const uint64_t pb = (uint64_t)(uint32_t)pg * (uint64_t)p.s_page;
+        dma::lds_load16_s((dma::gptr_t)(k8 + pb), off, lds0 + (uint32_t)st * F8 + 1024 * t8);
+        dma::lds_load16_s((dma::gptr_t)(v8 + pb), off, lds0 + (uint32_t)st * F8 + 64 * D + 1024 * t8);
+      }
+    };
+    // fp8 stage st -> bf16 stage: 16 bytes in, two swizzled 8-element chunks out
+    auto widen = [&](int st) {
+      constexpr int NCH = 2 * 64 * CH8;
+      for (int q = tid; q < NCH; q += NW * 64) {
+        const int m = q / (64 * CH8), qq = q - m * (64 * CH8);
+        const int r = qq / CH8, c16 = qq - r * CH8;
+        const u32x4 x = *(const u32x4 *)(l8 + (uint32_t)st * F8 + m * 64 * D + 16 * qq);
+        u32x4 y[2];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          y[w >> 1][2 * (w & 1)] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, false));
+          y[w >> 1][2 * (w & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, true));
+        }
+        const int f = m == 0 ? Stage<D>::fk(r) : Stage<D>::fv(r);
+        uint16_t *dst = (uint16_t *)(l8 + BF) + m * Stage<D>::V_OFF + r * D;
+        *(u32x4 *)(dst + 8 * ((2 * c16) ^ f)) = y[0];
+        *(u32x4 *)(dst + 8 * ((2 * c16 + 1) ^ f)) = y[1];
+      }
+    };
+    uint64_t word_nxt = 0;
+    if (kt0 < kt1) {
+      gather8(kt0, 0);
+      word_nxt = fetch_word(p, moff, plen, t, row_ok, r0, q_len, kv, kt0, lane);
+    }
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int cur = (kt - kt0) & 1;
+      wait_vmem();
+      __syncthreads();   // fp8 tile kt landed; every wave is done with the bf16 stage
+      const uint64_t wcur = word_nxt;
+      if (kt + 1 < kt1) {
+        // the mask word first (a dense mask's ballots wait for its loads)
+        word_nxt = fetch_word(p, moff, plen, t, row_ok, r0, q_len, kv, kt + 1, lane);
+        gather8(kt + 1, cur ^ 1);
+      }
+      widen(cur);
+      __syncthreads();
+      const uint16_t *stage = (const uint16_t *)(l8 + BF);
+      f32x16 sacc[2];
+      qk_tile<D>(stage, lo, qf, sacc);
+      const int kin = kv - 64 * kt;
+      const uint64_t inb = low_bits(kin);
+      const uint64_t w = wcur & inb;
+      if (kin < 64 || __ballot(row_ok && w != inb) != 0ull) apply_word(sacc, w, hi);
+      float alpha;
+      if (softmax_tile(sacc, m_ref, c, alpha)) {
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+        lsum *= alpha;
+      }
+      pv_tile<D>(stage, lo, sacc, oacc, lsum);
+    }
+  } else {
   uint64_t word_nxt = 0;
   if (kt0 < kt1) {
     const typename KV::Pages pg0 = pages(kt0);
@@ -297,9 +383,10 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_kernel(VerifyParams p) {
     wait_vmem();
     __syncthreads();
   }
+  }
 
   const float lt = sum_halves(lsum);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float inv = lt > 0.f ? p.v_scale / lt : 0.f;
   const float lse = lt > 0.f ? (m_ref + __log2f(lt)) * kLn2 : neg_inf();
   if (!row_ok) return;
   if (nsplit <= 1) {
@@ -349,12 +436,18 @@ __global__ __launch_bounds__(256) void verify_combine(VerifyParams p) {
 
 template <int D, int NW, typename OutT>
 ma_status run(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh) {
-  const size_t lds = 2 * Stage<D>::BYTES;
+  size_t lds = 2 * Stage<D>::BYTES;
   // Uniform pages: the rows of one gather instruction share a page whose
   // bytes a 32-bit offset reaches.
   const bool up = (1 << a.page_shift) >= KvDma<D, NW>::RPI &&
                   ((int64_t)1 << a.page_shift) * a.s_slot * 2 < ((int64_t)1 << 31);
   auto kern = up ? verify_kernel<D, NW, OutT, true> : verify_kernel<D, NW, OutT, false>;
+  if (a.kv8) {
+    // two fp8 stages (K, V bytes) and one bf16 stage; the host checked the
+    // page size (at least 1024 / d keys) and the 32-bit offsets
+    kern = verify_kernel<D, NW, OutT, true, true>;
+    lds = 2 * (2 * 64 * D) + Stage<D>::BYTES;
+  }
   hipError_t e = hipSuccess;
   if (lds > 64 * 1024) e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
@@ -454,7 +547,8 @@ ma_status launch_verify(const VerifyArgs &a) {
   prm.max_splits = sh.sp.max_splits;
   prm.max_kv = a.max_kv;
   prm.scale = a.scale;
-  prm.scale_log2 = a.scale * kLog2e;
+  prm.scale_log2 = a.scale * (a.kv8 ? a.k_descale : 1.f) * kLog2e;
+  prm.v_scale = a.kv8 ? a.v_descale : 1.f;
   switch (a.d) {
     case 64: return run_d<64>(a, prm, sh);
     case 128: return run_d<128>(a, prm, sh);

@@ -137,6 +137,29 @@ def test_decode_validation_before_hip():
     assert ma.attn_verify_tree_workspace(2, 64, 4000, 4, 1, 128) >= need
 
 
+def _decode8(kind=L.KIND["causal"], window=0, ks=1.0, vs=1.0, page=16, d=128, ws=None, ws_bytes=0,
+             strides=(2048, 128, 128)):
+    st = (ctypes.c_int64 * 3)(*strides)
+    maxp = (4000 + page - 1) // page
+    return L.LIB.attn_decode_kv8(FAKE, 2, 4, FAKE, FAKE, 1, d, page, st, FAKE, maxp, FAKE, FAKE, 2, 1, 4000, kind,
+                                 window, None, None, 0, L.F32, 0.1, ks, vs, ws, ws_bytes, FAKE, None, None)
+
+
+def test_decode_kv8_validation_before_hip():
+    need = ma.attn_decode_workspace(2, 1, 4000, 4, 1, 128)
+    ok = dict(ws=FAKE, ws_bytes=need)
+    assert _decode8(ks=0.0, **ok) == L.MA_ERR_INVALID
+    assert _decode8(vs=-1.0, **ok) == L.MA_ERR_INVALID
+    assert _decode8(ks=float("inf"), **ok) == L.MA_ERR_INVALID
+    assert _decode8(vs=float("nan"), **ok) == L.MA_ERR_INVALID
+    assert _decode8(page=4, **ok) == L.MA_ERR_UNSUPPORTED          # fewer than 1024 / d keys per page
+    assert _decode8(d=64, page=8, **ok) == L.MA_ERR_UNSUPPORTED
+    assert _decode8(strides=(1 << 32, 128, 128), **ok) == L.MA_ERR_UNSUPPORTED
+    assert _decode8(kind=L.KIND["window"], window=0, **ok) == L.MA_ERR_INVALID
+    assert _decode8(kind=L.KIND["ranges"], **ok) == L.MA_ERR_UNSUPPORTED
+    assert _decode8(ws=FAKE, ws_bytes=need - 1) == L.MA_ERR_SIZE
+
+
 def _backward(plan, d=128, out_dt=L.BF16, total_q=8, ws=FAKE, ws_bytes=1 << 20, dout=FAKE, lse=FAKE, maxp=300):
     st = (ctypes.c_int64 * 3)(2048, 128, 128)
     return L.LIB.attn_backward_masked(plan.handle if plan else None, FAKE, total_q, 4, FAKE, FAKE, 1, d, 16, st,
