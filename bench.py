@@ -350,6 +350,25 @@ def decode_lines(steps, warmup):
             print(json.dumps({"workload": f"decode_q{q_len}", "mask": name, "ms": round(ms, 4),
                               "kv_gbs": round(gbs, 1), "pct_of_hbm": round(100 * gbs / 8000.0, 1),
                               "batch": w.batch, "kv_total": int(w.kv_lens.sum())}), flush=True)
+        if q_len == 1:
+            # the same batch over e4m3 caches (half the bytes per key)
+            f8 = W.fp8_inputs(w)
+            k8 = torch.from_numpy(np.ascontiguousarray(f8["k8"])).cuda()
+            v8 = torch.from_numpy(np.ascontiguousarray(f8["v8"])).cuda()
+            for name in ("causal", "window"):
+                win = w.masks[name].window if name == "window" else 0
+
+                def step8():
+                    ma.attn_decode_kv8(dev["q"], k8, v8, dev["pt"], dev["cu"], dev["kv"], q_len, max_kv, w.scale,
+                                       f8["k_s"], f8["v_s"], mask_kind=name, window=win, workspace=ws, out=out,
+                                       lse=lse)
+                ms = time_steps(step8, steps, warmup, torch.cuda.current_stream())
+                keys = [int(k) if name == "causal" else min(int(k), win + q_len - 1) for k in w.kv_lens]
+                kv_bytes = 2 * sum(keys) * w.hkv * w.d
+                gbs = kv_bytes / (ms * 1e-3) / 1e9
+                print(json.dumps({"workload": "decode_q1_kv8", "mask": name, "ms": round(ms, 4),
+                                  "kv_gbs": round(gbs, 1), "pct_of_hbm": round(100 * gbs / 8000.0, 1),
+                                  "batch": w.batch, "kv_total": int(w.kv_lens.sum())}), flush=True)
         del dev
 
 
