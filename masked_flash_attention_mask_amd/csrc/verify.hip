@@ -57,13 +57,17 @@ struct Shape {
   int gh;      // query heads per workgroup
   int nw;      // waves per workgroup (1, 2, 4 or 8)
   SplitShape sp;
+  bool waves_split = false;   // decode: the waves take the split's tiles in turn
 };
 
 // The largest GH dividing the GQA group whose GH x max_q rows fit the waves
 // a workgroup may have (8; 4 at d = 256, whose accumulators need a whole
 // SIMD's registers per wave).  Memory-bound decode loses nothing to the
 // padding rows of a wave.
-Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles, bool positional = false) {
+// waves_ok: the wave-split decode kernel may run (bf16 caches whose pages
+// hold whole gather instructions).
+Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles, bool positional = false,
+                bool waves_ok = false) {
   const int group = hq / hkv;
   const int max_rows = 32 * (d == 256 ? 4 : 8);
   int gh = 1;
@@ -79,11 +83,16 @@ Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles, boo
   // Rows that fit one wave under a positional mask (decode): four waves share
   // each tile's gather (the extra waves' rows are padding), which keeps more
   // of it in flight per CU (measured -6% on 16 x 4k-16k decode).
-  if (positional && d <= 128 && need <= 1) nw = 4;
+  const bool four = positional && d <= 128 && need <= 1;
+  if (four) nw = 4;
   while (nw < need) nw <<= 1;
-  // Eight-wave workgroups run one per CU: aim for one round of them (the
-  // split partials cost a write and a read per split).
-  return Shape{gh, nw, split_shape(batch * (hq / gh), max_tiles, nw >= 8 ? 256 : kTargetWorkgroups)};
+  const bool ws = four && waves_ok;
+  // One round of workgroups: eight-wave ones and the wave-split decode ones
+  // at d 128 (128 KB of LDS) run one per CU.
+  const int target = ws ? (d == 128 ? 256 : 512) : (nw >= 8 ? 256 : kTargetWorkgroups);
+  Shape sh{gh, nw, split_shape(batch * (hq / gh), max_tiles, target)};
+  sh.waves_split = ws;
+  return sh;
 }
 
 // Tiles a sequence's walk can need: all of them, or for a sliding window the
@@ -399,6 +408,167 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_kernel(VerifyParams p) {
   }
 }
 
+// lgkmcnt(0): this wave's LDS reads (and scalar loads) have returned.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// vmcnt(n) for a compile-time n < 64 (the other counters left free).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Decode with positional masks when the rows fit one wave (a GQA group's
+// heads x a few queries): the NW waves of a workgroup take the split's tiles
+// in turn (wave w: tiles kt0 + w, kt0 + w + NW, ...), each with its own LDS
+// stage, online softmax and accumulators, so every tile is computed once
+// (not once per wave); at the end the waves' partial results are merged
+// through LDS in wave order.  Each wave gathers a whole tile itself: K and V
+// separately, the next tile's K issued once this tile's K^T products are
+// done and its V once P V is done, and waits only for its own gathers (no
+// workgroup barrier in the loop).
+template <int D, int NW, typename OutT>
+__global__ __launch_bounds__(NW * 64, 1) void decode_waves_kernel(VerifyParams p) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int split = blockIdx.x, b = blockIdx.z;
+  const int q0 = p.cu_seqlens_q[b], q_len = p.cu_seqlens_q[b + 1] - q0;
+  const int kv = min(p.kv_lens[b], p.max_kv);
+  const int nkt = (kv + 63) / 64;
+  const int ktf = first_tile(p, q_len, kv);
+  const int ntiles = nkt - ktf;
+  const int nsplit = (ntiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  if (split >= nsplit && !(split == 0 && ntiles <= 0)) return;
+  const int kt0 = ktf + split * p.tiles_per_split;
+  const int kt1 = min(nkt, kt0 + p.tiles_per_split);
+  // every wave holds the same rows: (head hh of the group's GH, query t)
+  const int r = l32;
+  const int hh = min(r / p.qs, p.gh - 1);
+  const int t = r % p.qs;
+  const bool row_ok = r / p.qs < p.gh && t < q_len;
+  const int h = blockIdx.y * p.gh + hh;
+  const int g = (blockIdx.y * p.gh) / p.group;
+  const int64_t tok = (int64_t)q0 + t;
+  const int plen = p.mode == kPrefix ? p.prefix_len[b] : 0;
+
+  bf16x8 qf[D / 16];
+  load_q<D>(qf, (const uint16_t *)p.q + (tok * p.hq + h) * D, row_ok, hi);
+  // Q has landed before the gathers start: otherwise the compiler's wait for
+  // it sits at its first use inside the loop and drains every gather
+  wait_vmem();
+  const uint16_t *kbase = (const uint16_t *)p.k + (int64_t)g * p.s_head;
+  const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)g * p.s_head;
+  const int32_t *pt = p.page_table + (int64_t)b * p.max_pages;
+  using KV = KvDma<D, 1>;
+  constexpr int G = KV::IPW;   // gather instructions per matrix and tile (one wave)
+  const LaneOffsets<D> lo(lane);
+  uint16_t *stage = lds + wave * Stage<D>::ELEMS;
+  const uint32_t sk = lds_addr(stage), sv = sk + 2u * Stage<D>::V_OFF;
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
+  float m_ref = neg_inf();
+  float lsum = 0.f;
+  const float c = p.scale_log2;
+
+  int kt = kt0 + wave;
+  typename KV::Pages pg;
+  if (kt < kt1) {
+    pg = KV::pages_uniform(pt, p.page_shift, kt, kv, 0);
+    issue_mat<D, 1, false>(kbase, pg, p.page_shift, p.s_page, p.s_slot, kt, kv, sk, 0, lane);
+    issue_mat<D, 1, true>(vbase, pg, p.page_shift, p.s_page, p.s_slot, kt, kv, sv, 0, lane);
+  }
+  for (; kt < kt1; kt += NW) {
+    const int nk = kt + NW;
+    uint64_t wcur = 0;
+    if (row_ok) {
+      const int pos = t + kv - q_len;
+      wcur = p.mode == kCausal ? interval_word(0, pos, kt)
+           : p.mode == kWindow ? interval_word(pos - p.window + 1, pos, kt)
+                               : interval_word(0, max(pos, plen - 1), kt);
+    }
+    wait_vmem_n<G>();   // this tile's K (its V may still be in flight)
+    f32x16 sacc[2];
+    qk_tile<D>(stage, lo, qf, sacc);
+    typename KV::Pages pgn;
+    if (nk < kt1) {
+      pgn = KV::pages_uniform(pt, p.page_shift, nk, kv, 0);
+      wait_lds();   // this wave's K reads have returned before the K half is rewritten
+      issue_mat<D, 1, false>(kbase, pgn, p.page_shift, p.s_page, p.s_slot, nk, kv, sk, 0, lane);
+    }
+    const int kin = kv - 64 * kt;
+    const uint64_t inb = low_bits(kin);
+    const uint64_t w = wcur & inb;
+    if (kin < 64 || __ballot(row_ok && w != inb) != 0ull) apply_word(sacc, w, hi);
+    float alpha;
+    if (softmax_tile(sacc, m_ref, c, alpha)) {
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+      lsum *= alpha;
+    }
+    // this tile's V (the next tile's K may still be in flight)
+    if (nk < kt1)
+      wait_vmem_n<G>();
+    else
+      wait_vmem();
+    pv_tile<D>(stage, lo, sacc, oacc, lsum);
+    if (nk < kt1) {
+      wait_lds();   // likewise for the V reads
+      issue_mat<D, 1, true>(vbase, pgn, p.page_shift, p.s_page, p.s_slot, nk, kv, sv, 0, lane);
+    }
+  }
+  wait_vmem();
+
+  // Merge the waves' (m_ref, lsum, O) through LDS (the stages are free now):
+  // wave w stores its lane-private values, wave 0 combines them in wave order.
+  __syncthreads();
+  float *mf = (float *)lds;
+  constexpr int PER = D / 32 * 16 + 2;   // floats per lane: O, then m_ref and lsum
+  {
+    float *mine = mf + ((size_t)wave * 64 + lane) * PER;
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mine[16 * n + e] = oacc[n][e];
+    mine[PER - 2] = m_ref;
+    mine[PER - 1] = lsum;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float mx = neg_inf();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, mf[((size_t)w * 64 + lane) * PER + PER - 2]);
+  float lt_lane = 0.f;
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float *src = mf + ((size_t)w * 64 + lane) * PER;
+    const float mw = src[PER - 2];
+    const float sc = mw == neg_inf() ? 0.f : fast_exp2(mw - mx);
+    lt_lane += sc * src[PER - 1];
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[n][e] += sc * src[16 * n + e];
+  }
+  m_ref = mx;
+  const float lt = sum_halves(lt_lane);
+  const float inv = lt > 0.f ? p.v_scale / lt : 0.f;
+  const float lse = lt > 0.f ? (m_ref + __log2f(lt)) * kLn2 : neg_inf();
+  if (!row_ok) return;
+  if (nsplit <= 1) {
+    store_row<D, OutT>((OutT *)p.out + (tok * p.hq + h) * D, oacc, inv, hi);
+    if (p.lse && hi == 0) p.lse[tok * p.hq + h] = lse;
+  } else {
+    const int64_t slot = (((int64_t)b * p.max_splits + split) * p.hq + h) * p.qs + t;
+    store_row<D, float>(p.ws_o + slot * D, oacc, inv, hi);
+    if (hi == 0) p.ws_lse[slot] = lse;
+  }
+}
+
 // Merges the split partials of one (sequence, query head) in split order:
 // O = sum_s exp(LSE_s - M) O_s / sum_s exp(LSE_s - M), LSE = M + ln(sum).
 template <int D, typename OutT>
@@ -447,6 +617,12 @@ ma_status run(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh) {
     // page size (at least 1024 / d keys) and the 32-bit offsets
     kern = verify_kernel<D, NW, OutT, true, true>;
     lds = 2 * (2 * 64 * D) + Stage<D>::BYTES;
+  } else if constexpr (NW == 4 && D <= 128) {
+    if (sh.waves_split && up) {
+      // one stage per wave; the merge reuses them
+      kern = decode_waves_kernel<D, NW, OutT>;
+      lds = NW * Stage<D>::BYTES;
+    }
   }
   hipError_t e = hipSuccess;
   if (lds > 64 * 1024) e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -513,8 +689,12 @@ size_t verify_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq
 ma_status launch_verify(const VerifyArgs &a) {
   const int mode = mode_of(a.mask_kind);
   const bool positional = mode == kCausal || mode == kWindow || mode == kPrefix;
+  // pages of at least one gather instruction's rows (512 / d keys) whose
+  // bytes a 32-bit offset reaches
+  const bool uniform = (1 << a.page_shift) >= 512 / a.d &&
+                       ((int64_t)1 << a.page_shift) * a.s_slot * 2 < ((int64_t)1 << 31);
   Shape sh = shape_for(a.batch, a.hq, a.hkv, a.d, a.max_q, max_walk_tiles(mode, a.window, a.max_q, a.max_kv),
-                       positional);
+                       positional, uniform && !a.kv8);
   // Never more splits than the whole-context shape the workspace was sized for.
   const Shape full = shape_for(a.batch, a.hq, a.hkv, a.d, a.max_q, max_walk_tiles(kDense, 0, a.max_q, a.max_kv));
   if (sh.sp.max_splits > full.sp.max_splits) sh.sp = full.sp;

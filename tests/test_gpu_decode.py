@@ -72,16 +72,24 @@ def test_decode_mask_kinds(d, hq, hkv):
         assert lse_err(lse, ref_l) <= 1e-2, name
 
 
-def test_decode_equivalent_forms_bit_identical():
-    """Equal masks in different forms give identical words, hence identical
-    outputs: causal vs its dense rows, a window wider than every context vs
-    causal, dense vs packed."""
+def test_decode_equivalent_forms_agree():
+    """Equal masks in forms that take the same kernel give identical outputs:
+    a window wider than every context vs causal (both positional), dense vs
+    packed (both read mask words). Positional masks at d <= 128 spread one
+    split's tiles over the workgroup's waves and merge the waves' partial
+    states, while the word-reading forms walk the tiles in order, so causal
+    vs its dense rows agrees only to the rounding of the bf16 probabilities
+    (each wave rounds them against its own running maximum)."""
     w = _workload(801, 128, 8, 2)
     dev = device_inputs(w)
     c, lc = _decode(w, dev, "causal")
-    for name in ("causal_dense", "wide_window"):
-        o, lo = _decode(w, dev, name)
-        assert torch.equal(o, c) and torch.equal(lo, lc), name
+    o, lo = _decode(w, dev, "wide_window")
+    assert torch.equal(o, c) and torch.equal(lo, lc)
+    o, lo = _decode(w, dev, "causal_dense")
+    e_o = max_abs_err(o, c.cpu().numpy().astype(np.float64))
+    e_l = lse_err(lo, lc.cpu().numpy().astype(np.float64))
+    _say("causal vs causal_dense", e_o, e_l)
+    assert e_o <= 4e-3 and e_l <= 1e-4, (e_o, e_l)
     o1, l1 = _decode(w, dev, "dense")
     o2, l2 = _decode(w, dev, "packed")
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
