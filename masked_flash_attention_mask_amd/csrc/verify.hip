@@ -64,8 +64,8 @@ struct Shape {
 // a workgroup may have (8; 4 at d = 256, whose accumulators need a whole
 // SIMD's registers per wave).  Memory-bound decode loses nothing to the
 // padding rows of a wave.
-// waves_ok: the wave-split decode kernel may run (bf16 caches whose pages
-// hold whole gather instructions).
+// waves_ok: the wave-split decode kernel may run (pages hold whole gather
+// instructions).
 Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles, bool positional = false,
                 bool waves_ok = false) {
   const int group = hq / hkv;
@@ -427,7 +427,12 @@ __device__ __forceinline__ void wait_vmem_n() {
 // separately, the next tile's K issued once this tile's K^T products are
 // done and its V once P V is done, and waits only for its own gathers (no
 // workgroup barrier in the loop).
-template <int D, int NW, typename OutT>
+// KV8 (e4m3 caches): each wave gathers its tile's bytes into its own fp8
+// stage and widens them exactly to bf16 into its own one-matrix buffer, K
+// before the K^T products and V after them (the buffer holds one at a
+// time); the next tile's K bytes are gathered once K is widened, its V bytes
+// once V is.
+template <int D, int NW, typename OutT, bool KV8 = false>
 __global__ __launch_bounds__(NW * 64, 1) void decode_waves_kernel(VerifyParams p) {
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -457,21 +462,116 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_waves_kernel(VerifyParams p
   // Q has landed before the gathers start: otherwise the compiler's wait for
   // it sits at its first use inside the loop and drains every gather
   wait_vmem();
-  const uint16_t *kbase = (const uint16_t *)p.k + (int64_t)g * p.s_head;
-  const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)g * p.s_head;
   const int32_t *pt = p.page_table + (int64_t)b * p.max_pages;
-  using KV = KvDma<D, 1>;
-  constexpr int G = KV::IPW;   // gather instructions per matrix and tile (one wave)
-  const LaneOffsets<D> lo(lane);
-  uint16_t *stage = lds + wave * Stage<D>::ELEMS;
-  const uint32_t sk = lds_addr(stage), sv = sk + 2u * Stage<D>::V_OFF;
-
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) oacc[n] = f32x16{};
   float m_ref = neg_inf();
   float lsum = 0.f;
   const float c = p.scale_log2;
+  const LaneOffsets<D> lo(lane);
+  if constexpr (KV8) {
+    constexpr int CH8 = D / 16;          // 16-byte chunks of an fp8 row
+    constexpr int T8 = D / 16;           // 1 KB gather instructions per matrix and tile
+    constexpr int RPI8 = 1024 / D;       // key rows per gather instruction
+    constexpr uint32_t M8 = 64u * D;     // bytes of one fp8 matrix tile
+    constexpr uint32_t WB = 4u * M8;     // bytes per wave: fp8 K, fp8 V, bf16 buffer
+    uint8_t *l8 = (uint8_t *)lds + (uint32_t)wave * WB;
+    uint16_t *buf = (uint16_t *)(l8 + 2 * M8);
+    const uint32_t s8 = lds_addr(l8);
+    const int pmask = (1 << p.page_shift) - 1;
+    const __attribute__((address_space(4))) int32_t *cpt = (const __attribute__((address_space(4))) int32_t *)pt;
+    const uint8_t *k8 = (const uint8_t *)p.k + (int64_t)g * p.s_head;
+    const uint8_t *v8 = (const uint8_t *)p.v + (int64_t)g * p.s_head;
+    // Instruction t fills chunks [64 t, 64 t + 64) of the plain row-major
+    // [64][D] byte tile; its RPI8 rows share one page (pages hold at least
+    // RPI8 keys), keys past kv repeat the last key.
+    auto gather8 = [&](const uint8_t *base, int kt, uint32_t dst) {
+#pragma unroll
+      for (int t8 = 0; t8 < T8; ++t8) {
+        const int key0 = min(kt * 64 + RPI8 * t8, kv - 1);
+        const int32_t pg = cpt[key0 >> p.page_shift];
+        const int r = RPI8 * t8 + lane / CH8, pc = lane % CH8;
+        const int key = min(kt * 64 + r, kv - 1);
+        const uint32_t off = (uint32_t)((key & pmask) * (int)p.s_slot) + 16 * pc;
+        const uint64_t pb = (uint64_t)(uint32_t)pg * (uint64_t)p.s_page;
+        dma::lds_load16_s((dma::gptr_t)(base + pb), off, dst + 1024 * t8);
+      }
+    };
+    // fp8 matrix tile -> the bf16 buffer in that matrix's swizzled layout:
+    // 16 bytes in, two 8-element chunks out, per lane and step.
+    auto widen = [&](const uint8_t *src, bool is_v) {
+#pragma unroll 4
+      for (int q = lane; q < 64 * CH8; q += 64) {
+        const int r = q / CH8, c16 = q - r * CH8;
+        const u32x4 x = *(const u32x4 *)(src + 16 * q);
+        u32x4 y[2];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          y[w >> 1][2 * (w & 1)] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, false));
+          y[w >> 1][2 * (w & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, true));
+        }
+        const int f = is_v ? Stage<D>::fv(r) : Stage<D>::fk(r);
+        uint16_t *dst = buf + r * D;
+        *(u32x4 *)(dst + 8 * ((2 * c16) ^ f)) = y[0];
+        *(u32x4 *)(dst + 8 * ((2 * c16 + 1) ^ f)) = y[1];
+      }
+      // every lane's chunks are in the buffer before any lane reads it
+      wait_lds();
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+    };
+    int kt = kt0 + wave;
+    if (kt < kt1) {
+      gather8(k8, kt, s8);
+      gather8(v8, kt, s8 + M8);
+    }
+    for (; kt < kt1; kt += NW) {
+      const int nk = kt + NW;
+      uint64_t wcur = 0;
+      if (row_ok) {
+        const int pos = t + kv - q_len;
+        wcur = p.mode == kCausal ? interval_word(0, pos, kt)
+             : p.mode == kWindow ? interval_word(pos - p.window + 1, pos, kt)
+                                 : interval_word(0, max(pos, plen - 1), kt);
+      }
+      wait_vmem_n<T8>();   // this tile's K bytes (its V bytes may still be in flight)
+      widen(l8, false);
+      if (nk < kt1) gather8(k8, nk, s8);   // the K bytes were read (wait_lds in widen)
+      f32x16 sacc[2];
+      qk_tile<D>(buf, lo, qf, sacc);
+      const int kin = kv - 64 * kt;
+      const uint64_t inb = low_bits(kin);
+      const uint64_t w = wcur & inb;
+      if (kin < 64 || __ballot(row_ok && w != inb) != 0ull) apply_word(sacc, w, hi);
+      float alpha;
+      if (softmax_tile(sacc, m_ref, c, alpha)) {
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n) oacc[n] *= alpha;
+        lsum *= alpha;
+      }
+      // the K^T products' buffer reads are done before V overwrites it
+      wait_lds();
+      asm volatile("" ::: "memory");
+      if (nk < kt1)
+        wait_vmem_n<T8>();   // this tile's V bytes (the next K bytes may be in flight)
+      else
+        wait_vmem();
+      widen(l8 + M8, true);
+      if (nk < kt1) gather8(v8, nk, s8 + M8);
+      pv_tile<D>(buf - Stage<D>::V_OFF, lo, sacc, oacc, lsum);
+      // the P V buffer reads are done before the next K is widened into it
+      wait_lds();
+      asm volatile("" ::: "memory");
+    }
+  } else {
+  const uint16_t *kbase = (const uint16_t *)p.k + (int64_t)g * p.s_head;
+  const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)g * p.s_head;
+  using KV = KvDma<D, 1>;
+  constexpr int G = KV::IPW;   // gather instructions per matrix and tile (one wave)
+  uint16_t *stage = lds + wave * Stage<D>::ELEMS;
+  const uint32_t sk = lds_addr(stage), sv = sk + 2u * Stage<D>::V_OFF;
+
 
   int kt = kt0 + wave;
   typename KV::Pages pg;
@@ -518,6 +618,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_waves_kernel(VerifyParams p
       wait_lds();   // likewise for the V reads
       issue_mat<D, 1, true>(vbase, pgn, p.page_shift, p.s_page, p.s_slot, nk, kv, sv, 0, lane);
     }
+  }
   }
   wait_vmem();
 
@@ -617,6 +718,13 @@ ma_status run(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh) {
     // page size (at least 1024 / d keys) and the 32-bit offsets
     kern = verify_kernel<D, NW, OutT, true, true>;
     lds = 2 * (2 * 64 * D) + Stage<D>::BYTES;
+    if constexpr (NW == 4 && D <= 128) {
+      if (sh.waves_split) {
+        // per wave: fp8 K and V tiles and a one-matrix bf16 buffer
+        kern = decode_waves_kernel<D, NW, OutT, true>;
+        lds = NW * 4 * 64 * D;
+      }
+    }
   } else if constexpr (NW == 4 && D <= 128) {
     if (sh.waves_split && up) {
       // one stage per wave; the merge reuses them
@@ -694,7 +802,7 @@ ma_status launch_verify(const VerifyArgs &a) {
   const bool uniform = (1 << a.page_shift) >= 512 / a.d &&
                        ((int64_t)1 << a.page_shift) * a.s_slot * 2 < ((int64_t)1 << 31);
   Shape sh = shape_for(a.batch, a.hq, a.hkv, a.d, a.max_q, max_walk_tiles(mode, a.window, a.max_q, a.max_kv),
-                       positional, uniform && !a.kv8);
+                       positional, uniform);
   // Never more splits than the whole-context shape the workspace was sized for.
   const Shape full = shape_for(a.batch, a.hq, a.hkv, a.d, a.max_q, max_walk_tiles(kDense, 0, a.max_q, a.max_kv));
   if (sh.sp.max_splits > full.sp.max_splits) sh.sp = full.sp;
