@@ -6,9 +6,9 @@
 // recommends).  A PARTIAL tile carries one 64-bit word per query row; each
 // lane fetches its own row's word with one coalesced 8-byte load, prefetched
 // one tile ahead, and masks its scores with shifts of that word.  The mask
-// is thus never read per element from memory (the non-coalesced pattern the
-// same issue blames for a custom mask running about twice as slow as
-// causal).
+// is thus never read per element from memory (the non-coalesced pattern
+// that issue holds responsible for a custom mask taking roughly double the
+// causal kernel's time).
 //
 // Per tile (64 keys), every wave owns 32 query rows:
 //   paged K/V gather -> registers (one tile ahead) -> LDS (K row-major, V
