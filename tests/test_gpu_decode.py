@@ -8,7 +8,7 @@ import torch
 
 import masked_flash_attention_mask_amd as ma
 import workloads as W
-from helpers import TOL_BF16, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle
+from helpers import TOL_BF16, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle, repage
 from oracle import masks as OM
 
 pytestmark = pytest.mark.gpu
@@ -93,6 +93,32 @@ def test_decode_equivalent_forms_agree():
     o1, l1 = _decode(w, dev, "dense")
     o2, l2 = _decode(w, dev, "packed")
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_page_sizes(d):
+    """Positional-mask decode over pages of 1 to 256 keys in a random order
+    (spare pages NaN).  Pages holding a whole gather instruction's rows
+    (512 / d keys) take the wave-split kernel, smaller ones the kernel whose
+    waves share each tile; every page size matches the oracle, and the
+    wave-split results do not depend on the page size."""
+    w = _workload(803, d, 8, 2)
+    names = ("causal", "window", "prefix")
+    ref = {n: oracle(w, n) for n in names}
+    first = {}
+    for ps in (1, 4, 16, 64, 256):
+        wp = repage(w, ps, 900 + ps)
+        dev = device_inputs(wp)
+        for n in names:
+            _say("decode pages", d, ps, n)
+            o, lse = _decode(wp, dev, n)
+            assert max_abs_err(o, ref[n][0]) <= TOL_BF16, (ps, n)
+            assert lse_err(lse, ref[n][1]) <= 1e-2, (ps, n)
+            if ps >= 512 // d:
+                if n in first:
+                    assert torch.equal(o, first[n][0]) and torch.equal(lse, first[n][1]), (ps, n)
+                else:
+                    first[n] = (o, lse)
 
 
 def test_decode_bf16_output_and_window_bites():

@@ -9,7 +9,7 @@ import torch
 
 import masked_flash_attention_mask_amd as ma
 import workloads as W
-from helpers import TOL_BF16, device_inputs, lse_err, max_abs_err, oracle
+from helpers import TOL_BF16, device_inputs, lse_err, max_abs_err, oracle, repage
 from oracle import fp8 as OF
 from test_gpu_decode import KV_LENS, Q_LENS, _workload
 
@@ -61,6 +61,30 @@ def test_decode_kv8_mask_kinds(d, hq, hkv):
         err = max_abs_err(out, ref_o)
         assert err <= TOL_BF16, (name, err)
         assert lse_err(lse, ref_l) <= 1e-2, name
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_kv8_page_sizes(d):
+    """e4m3 caches in pages of the smallest allowed size (1024 / d keys) up
+    to 256 keys: every positional mask matches the oracle on the decoded
+    caches, and the output does not depend on the page size."""
+    w = _workload(804, d, 8, 2)
+    names = ("causal", "window", "prefix")
+    first = {}
+    for ps in (1024 // d, 64, 256):
+        wp = repage(w, ps, 910 + ps)
+        dev = device_inputs(wp)
+        f8, wd, dev8 = _kv8(wp)
+        for n in names:
+            _say("decode kv8 pages", d, ps, n)
+            o, lse = _decode8(wp, dev, dev8, f8, n, max(Q_LENS), max(KV_LENS))
+            ref_o, ref_l = oracle(wd, n)
+            assert max_abs_err(o, ref_o) <= TOL_BF16, (ps, n)
+            assert lse_err(lse, ref_l) <= 1e-2, (ps, n)
+            if n in first:
+                assert torch.equal(o, first[n][0]) and torch.equal(lse, first[n][1]), (ps, n)
+            else:
+                first[n] = (o, lse)
 
 
 def test_decode_kv8_bf16_output_and_determinism():
