@@ -35,6 +35,8 @@ using namespace dev::dma;
 namespace {
 
 constexpr int kTargetWorkgroups = 512;
+// Waves of a wave-split decode workgroup over e4m3 caches at d = 128.
+constexpr int kDecodeWaves128 = 5;
 
 enum MaskMode : int32_t { kDense = 0, kPacked = 1, kCausal = 2, kWindow = 3, kPrefix = 4 };
 
@@ -55,7 +57,7 @@ SplitShape split_shape(int units, int max_tiles, int target = kTargetWorkgroups)
 
 struct Shape {
   int gh;      // query heads per workgroup
-  int nw;      // waves per workgroup (1, 2, 4 or 8)
+  int nw;      // waves per workgroup (1, 2, 4 or 8; 5 for the wave-split decode at d 128)
   SplitShape sp;
   bool waves_split = false;   // decode: the waves take the split's tiles in turn
 };
@@ -67,7 +69,7 @@ struct Shape {
 // waves_ok: the wave-split decode kernel may run (pages hold whole gather
 // instructions).
 Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles, bool positional = false,
-                bool waves_ok = false) {
+                bool waves_ok = false, bool kv8 = false) {
   const int group = hq / hkv;
   const int max_rows = 32 * (d == 256 ? 4 : 8);
   int gh = 1;
@@ -87,6 +89,9 @@ Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles, boo
   if (four) nw = 4;
   while (nw < need) nw <<= 1;
   const bool ws = four && waves_ok;
+  // the wave-split kernel over e4m3 caches at d 128: five waves' 32 KB fill
+  // the CU's 160 KB (measured -5%; over bf16 caches a fifth wave costs +9%)
+  if (ws && kv8 && d == 128) nw = kDecodeWaves128;
   // One round of workgroups: eight-wave ones and the wave-split decode ones
   // at d 128 (128 KB of LDS) run one per CU.
   const int target = ws ? (d == 128 ? 256 : 512) : (nw >= 8 ? 256 : kTargetWorkgroups);
@@ -705,6 +710,27 @@ __global__ __launch_bounds__(256) void verify_combine(VerifyParams p) {
   }
 }
 
+// Launches kern over the (split, head group, sequence) grid with nw waves
+// per workgroup, then the merge of the split partials.
+template <int D, typename OutT, typename Kern>
+ma_status launch_split(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh, Kern kern, int nw,
+                       size_t lds) {
+  hipError_t e = hipSuccess;
+  if (lds > 64 * 1024) e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+  hipStream_t s = (hipStream_t)a.stream;
+  hipLaunchKernelGGL(kern, dim3(sh.sp.max_splits, a.hq / sh.gh, a.batch), dim3(nw * 64), lds, s, prm);
+  e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify launch: %s", hipGetErrorString(e));
+  if (sh.sp.max_splits > 1) {
+    const int chunks = (a.max_q * (D / 4) + 255) / 256;
+    hipLaunchKernelGGL((verify_combine<D, OutT>), dim3(a.hq, a.batch, chunks), dim3(256), 0, s, prm);
+    e = hipGetLastError();
+    if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify combine launch: %s", hipGetErrorString(e));
+  }
+  return MA_OK;
+}
+
 template <int D, int NW, typename OutT>
 ma_status run(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh) {
   size_t lds = 2 * Stage<D>::BYTES;
@@ -718,34 +744,18 @@ ma_status run(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh) {
     // page size (at least 1024 / d keys) and the 32-bit offsets
     kern = verify_kernel<D, NW, OutT, true, true>;
     lds = 2 * (2 * 64 * D) + Stage<D>::BYTES;
-    if constexpr (NW == 4 && D <= 128) {
-      if (sh.waves_split) {
-        // per wave: fp8 K and V tiles and a one-matrix bf16 buffer
-        kern = decode_waves_kernel<D, NW, OutT, true>;
-        lds = NW * 4 * 64 * D;
-      }
-    }
-  } else if constexpr (NW == 4 && D <= 128) {
-    if (sh.waves_split && up) {
-      // one stage per wave; the merge reuses them
-      kern = decode_waves_kernel<D, NW, OutT>;
-      lds = NW * Stage<D>::BYTES;
-    }
   }
-  hipError_t e = hipSuccess;
-  if (lds > 64 * 1024) e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
-  hipStream_t s = (hipStream_t)a.stream;
-  hipLaunchKernelGGL(kern, dim3(sh.sp.max_splits, a.hq / sh.gh, a.batch), dim3(NW * 64), lds, s, prm);
-  e = hipGetLastError();
-  if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify launch: %s", hipGetErrorString(e));
-  if (sh.sp.max_splits > 1) {
-    const int chunks = (a.max_q * (D / 4) + 255) / 256;
-    hipLaunchKernelGGL((verify_combine<D, OutT>), dim3(a.hq, a.batch, chunks), dim3(256), 0, s, prm);
-    e = hipGetLastError();
-    if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify combine launch: %s", hipGetErrorString(e));
-  }
-  return MA_OK;
+  return launch_split<D, OutT>(a, prm, sh, kern, NW, lds);
+}
+
+// The wave-split decode kernel with NW waves: one stage per wave (bf16), or
+// per wave fp8 K and V tiles and a one-matrix bf16 buffer (e4m3); the merge
+// reuses them.
+template <int D, int NW, typename OutT>
+ma_status run_waves(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh) {
+  if (a.kv8)
+    return launch_split<D, OutT>(a, prm, sh, decode_waves_kernel<D, NW, OutT, true>, NW, (size_t)NW * 4 * 64 * D);
+  return launch_split<D, OutT>(a, prm, sh, decode_waves_kernel<D, NW, OutT, false>, NW, (size_t)NW * Stage<D>::BYTES);
 }
 
 template <int D, typename OutT>
@@ -754,6 +764,11 @@ ma_status run_nw(const VerifyArgs &a, const VerifyParams &prm, const Shape &sh) 
     if (sh.nw != 4) return set_error(MA_ERR_UNSUPPORTED, "%d waves at head_dim 256", sh.nw);
     return run<D, 4, OutT>(a, prm, sh);
   } else {
+    if (sh.waves_split) {
+      if (sh.nw == kDecodeWaves128) return run_waves<D, kDecodeWaves128, OutT>(a, prm, sh);
+      if (sh.nw != 4) return set_error(MA_ERR_UNSUPPORTED, "%d decode waves", sh.nw);
+      return run_waves<D, 4, OutT>(a, prm, sh);
+    }
     switch (sh.nw) {
       case 1: return run<D, 1, OutT>(a, prm, sh);
       case 2: return run<D, 2, OutT>(a, prm, sh);
@@ -802,7 +817,7 @@ ma_status launch_verify(const VerifyArgs &a) {
   const bool uniform = (1 << a.page_shift) >= 512 / a.d &&
                        ((int64_t)1 << a.page_shift) * a.s_slot * 2 < ((int64_t)1 << 31);
   Shape sh = shape_for(a.batch, a.hq, a.hkv, a.d, a.max_q, max_walk_tiles(mode, a.window, a.max_q, a.max_kv),
-                       positional, uniform);
+                       positional, uniform, a.kv8 != 0);
   // Never more splits than the whole-context shape the workspace was sized for.
   const Shape full = shape_for(a.batch, a.hq, a.hkv, a.d, a.max_q, max_walk_tiles(kDense, 0, a.max_q, a.max_kv));
   if (sh.sp.max_splits > full.sp.max_splits) sh.sp = full.sp;
