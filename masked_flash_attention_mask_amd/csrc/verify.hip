@@ -57,7 +57,7 @@ SplitShape split_shape(int units, int max_tiles, int target = kTargetWorkgroups)
 
 struct Shape {
   int gh;      // query heads per workgroup
-  int nw;      // waves per workgroup (1, 2, 4 or 8; 5 for the wave-split decode at d 128)
+  int nw;      // waves per workgroup (1, 2, 4 or 8; 5 for the e4m3 wave-split decode at d 128)
   SplitShape sp;
   bool waves_split = false;   // decode: the waves take the split's tiles in turn
 };
@@ -82,9 +82,11 @@ Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles, boo
   // At d = 256 a workgroup keeps 4 waves even for a few rows: each wave's
   // share of the tile gather (addresses in registers) then stays small.
   int nw = d == 256 ? 4 : 1;
-  // Rows that fit one wave under a positional mask (decode): four waves share
-  // each tile's gather (the extra waves' rows are padding), which keeps more
-  // of it in flight per CU (measured -6% on 16 x 4k-16k decode).
+  // Rows that fit one wave under a positional mask (decode): four waves.
+  // Where pages hold whole gather instructions (waves_ok) they take the
+  // split's tiles in turn (the wave-split kernel); otherwise they share each
+  // tile's gather (the extra waves' rows are padding), which keeps more of it
+  // in flight per CU (measured -6% on 16 x 4k-16k decode).
   const bool four = positional && d <= 128 && need <= 1;
   if (four) nw = 4;
   while (nw < need) nw <<= 1;
@@ -93,7 +95,7 @@ Shape shape_for(int batch, int hq, int hkv, int d, int max_q, int max_tiles, boo
   // the CU's 160 KB (measured -5%; over bf16 caches a fifth wave costs +9%)
   if (ws && kv8 && d == 128) nw = kDecodeWaves128;
   // One round of workgroups: eight-wave ones and the wave-split decode ones
-  // at d 128 (128 KB of LDS) run one per CU.
+  // at d 128 (128 KB of LDS, 160 KB over e4m3 caches) run one per CU.
   const int target = ws ? (d == 128 ? 256 : 512) : (nw >= 8 ? 256 : kTargetWorkgroups);
   Shape sh{gh, nw, split_shape(batch * (hq / gh), max_tiles, target)};
   sh.waves_split = ws;
