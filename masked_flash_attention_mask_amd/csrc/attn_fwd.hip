@@ -54,12 +54,23 @@ struct PrefillParams {
 // Workgroup -> (work item, query head).  Workgroups are dispatched to the 8
 // XCDs round-robin; when Hq is a multiple of 8, each XCD gets a contiguous
 // block of Hq/8 query heads (so its L2 serves the K/V of few K/V heads) and
-// walks the work items in plan order (most work first).
-__device__ __forceinline__ void map_block(int b, int num_items, int hq, int &item, int &h) {
+// walks the work items in plan order (most work first).  When an XCD would
+// hold fewer query heads than a GQA group (Hq/8 < group), the r = group /
+// (Hq/8) XCDs of one K/V head instead take all of that group's query heads,
+// each XCD every r-th work item: the heads that read the same K/V tiles
+// then run side by side behind one L2.  The grid is then padded to a
+// multiple of r work items; padding workgroups get item >= num_items.
+__device__ __forceinline__ void map_block(int b, int num_items, int hq, int group, int &item, int &h) {
   if ((hq & 7) == 0) {
     const int m = hq >> 3, x = b & 7, slot = b >> 3;
-    item = slot / m;
-    h = x * m + slot % m;
+    if (m < group && group % m == 0) {
+      const int r = group / m;
+      item = (slot / group) * r + x % r;
+      h = (x / r) * group + slot % group;
+    } else {
+      item = slot / m;
+      h = x * m + slot % m;
+    }
   } else {
     item = b / hq;
     h = b - item * hq;
@@ -120,7 +131,8 @@ __global__ __launch_bounds__(BQ * 2, (prefill_occupancy<D, BQ, DMA>())) void pre
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   int item_idx, h;
-  map_block(blockIdx.x, p.num_items, p.hq, item_idx, h);
+  map_block(blockIdx.x, p.num_items, p.hq, p.group, item_idx, h);
+  if (item_idx >= p.num_items) return;
   const Item it = p.items[item_idx];
   const SeqInfo sq = p.seqs[it.seq];
   const int g = h / p.group;
@@ -426,7 +438,8 @@ __global__ __launch_bounds__(BQ * 2, 1) void prefill_f32_kernel(PrefillParams p)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   int item_idx, h;
-  map_block(blockIdx.x, p.num_items, p.hq, item_idx, h);
+  map_block(blockIdx.x, p.num_items, p.hq, p.group, item_idx, h);
+  if (item_idx >= p.num_items) return;
   const Item it = p.items[item_idx];
   const SeqInfo sq = p.seqs[it.seq];
   const int g = h / p.group;
@@ -569,7 +582,13 @@ ma_status launch_prefill(const PrefillArgs &a) {
   prm.num_items = pl->num_rows;
   prm.scale = a.scale;
   prm.scale_log2 = a.scale * kLog2e;
-  const int64_t grid64 = (int64_t)pl->num_rows * a.hq;
+  // work items padded for map_block's K/V-group mapping
+  int64_t items = pl->num_rows;
+  if (a.hq % 8 == 0 && a.hq / 8 < prm.group && prm.group % (a.hq / 8) == 0) {
+    const int64_t r = prm.group / (a.hq / 8);
+    items = (items + r - 1) / r * r;
+  }
+  const int64_t grid64 = items * a.hq;
   if (grid64 > INT32_MAX) return set_error(MA_ERR_UNSUPPORTED, "grid too large");
   const int grid = (int)grid64;
   const bool bq128 = pl->tile_q == 128;
