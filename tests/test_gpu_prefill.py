@@ -283,6 +283,26 @@ def test_config3a_full_size_sampled():
     assert lse_err(l1, ref_l) <= 1e-2
 
 
+@pytest.mark.parametrize("hkv", [1, 2, 4, 8])
+def test_bf16_head_group_map(hkv):
+    """8 query heads over 1, 2, 4 or 8 K/V heads: with fewer query heads per
+    XCD than a GQA group, the workgroups of one K/V head's query heads are
+    spread over that head's XCDs by work item, the grid padded to a multiple
+    of them (seven q-tiles here, so padding workgroups exist); every (q-tile,
+    head) must still be computed exactly once."""
+    q_lens, kv_lens = [300, 1, 129, 40], [300, 90, 129, 500]
+    w = _ragged(120 + hkv, 128, 8, hkv, q_lens, kv_lens)
+    w.masks["causal"] = W.MaskInput("causal")
+    w.masks["window"] = W.MaskInput("window", window=70)
+    dev = device_inputs(w)
+    for mask in ("causal", "window"):
+        _say("head group map", hkv, mask)
+        out, lse, _ = run_prefill(w, dev, mask, tile_q=128)
+        ref_o, ref_l = oracle(w, mask)
+        assert max_abs_err(out, ref_o) <= TOL_BF16, mask
+        assert lse_err(lse, ref_l) <= 1e-2, mask
+
+
 def test_config3b_full_size_sampled_and_not_vacuous():
     rng = np.random.default_rng(32)
     rows = {0: _sample_rows(16384, rng, 24)}
