@@ -164,8 +164,22 @@ typedef struct {
 
 /* Compile a mask into a plan and make it resident on the device (one
  * stream-ordered upload, or a device classification pass for a device-resident
- * DENSE_BOOL / PACKED_U64 mask).  The plan depends on the mask only: equal
- * masks give byte-identical plans whatever descriptors described them.
+ * DENSE_BOOL / PACKED_U64 mask).  The mask forms are those of the pages: the
+ * kernel's causal flag or flattened custom mask (sglang-jax pull request 20,
+ * the custom-mask argument of the ragged paged attention kernel), the
+ * per-sequence prefix (aphrodite-engine issue 1526, prefixlm_mask_mod), a
+ * bit-packed mask or a block-sparse one (flashinfer issue 724, issue body and
+ * the maintainer's reply), (q_range, k_range, type, chunk_size) lists
+ * (MagiAttention issue 316, "Proposed API") and the sliding window ANDed into
+ * the causal mask (mlxcel pull request 555, description).  Each tile of
+ * tile_q x tile_k entries is FULL, SKIP or PARTIAL over its in-bounds entries
+ * and only PARTIAL tiles carry words, which is how the kernels avoid reading
+ * the mask per element (flashinfer issue 724: the non-coalesced mask reads it
+ * blames for the slowdown).  A host-compiled plan depends on the mask only:
+ * equal masks give byte-identical plans whatever descriptors described them.
+ * A device-classified plan has the same tile classes and words (export) but
+ * its own execution order, so its serialisation may differ from a host
+ * plan's.
  * Errors: INVALID / CONFLICT (window given with another kind; a custom mask
  * combined with causal is expressed by choosing one kind) / SIZE (mask_numel
  * short of sum q_len*kv_len, or of sum q_len*ceil(kv_len/64) words) /
@@ -195,7 +209,12 @@ ma_status mask_plan_export(const ma_plan *plan, uint8_t *classes, uint64_t *word
  * words), for byte-identity checks.  Call with dst = NULL to get *bytes. */
 ma_status mask_plan_serialize(const ma_plan *plan, void *dst, size_t *bytes);
 
-/* Masked prefill over a compiled plan.
+/* Masked prefill over a compiled plan: ragged query sequences against paged
+ * K/V under a mask (sglang-jax pull request 20, ragged paged attention with a
+ * custom mask; flashinfer issue 724, the custom-mask prefill whose speed the
+ * issue measures against the causal kernel).  SKIP tiles are never visited,
+ * FULL tiles take no mask work, PARTIAL tiles mask each score with their
+ * row's word.
  *  q        device [total_q, Hq, d], in_dtype, contiguous
  *  k_cache, v_cache  device paged caches of in_dtype; element (page, slot,
  *           head, x) at page*kv_strides[0] + slot*kv_strides[1] +
@@ -285,7 +304,10 @@ size_t attn_verify_tree_workspace(int32_t batch, int32_t max_q, int32_t max_kv, 
 /* Speculative tree verify: every sequence's draft-tree queries (q_len <= 64
  * per sequence) against its cached context plus the draft tokens, under a
  * full-row custom mask (DENSE_BOOL or PACKED_U64, device memory, rows over
- * all kv_len keys).  Lengths stay on the device (no host round trip):
+ * all kv_len keys) — tree attention for speculative decoding expressed as a
+ * custom mask (flashinfer issue 724, the maintainer's reply; the TARGET_VERIFY
+ * mode of sglang-jax pull request 20).  Lengths stay on the device (no host
+ * round trip):
  *  cu_seqlens_q device int32 [batch+1], kv_lens device int32 [batch];
  *  max_q >= every q_len (<= 64), max_kv >= every kv_len (host bounds used for
  *  the launch shape and the workspace).
@@ -294,7 +316,13 @@ size_t attn_verify_tree_workspace(int32_t batch, int32_t max_q, int32_t max_kv, 
  * whose partial results are merged in a fixed order.  Requires in_dtype BF16
  * and d in {64, 128, 256}.  workspace: device, at least
  * attn_verify_tree_workspace(...) bytes (NULL allowed
- * when that is 0), owned by the caller; its contents need no initialisation. */
+ * when that is 0), owned by the caller; its contents need no initialisation.
+ * Mask size: the layout of the mask kinds above (rows of kv_len bytes, or of
+ * ceil(kv_len / 64) words, per query, sequences concatenated).  Because the
+ * lengths are device-resident, the host checks only that mask_numel covers
+ * one element per query row (MA_ERR_SIZE otherwise); any element at or past
+ * mask_numel reads as 0, i.e. its key is masked, and nothing past the
+ * buffer is read. */
 ma_status attn_verify_tree(const void *q, int64_t total_q, int32_t hq, const void *k_cache,
                            const void *v_cache, int32_t hkv, int32_t d, int32_t page_size,
                            const int64_t kv_strides[3], const int32_t *page_table,
@@ -327,7 +355,9 @@ size_t attn_decode_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32
  * tiles it can see.  A row that sees no key gets O = 0 and LSE = -inf.
  * Requires in_dtype BF16 and d in {64, 128, 256}.  workspace: device, at
  * least attn_decode_workspace(...) bytes (NULL allowed when that is 0), owned
- * by the caller; its contents need no initialisation. */
+ * by the caller; its contents need no initialisation.  DENSE_BOOL /
+ * PACKED_U64 masks follow attn_verify_tree's size rule (one element per
+ * query row checked on the host, elements past mask_numel read as 0). */
 ma_status attn_decode(const void *q, int64_t total_q, int32_t hq, const void *k_cache,
                       const void *v_cache, int32_t hkv, int32_t d, int32_t page_size,
                       const int64_t kv_strides[3], const int32_t *page_table, int32_t max_pages,

@@ -421,6 +421,18 @@ static ma_status check_small_q(const void *q, const void *k_cache, const void *v
   return MA_OK;
 }
 
+// A dense or packed mask needs at least one element per query row (every
+// row that exists has kv_len >= q_len >= 1 keys).  The exact size depends on
+// the device-resident lengths and is not known here; the kernels read
+// elements at or past mask_numel as 0 (masked), never past the buffer.
+static ma_status check_mask_rows(const void *mask, int64_t mask_numel, int64_t total_q) {
+  if (!mask || mask_numel < 1) return set_error(MA_ERR_INVALID, "mask is required");
+  if (mask_numel < total_q)
+    return set_error(MA_ERR_SIZE, "mask has %lld elements, fewer than its %lld query rows need",
+                     (long long)mask_numel, (long long)total_q);
+  return MA_OK;
+}
+
 static ma_status run_small_q(const void *q, int32_t hq, const void *k_cache, const void *v_cache, int32_t hkv,
                              int32_t d, int32_t page_size, const int64_t kv_strides[3], const int32_t *page_table,
                              int32_t max_pages, const int32_t *cu_seqlens_q, const int32_t *kv_lens,
@@ -494,7 +506,7 @@ ma_status attn_decode(const void *q, int64_t total_q, int32_t hq, const void *k_
       break;
     case MA_KIND_DENSE_BOOL:
     case MA_KIND_PACKED_U64:
-      if (!mask || mask_numel < 1) return set_error(MA_ERR_INVALID, "mask is required");
+      if ((st = check_mask_rows(mask, mask_numel, total_q)) != MA_OK) return st;
       break;
     case MA_KIND_RANGES:
       return set_error(MA_ERR_UNSUPPORTED, "decode takes RANGES masks as dense or packed rows");
@@ -534,7 +546,7 @@ ma_status attn_decode_kv8(const void *q, int64_t total_q, int32_t hq, const void
       break;
     case MA_KIND_DENSE_BOOL:
     case MA_KIND_PACKED_U64:
-      if (!mask || mask_numel < 1) return set_error(MA_ERR_INVALID, "mask is required");
+      if ((st = check_mask_rows(mask, mask_numel, total_q)) != MA_OK) return st;
       break;
     case MA_KIND_RANGES:
       return set_error(MA_ERR_UNSUPPORTED, "decode takes RANGES masks as dense or packed rows");
@@ -560,7 +572,7 @@ ma_status attn_verify_tree(const void *q, int64_t total_q, int32_t hq, const voi
   if (st != MA_OK) return st;
   if (mask_kind != MA_KIND_DENSE_BOOL && mask_kind != MA_KIND_PACKED_U64)
     return set_error(MA_ERR_CONFLICT, "tree verify takes a custom mask (dense or packed), got kind %d", mask_kind);
-  if (!mask || mask_numel < 1) return set_error(MA_ERR_INVALID, "mask is required");
+  if ((st = check_mask_rows(mask, mask_numel, total_q)) != MA_OK) return st;
   return run_small_q(q, hq, k_cache, v_cache, hkv, d, page_size, kv_strides, page_table, max_pages, cu_seqlens_q,
                      kv_lens, batch, max_q, max_kv, mask_kind, 0, nullptr, mask, mask_numel, out_dtype, scale,
                      workspace, ws_bytes, out, lse, stream);

@@ -141,6 +141,20 @@ __device__ __forceinline__ int64_t mask_offset(const VerifyParams &p, int b) {
   return off;
 }
 
+// A sequence's query count, clamped to the max_q row slots per head that the
+// launch (and the workspace) provide: lengths live on the device, so the host
+// cannot refuse a longer sequence; its rows past max_q are not computed.
+__device__ __forceinline__ int seq_q_len(const VerifyParams &p, int b, int q0) {
+  return max(0, min(p.cu_seqlens_q[b + 1] - q0, p.qs));
+}
+
+// Splits of a walk of ntiles k-tiles, never more than the launch has (a
+// window walk is bounded by the host's max_walk_tiles only while q_len <=
+// max_q, which seq_q_len ensures).
+__device__ __forceinline__ int num_splits(const VerifyParams &p, int ntiles) {
+  return min((ntiles + p.tiles_per_split - 1) / p.tiles_per_split, p.max_splits);
+}
+
 // First k-tile any row of the sequence can see.
 __device__ __forceinline__ int first_tile(const VerifyParams &p, int q_len, int kv) {
   if (p.mode != kWindow) return 0;
@@ -229,12 +243,12 @@ __global__ __launch_bounds__(NW * 64, 1) void verify_kernel(VerifyParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int split = blockIdx.x, b = blockIdx.z;
-  const int q0 = p.cu_seqlens_q[b], q_len = p.cu_seqlens_q[b + 1] - q0;
+  const int q0 = p.cu_seqlens_q[b], q_len = seq_q_len(p, b, q0);
   const int kv = min(p.kv_lens[b], p.max_kv);  // the page table covers max_kv keys
   const int nkt = (kv + 63) / 64;
   const int ktf = first_tile(p, q_len, kv);
   const int ntiles = nkt - ktf;
-  const int nsplit = (ntiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  const int nsplit = num_splits(p, ntiles);
   if (split >= nsplit && !(split == 0 && ntiles <= 0)) return;
   const int kt0 = ktf + split * p.tiles_per_split;
   const int kt1 = min(nkt, kt0 + p.tiles_per_split);
@@ -445,12 +459,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_waves_kernel(VerifyParams p
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int split = blockIdx.x, b = blockIdx.z;
-  const int q0 = p.cu_seqlens_q[b], q_len = p.cu_seqlens_q[b + 1] - q0;
+  const int q0 = p.cu_seqlens_q[b], q_len = seq_q_len(p, b, q0);
   const int kv = min(p.kv_lens[b], p.max_kv);
   const int nkt = (kv + 63) / 64;
   const int ktf = first_tile(p, q_len, kv);
   const int ntiles = nkt - ktf;
-  const int nsplit = (ntiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  const int nsplit = num_splits(p, ntiles);
   if (split >= nsplit && !(split == 0 && ntiles <= 0)) return;
   const int kt0 = ktf + split * p.tiles_per_split;
   const int kt1 = min(nkt, kt0 + p.tiles_per_split);
@@ -682,10 +696,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_waves_kernel(VerifyParams p
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void verify_combine(VerifyParams p) {
   const int h = blockIdx.x, b = blockIdx.y;
-  const int q0 = p.cu_seqlens_q[b], q_len = p.cu_seqlens_q[b + 1] - q0;
+  const int q0 = p.cu_seqlens_q[b], q_len = seq_q_len(p, b, q0);
   const int kv = min(p.kv_lens[b], p.max_kv);
   const int ntiles = (kv + 63) / 64 - first_tile(p, q_len, kv);
-  const int nsplit = (ntiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  const int nsplit = num_splits(p, ntiles);
   if (nsplit <= 1) return;
   const int64_t sbase = (int64_t)b * p.max_splits;
   // one (row, 4 columns) item per thread; blockIdx.z picks the chunk of items

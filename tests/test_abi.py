@@ -95,10 +95,11 @@ def test_prefill_validation_before_hip():
     assert plan.info().on_device == 0       # nothing was uploaded
 
 
-def _verify(kind=L.KIND["packed"], max_q=64, ws=None, ws_bytes=0, d=128, in_dt=L.BF16, batch=2, max_kv=4000):
+def _verify(kind=L.KIND["packed"], max_q=64, ws=None, ws_bytes=0, d=128, in_dt=L.BF16, batch=2, max_kv=4000,
+            numel=1000):
     st = (ctypes.c_int64 * 3)(2048, 128, 128)
     return L.LIB.attn_verify_tree(FAKE, 128, 4, FAKE, FAKE, 1, d, 16, st, FAKE, 300, FAKE, FAKE, batch, max_q,
-                                  max_kv, kind, FAKE, 100, in_dt, L.F32, 0.1, ws, ws_bytes, FAKE, None, None)
+                                  max_kv, kind, FAKE, numel, in_dt, L.F32, 0.1, ws, ws_bytes, FAKE, None, None)
 
 
 def test_verify_validation_before_hip():
@@ -110,6 +111,21 @@ def test_verify_validation_before_hip():
     assert need > 0
     assert _verify(ws=FAKE, ws_bytes=need - 1) == L.MA_ERR_SIZE
     assert ma.attn_verify_tree_workspace(0, 64, 4000, 4, 1, 128) == 0
+
+
+def test_short_custom_mask_is_a_size_error():
+    """Lengths are on the device, so the host checks the one bound it can: a
+    dense or packed mask needs an element per query row (128 rows here);
+    shorter masks are MA_ERR_SIZE before any HIP call, for tree verify and
+    decode alike.  (Elements past mask_numel of a longer mask read as 0, i.e.
+    masked; the GPU tests check that.)"""
+    need = ma.attn_verify_tree_workspace(2, 64, 4000, 4, 1, 128)
+    for kind in (L.KIND["packed"], L.KIND["dense"]):
+        assert _verify(kind=kind, numel=127, ws=FAKE, ws_bytes=need) == L.MA_ERR_SIZE
+        assert _verify(kind=kind, numel=0, ws=FAKE, ws_bytes=need) == L.MA_ERR_INVALID
+    dneed = ma.attn_decode_workspace(2, 1, 4000, 4, 1, 128)
+    for kind in (L.KIND["packed"], L.KIND["dense"]):
+        assert _decode(kind=kind, mask=FAKE, numel=1, ws=FAKE, ws_bytes=dneed) == L.MA_ERR_SIZE   # 2 rows
 
 
 def _decode(kind=L.KIND["causal"], window=0, prefix=None, mask=None, numel=0, max_q=1, ws=None, ws_bytes=0,

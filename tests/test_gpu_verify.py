@@ -60,3 +60,31 @@ def test_verify_matches_prefill_over_device_plan():
     o2, _ = ma.attn_prefill_masked(plan, dev["q"], dev["k"], dev["v"], dev["pt"], w.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert (o1 - o2).abs().max().item() <= 2e-3
+
+
+@pytest.mark.parametrize("form", ["tree_packed", "tree_dense"])
+def test_short_mask_reads_missing_elements_as_masked(form):
+    """A mask buffer shorter than its sequences need (lengths are on the
+    device, the host cannot check the exact size): elements at or past
+    mask_numel read as 0, so the result equals the oracle over the same mask
+    with those elements cleared (rows that lose every key give O = 0 and
+    LSE = -inf)."""
+    w = W.config2(seed=77, batch=3, nodes=20, ctx_lo=50, ctx_hi=200, hq=8, hkv=2, d=128)
+    print("[case] short mask", form, flush=True)
+    dev = device_inputs(w)
+    mi = w.masks[form]
+    keep = mi.data.size - mi.data.size // 5          # drop the last fifth of the buffer
+    short = mi.data[:keep]
+    data = short if mi.kind == "dense" else short.view(np.int64)
+    mask = torch.from_numpy(np.ascontiguousarray(data)).cuda()
+    out, lse = ma.attn_verify_tree(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], mask, mi.kind,
+                                   int(w.q_lens.max()), int(w.kv_lens.max()), w.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    cleared = mi.data.copy()
+    cleared[keep:] = 0
+    w.masks["cleared"] = W.gen.MaskInput(mi.kind, data=cleared)
+    ref_o, ref_l = oracle(w, "cleared")
+    assert max_abs_err(out, ref_o) <= TOL_BF16
+    assert lse_err(lse, ref_l) <= 1e-2
+    # the last sequence lost whole rows: they are empty
+    assert torch.isneginf(lse[-1]).all() and (out[-1] == 0).all()
