@@ -24,6 +24,9 @@
 // order (deterministic, no atomics).
 #include <hip/hip_runtime.h>
 
+#include <climits>
+#include <type_traits>
+
 #include "internal.h"
 #include "kernels_common.h"
 #include "tile_dma_bf16.h"
@@ -129,6 +132,9 @@ struct VerifyParams {
   int32_t tiles_per_split, max_splits, max_kv;
   float scale, scale_log2;   // scale_log2 includes the K descale factor (fp8 caches)
   float v_scale;             // V descale factor (fp8 caches; 1 otherwise)
+  // balanced tree verify (verify_pipe_kernel): head blocks per sequence,
+  // workgroups, sequences
+  int32_t nhb, grid, batch;
 };
 
 __device__ __forceinline__ int64_t mask_offset(const VerifyParams &p, int b) {
@@ -726,6 +732,430 @@ __global__ __launch_bounds__(256) void verify_combine(VerifyParams p) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Tree verify over a balanced partition of the tiles (custom masks, d <= 128)
+// ---------------------------------------------------------------------------
+// A unit is (sequence b, head block hb): GH query heads of one GQA group and
+// their q_len queries, at most 256 row slots (eight waves of 32), head-major,
+// so that each K/V tile gathered serves the whole group.  Its k-tiles are
+// 0 .. n_b - 1, n_b = ceil(kv_len / 64).  A unit is cut into k_b =
+// ceil(n_b / T) pieces of near-equal length, one workgroup each, where T is
+// the smallest tile count for which all pieces fit the grid (sum over units
+// of k_b <= G): every workgroup then has at most T tiles and a single piece,
+// however unevenly the contexts are spread.  T and the piece of each
+// workgroup are computed on the device from the device-resident lengths (a
+// binary search over T and prefix sums across a wave).  A unit in one piece
+// is written directly; the pieces of a cut unit leave partial (O, LSE) rows
+// in their workgroups' slots, which verify_pipe_combine merges in piece
+// order (deterministic, no atomics).
+//
+// Inside a piece the loop is software-pipelined: step j issues the S^T
+// products of tile j + 1 beside the masking and softmax of tile j, then
+// O^T += V^T P^T of tile j.  Four LDS stages hold tiles j .. j + 3: step j
+// gathers tile j + 3 (K, V and the rows' packed mask words, all by LDS DMA)
+// into the stage tile j - 1 has left, and ends waiting only for tile j + 2,
+// so a tile's gathers have two steps to land.  No compiler-visible load is
+// in flight in the loop, so every wait is an explicit vmcnt.
+constexpr int kPipeGrid = 256;   // one 8-wave workgroup per CU
+constexpr int kPipeRows = 256;   // row slots of a unit
+constexpr int kPipeWaves = 8;
+constexpr int kPipeStages = 4;
+
+// Tiles of every unit of sequence b (its head blocks share them); a
+// sequence with queries but no keys keeps one tile so that its rows are
+// written (O = 0, LSE = -inf).
+__device__ __forceinline__ int seq_tiles(const VerifyParams &p, int b) {
+  const int q0 = p.cu_seqlens_q[b];
+  if (seq_q_len(p, b, q0) <= 0) return 0;
+  const int kv = min(p.kv_lens[b], p.max_kv);
+  return kv > 0 ? (kv + 63) / 64 : 1;
+}
+
+// Packed mask words of sequence b (true lengths: the caller's layout).
+__device__ __forceinline__ int64_t seq_words(const VerifyParams &p, int b) {
+  const int64_t ql = p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b], kv = p.kv_lens[b];
+  return ql * ((kv + 63) / 64);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32)) << 32) |
+                   (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u));
+}
+
+// The piece of workgroup `wg`: unit (b, hb), its tiles [kt0, kt1) of n, its
+// index k among the unit's npieces pieces, and the sequence's first mask
+// word.  b < 0: the workgroup has no piece.
+struct Piece {
+  int b, hb, kt0, kt1, n, k, npieces;
+  int64_t moff;
+};
+
+// Every lane returns the same (scalar) values.  Batches of up to 64
+// sequences keep each sequence's tile count in its lane for the whole search;
+// larger ones reread them per chunk.
+__device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
+  const bool one_chunk = p.batch <= 64;
+  const int n_lane = lane < p.batch ? seq_tiles(p, lane) : 0;
+  auto tiles_at = [&](int b) { return one_chunk ? (b < p.batch ? n_lane : 0) : (b < p.batch ? seq_tiles(p, b) : 0); };
+  // Smallest T in [1, max n_b] with sum_b nhb * ceil(n_b / T) <= G (T = max
+  // n_b always fits: the host sizes G to at least the number of units).
+  int maxn = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += 64) maxn = max(maxn, tiles_at(c0 + lane));
+  maxn = wave_max(maxn);
+  int lo_t = 1, hi_t = max(maxn, 1);
+  while (lo_t < hi_t) {
+    const int mid = (lo_t + hi_t) >> 1;
+    int need = 0;
+    for (int c0 = 0; c0 < p.batch; c0 += 64) {
+      const int n = tiles_at(c0 + lane);
+      need += wave_sum(p.nhb * ((n + mid - 1) / mid));
+    }
+    if (need <= p.grid) hi_t = mid;
+    else lo_t = mid + 1;
+  }
+  const int T = __builtin_amdgcn_readfirstlane(lo_t);
+  // the sequence whose units hold workgroup wg: prefix sums of nhb * k_b
+  int base = 0;
+  int64_t mbase = 0;
+  Piece r{-1, 0, 0, 0, 0, 0, 0, 0};
+  for (int c0 = 0; c0 < p.batch; c0 += 64) {
+    const int b = c0 + lane;
+    const int n = tiles_at(b);
+    const int wgs = p.nhb * ((n + T - 1) / T);
+    const int64_t me = b < p.batch ? seq_words(p, b) : 0;
+    const int incl = wave_incl_scan(wgs, lane);
+    const int64_t mincl = wave_incl_scan(me, lane);
+    if (r.b < 0) {
+      const uint64_t hit = __ballot(b < p.batch && base + incl > wg);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        r.b = c0 + l;
+        const int first = base + __shfl(incl - wgs, l, 64);
+        r.n = __shfl(n, l, 64);
+        r.npieces = (r.n + T - 1) / T;
+        const int off = wg - first;
+        r.hb = off / r.npieces;
+        r.k = off - r.hb * r.npieces;
+        r.moff = mbase + __shfl(mincl - me, l, 64);
+      }
+    }
+    base += __shfl(incl, 63, 64);
+    mbase += __shfl(mincl, 63, 64);
+  }
+  r.b = __builtin_amdgcn_readfirstlane(r.b);
+  r.n = __builtin_amdgcn_readfirstlane(r.n);
+  r.npieces = __builtin_amdgcn_readfirstlane(r.npieces);
+  r.hb = __builtin_amdgcn_readfirstlane(r.hb);
+  r.k = __builtin_amdgcn_readfirstlane(r.k);
+  r.moff = uniform64(r.moff);
+  r.kt0 = r.k * r.n / r.npieces;
+  r.kt1 = (r.k + 1) * r.n / r.npieces;
+  return r;
+}
+
+// What a workgroup leaves for the merge: the unit whose first piece it ran
+// when that unit has more pieces (b < 0 otherwise).  Every workgroup writes
+// its record on every launch.
+struct CutUnit {
+  int32_t b, hb, npieces, q0, q_len, pad0, pad1, pad2;
+};
+
+// Workgroups are dispatched to the 8 XCDs round-robin.  When the grid is a
+// multiple of 8, dispatch slot x runs logical workgroup (x % 8) * (G / 8) +
+// x / 8, so consecutive workgroups - the pieces of one unit, which read the
+// same query rows, and later the merge of those pieces - share one XCD's L2.
+__device__ __forceinline__ int pipe_logical(int x, int g) {
+  return (g & 7) == 0 ? (x & 7) * (g >> 3) + (x >> 3) : x;
+}
+
+// Direct global -> LDS load of 4 bytes per lane (LDS address M0 + 4 lane).
+__device__ __forceinline__ void lds_load4(const void *src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+template <int D>
+struct PipeStage {
+  static constexpr uint32_t KV = (uint32_t)dma::Stage<D>::BYTES;   // K then V
+  static constexpr uint32_t WLO = KV;                               // low dwords of the rows' words
+  static constexpr uint32_t WHI = KV + 4 * kPipeRows;               // high dwords
+  static constexpr uint32_t BYTES = KV + 8 * kPipeRows;
+};
+
+template <int D, typename OutT>
+__global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyParams p, CutUnit *cuts) {
+  extern __shared__ __align__(16) uint16_t lds[];
+  constexpr int NW = kPipeWaves;
+  using KV = dma::KvDma<D, NW>;
+  using PS = PipeStage<D>;
+  constexpr int IPW = KV::IPW;
+  constexpr int N_TILE = 2 * IPW + 1;   // vector memory instructions per wave and tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int wg = pipe_logical(blockIdx.x, p.grid);
+
+  const Piece pc = locate_piece(p, wg, lane);
+  if (pc.b < 0) {
+    if (tid == 0) cuts[wg] = CutUnit{-1, 0, 0, 0, 0, 0, 0, 0};
+    return;
+  }
+  const int b = pc.b, hb = pc.hb, kt0 = pc.kt0, kt1 = pc.kt1;
+  const bool complete = pc.npieces == 1;
+  const int64_t moff = pc.moff;
+
+  const dma::LaneOffsets<D> lo(lane);
+  const uint32_t lds0 = dma::lds_addr(lds);
+  const dma::LaneGather<D, NW, dma::SwzK<D>> lgk(wave, lane, p.s_slot);
+  const dma::LaneGather<D, NW, dma::SwzV<D>> lgv(wave, lane, p.s_slot);
+  const uint32_t page_bytes = (uint32_t)(p.s_page * 2), slot_bytes = (uint32_t)(p.s_slot * 2);
+  constexpr int kPageRunShift = __builtin_ctz(KV::RPI * KV::IPW);
+  const int r = wave * 32 + l32;            // this lane's row slot
+  const int rd = 64 * (wave & 3) + lane;    // the row whose word half this lane's DMA moves
+  const uint64_t *mask64 = (const uint64_t *)p.mask;
+
+  const int q0 = p.cu_seqlens_q[b], q_len = seq_q_len(p, b, q0);
+  if (tid == 0)
+    cuts[wg] = pc.k == 0 && pc.npieces > 1 ? CutUnit{b, hb, pc.npieces, q0, q_len, 0, 0, 0}
+                                           : CutUnit{-1, 0, 0, 0, 0, 0, 0, 0};
+  const int kv_true = p.kv_lens[b];
+  const int kv = min(kv_true, p.max_kv);
+  const int nwords = (kv_true + 63) / 64;
+  const int hh = min(r / p.qs, p.gh - 1), t = r % p.qs;
+  const bool row_ok = r / p.qs < p.gh && t < q_len;
+  const int h = hb * p.gh + hh;
+  const int g = (hb * p.gh) / p.group;
+  const int64_t tok = (int64_t)q0 + t;
+  const int td = rd % p.qs;
+  const bool rd_ok = rd / p.qs < p.gh && td < q_len;
+  const int64_t wrow = moff + (int64_t)td * nwords;   // word index of k-tile 0 of the DMA row
+  const int64_t lrow = moff + (int64_t)t * nwords;     // the same for this lane's own row
+  bf16x8 qf[D / 16];
+  load_q<D>(qf, (const uint16_t *)p.q + (tok * p.hq + h) * D, row_ok, hi);
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) oacc[m] = f32x16{};
+  float m_ref = neg_inf();
+  float lsum = 0.f;
+  const float c = p.scale_log2;
+  if (kv > 0 && kt0 < kt1) {
+    const uint16_t *kbase = (const uint16_t *)p.k + (int64_t)g * p.s_head;
+    const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)g * p.s_head;
+    const int32_t *pt = p.page_table + (int64_t)b * p.max_pages;
+    const int nt = kt1 - kt0;
+    // Tile kt0 + j into stage j % 4: K, V and one half of 64 rows' words.
+    auto issue = [&](int j) {
+      const int kt = kt0 + j;
+      const uint32_t st = lds0 + (uint32_t)(j & 3) * PS::BYTES;
+      const typename KV::Pages pg = KV::pages_uniform(pt, p.page_shift, kt, kv, wave);
+      if (kt * 64 + 64 <= kv) {
+        if (p.page_shift >= kPageRunShift) {
+          dma::issue_mat_page<D, NW, dma::SwzK<D>>(kbase, pg.id[0], lgk, p.page_shift, page_bytes, slot_bytes, kt,
+                                                   st, wave);
+          dma::issue_mat_page<D, NW, dma::SwzV<D>>(vbase, pg.id[0], lgv, p.page_shift, page_bytes, slot_bytes, kt,
+                                                   st + 2u * dma::Stage<D>::V_OFF, wave);
+        } else {
+          dma::issue_mat_fast<D, NW, dma::SwzK<D>, false>(kbase, pg, lgk, p.page_shift, page_bytes, slot_bytes, kt,
+                                                          kv, st, wave, lane);
+          dma::issue_mat_fast<D, NW, dma::SwzV<D>, false>(vbase, pg, lgv, p.page_shift, page_bytes, slot_bytes, kt,
+                                                          kv, st + 2u * dma::Stage<D>::V_OFF, wave, lane);
+        }
+      } else {
+        dma::issue_mat_fast<D, NW, dma::SwzK<D>, true>(kbase, pg, lgk, p.page_shift, page_bytes, slot_bytes, kt, kv,
+                                                       st, wave, lane);
+        dma::issue_mat_fast<D, NW, dma::SwzV<D>, true>(vbase, pg, lgv, p.page_shift, page_bytes, slot_bytes, kt, kv,
+                                                       st + 2u * dma::Stage<D>::V_OFF, wave, lane);
+      }
+      const int64_t idx = wrow + kt;
+      const uint64_t *src = rd_ok && idx < p.mask_numel ? mask64 + idx : mask64;
+      lds_load4((const uint32_t *)src + (wave >> 2),
+                st + ((wave >> 2) ? PS::WHI : PS::WLO) + 256u * (uint32_t)(wave & 3));
+    };
+    // This lane's row word of tile kt0 + j (after the barrier that publishes
+    // its stage); rows outside the unit or past mask_numel read 0.
+    auto word_of = [&](int j) -> uint64_t {
+      const uint32_t *w32 = (const uint32_t *)((const char *)lds + (uint32_t)(j & 3) * PS::BYTES);
+      const uint32_t lo_w = w32[PS::WLO / 4 + r], hi_w = w32[PS::WHI / 4 + r];
+      const bool ok = row_ok && lrow + kt0 + j < p.mask_numel;
+      return ok ? ((uint64_t)hi_w << 32) | lo_w : 0ull;
+    };
+    f32x16 sa[2], sb[2];
+    issue(0);
+    if (nt > 1) issue(1);
+    if (nt > 2) {
+      issue(2);
+      wait_vmem_n<N_TILE>();   // tiles 0 and 1 have landed
+    } else {
+      dma::wait_vmem();
+    }
+    __syncthreads();
+    uint64_t word_cur = word_of(0);
+    dma::qk_tile<D, (D > 64 ? 4 : D / 16)>(lds, lo, qf, sa);
+    auto step = [&](f32x16 (&scur)[2], f32x16 (&snxt)[2], int j) {
+      const int kt = kt0 + j;
+      const uint64_t wcur = word_cur;
+      if (j + 3 < nt) issue(j + 3);
+      const int kin = kv - kt * 64;
+      const uint64_t inb = low_bits(kin);
+      const uint64_t wm = wcur & inb;
+      // no masking when every row of the wave sees the whole tile
+      if (kin < 64 || __ballot(row_ok && wm != inb) != 0ull) apply_word(scur, wm, hi);
+      dma::qk_tile_free<D>((const uint16_t *)((const char *)lds + (uint32_t)((j + 1) & 3) * PS::BYTES), lo, qf,
+                           snxt);
+      float alpha, ps;
+      const bool any = softmax_tile(scur, m_ref, c, alpha);
+      bf16x8 pb[4];
+      dma::pack_p(scur, pb, ps);
+      asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]), "+v"(ps));
+      if (any) {
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) oacc[m] *= alpha;
+        lsum *= alpha;
+      }
+      lsum += ps;
+      dma::pv_tile_packed<D>((const uint16_t *)((const char *)lds + (uint32_t)(j & 3) * PS::BYTES), lo, pb, oacc);
+      // tile j + 2 has landed (tile j + 3 may still be in flight)
+      if (j + 3 < nt)
+        wait_vmem_n<N_TILE>();
+      else
+        dma::wait_vmem();
+      __syncthreads();
+      if (j + 1 < nt) word_cur = word_of(j + 1);
+    };
+    for (int j = 0; j < nt; j += 2) {
+      step(sa, sb, j);
+      if (j + 1 < nt) step(sb, sa, j + 1);
+    }
+  }
+  const float lt = sum_halves(lsum);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse = lt > 0.f ? (m_ref + __log2f(lt)) * kLn2 : neg_inf();
+  if (!row_ok) return;
+  if (complete) {
+    store_row<D, OutT>((OutT *)p.out + (tok * p.hq + h) * D, oacc, inv, hi);
+    if (p.lse && hi == 0) p.lse[tok * p.hq + h] = lse;
+  } else {
+    const int64_t row = (int64_t)wg * kPipeRows + r;
+    store_row<D, float>(p.ws_o + row * D, oacc, inv, hi);
+    if (hi == 0) p.ws_lse[row] = lse;
+  }
+}
+
+// Merges the pieces of a cut unit: block (i, c) with workgroup i the unit's
+// first piece takes 256 (row, 4 columns) items of the unit's 256 x D outputs
+// (item = c * 256 + thread, D / 4 items per row) and merges the pieces i,
+// i + 1, ... in order:
+// O = sum_s exp(LSE_s - M) O_s / sum_s exp(LSE_s - M), LSE = M + ln(sum).
+// Each pass issues the loads of kMergeBatch pieces before using them.
+constexpr int kMergeBatch = 8;
+
+template <int D, typename OutT>
+__global__ __launch_bounds__(256) void verify_pipe_combine(VerifyParams p, const CutUnit *cuts) {
+  const int wg = pipe_logical(blockIdx.x, p.grid);
+  const CutUnit cu = cuts[wg];
+  if (cu.b < 0) return;
+  const int hb = cu.hb, np = cu.npieces, q0 = cu.q0, q_len = cu.q_len;
+  const int item = blockIdx.y * 256 + threadIdx.x;
+  const int r = item / (D / 4), c4 = item % (D / 4);
+  const int t = r % p.qs;
+  if (r / p.qs >= p.gh || t >= q_len) return;
+  const int h = hb * p.gh + r / p.qs;
+  float m_run = neg_inf(), l_run = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < np; k0 += kMergeBatch) {
+    float lse_k[kMergeBatch];
+    f32x4 o_k[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const bool has = k0 + k < np;
+      const int64_t row = (int64_t)(wg + k0 + k) * kPipeRows + r;
+      lse_k[k] = has ? p.ws_lse[row] : neg_inf();
+      o_k[k] = has ? *(const f32x4 *)(p.ws_o + row * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float mx = m_run;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) mx = fmaxf(mx, lse_k[k]);
+    if (mx == neg_inf()) continue;
+    const float sc = __expf(m_run - mx);   // 0 while nothing was merged
+    l_run *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float wgt = __expf(lse_k[k] - mx);
+      l_run += wgt;
+      acc += wgt * o_k[k];
+    }
+    m_run = mx;
+  }
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const int64_t tok = (int64_t)q0 + t;
+  store4<OutT>((OutT *)p.out + (tok * p.hq + h) * D + 4 * c4, acc[0] * inv, acc[1] * inv, acc[2] * inv,
+               acc[3] * inv);
+  if (p.lse && c4 == 0) p.lse[tok * p.hq + h] = l_run > 0.f ? m_run + __logf(l_run) : neg_inf();
+}
+
+// Dense mask rows -> packed words (key j of a row -> bit j % 64 of word
+// j / 64), in the packed layout of the same sequences; bytes at or past
+// mask_numel read as 0.  One thread per (query row, word) of sequence
+// blockIdx.y; the sequence offsets of both layouts are prefix sums over the
+// earlier sequences.
+// Only rows below max_q are written (the kernel reads no others), and no
+// word at or past `cap`.
+__global__ __launch_bounds__(256) void dense_to_words(VerifyParams p, uint64_t *words, int64_t cap) {
+  const int b = blockIdx.y;
+  int64_t doff = 0, woff = 0;
+  for (int i = 0; i < b; ++i) {
+    const int64_t ql = p.cu_seqlens_q[i + 1] - p.cu_seqlens_q[i], kv = p.kv_lens[i];
+    doff += ql * kv;
+    woff += ql * ((kv + 63) / 64);
+  }
+  const int q_len = seq_q_len(p, b, p.cu_seqlens_q[b]), kv = p.kv_lens[b];
+  const int nw = (kv + 63) / 64;
+  const uint8_t *m8 = (const uint8_t *)p.mask;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < (int64_t)q_len * nw;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)(idx / nw), w = (int)(idx % nw);
+    const int64_t base = doff + (int64_t)t * kv + 64 * w;
+    const int nb = min(64, kv - 64 * w);
+    uint64_t bits = 0;
+    if (nb == 64 && base + 64 <= p.mask_numel) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 v;
+        __builtin_memcpy(&v, m8 + base + 16 * q, 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bits |= (uint64_t)nonzero_bytes4(v[e]) << (16 * q + 4 * e);
+      }
+    } else {
+      for (int j = 0; j < nb; ++j)
+        if (base + j < p.mask_numel && m8[base + j] != 0) bits |= 1ull << j;
+    }
+    if (woff + idx < cap) words[woff + idx] = bits;
+  }
+}
+
 // Launches kern over the (split, head group, sequence) grid with nw waves
 // per workgroup, then the merge of the split partials.
 template <int D, typename OutT, typename Kern>
@@ -818,11 +1248,106 @@ size_t workspace_bytes(const Shape &sh, int32_t batch, int32_t max_q, int32_t hq
   return (size_t)batch * sh.sp.max_splits * hq * max_q * (d + 1) * sizeof(float);
 }
 
+// Shape of a balanced tree-verify launch (verify_pipe_kernel): custom masks
+// over bf16 caches at d <= 128 whose pages hold a gather instruction's rows
+// (`pages_ok`), with GH query heads x max_q rows per unit filling more than
+// half of its eight waves (smaller row sets, e.g. decode, keep the split
+// kernels).
+struct PipeShape {
+  bool ok;
+  int gh, nhb, grid;
+};
+
+PipeShape pipe_shape(int batch, int hq, int hkv, int d, int max_q, int max_kv, int mode, bool pages_ok, bool kv8) {
+  PipeShape s{false, 1, 1, 1};
+  if ((mode != kDense && mode != kPacked) || kv8 || d > 128 || !pages_ok) return s;
+  const int group = hq / hkv;
+  int gh = 1;
+  for (int c = group; c >= 1; --c)
+    if (group % c == 0 && c * max_q <= kPipeRows) {
+      gh = c;
+      break;
+    }
+  if (gh * max_q <= kPipeRows / 2) return s;
+  const int64_t units = (int64_t)batch * (hq / gh);
+  const int64_t wmax = units * ((max_kv + 63) / 64);
+  if (wmax >= ((int64_t)1 << 30)) return s;
+  // at least one workgroup per unit (the partition needs it), else one per
+  // CU, never more than there are tiles
+  int64_t grid = units > kPipeGrid ? units : kPipeGrid;
+  if (grid > wmax) grid = wmax;
+  s.ok = true;
+  s.gh = gh;
+  s.nhb = hq / gh;
+  s.grid = (int)grid;
+  return s;
+}
+
+// Workspace of a balanced launch: one partial (O, LSE) slot of 256 rows per
+// workgroup, and room for a dense mask converted to packed words.
+struct PipeWs {
+  size_t o, lse, cuts, words, total;
+};
+
+PipeWs pipe_ws(const PipeShape &s, int32_t batch, int32_t max_q, int32_t max_kv, int32_t d) {
+  PipeWs w{0, 0, 0, 0, 0};
+  if (!s.ok) return w;
+  const size_t slots = (size_t)s.grid;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  w.o = 0;
+  w.lse = up(slots * kPipeRows * d * sizeof(float));
+  w.cuts = w.lse + up(slots * kPipeRows * sizeof(float));
+  w.words = w.cuts + up(slots * sizeof(CutUnit));
+  w.total = w.words + (size_t)batch * max_q * ((max_kv + 63) / 64) * sizeof(uint64_t);
+  return w;
+}
+
+template <int D, typename OutT>
+ma_status run_pipe(const VerifyArgs &a, VerifyParams prm, const PipeShape &ps) {
+  hipStream_t s = (hipStream_t)a.stream;
+  const PipeWs w = pipe_ws(ps, a.batch, a.max_q, a.max_kv, a.d);
+  char *ws = (char *)a.workspace;
+  prm.ws_o = (float *)(ws + w.o);
+  prm.ws_lse = (float *)(ws + w.lse);
+  CutUnit *cuts = (CutUnit *)(ws + w.cuts);
+  hipError_t e = hipSuccess;
+  if (prm.mode == kDense) {
+    // the dense rows become packed words first; the main kernel reads words
+    uint64_t *words = (uint64_t *)(ws + w.words);
+    const int64_t cap = (int64_t)a.batch * a.max_q * ((a.max_kv + 63) / 64);
+    const int64_t items = (int64_t)a.max_q * ((a.max_kv + 63) / 64);
+    const int chunks = (int)((items + 255) / 256 < 64 ? (items + 255) / 256 : 64);
+    hipLaunchKernelGGL(dense_to_words, dim3(chunks, a.batch), dim3(256), 0, s, prm, words, cap);
+    e = hipGetLastError();
+    if (e != hipSuccess) return set_error(MA_ERR_HIP, "mask conversion launch: %s", hipGetErrorString(e));
+    prm.mask = words;
+    prm.mask_numel = cap;
+    prm.mode = kPacked;
+  }
+  const size_t lds = (size_t)kPipeStages * PipeStage<D>::BYTES;
+  auto kern = verify_pipe_kernel<D, OutT>;
+  if (lds > 64 * 1024) {
+    e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+  }
+  hipLaunchKernelGGL(kern, dim3(ps.grid), dim3(kPipeWaves * 64), lds, s, prm, cuts);
+  e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify launch: %s", hipGetErrorString(e));
+  hipLaunchKernelGGL((verify_pipe_combine<D, OutT>), dim3(ps.grid, kPipeRows * (D / 4) / 256), dim3(256), 0, s, prm,
+                     (const CutUnit *)cuts);
+  e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify combine launch: %s", hipGetErrorString(e));
+  return MA_OK;
+}
+
 }  // namespace
 
 size_t verify_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq, int32_t hkv, int32_t d) {
   const Shape sh = shape_for(batch, hq, hkv, d, max_q, max_walk_tiles(kDense, 0, max_q, max_kv));
-  return workspace_bytes(sh, batch, max_q, hq, d);
+  const size_t split = workspace_bytes(sh, batch, max_q, hq, d);
+  const size_t pipe = pipe_ws(pipe_shape(batch, hq, hkv, d, max_q, max_kv, kDense, true, false), batch, max_q,
+                              max_kv, d).total;
+  return split > pipe ? split : pipe;
 }
 
 ma_status launch_verify(const VerifyArgs &a) {
@@ -868,6 +1393,17 @@ ma_status launch_verify(const VerifyArgs &a) {
   prm.scale = a.scale;
   prm.scale_log2 = a.scale * (a.kv8 ? a.k_descale : 1.f) * kLog2e;
   prm.v_scale = a.kv8 ? a.v_descale : 1.f;
+  const bool pipe_pages = uniform && a.s_page * 2 < ((int64_t)1 << 32);
+  const PipeShape ps = pipe_shape(a.batch, a.hq, a.hkv, a.d, a.max_q, a.max_kv, mode, pipe_pages, a.kv8 != 0);
+  if (ps.ok) {
+    prm.gh = ps.gh;
+    prm.nhb = ps.nhb;
+    prm.grid = ps.grid;
+    prm.batch = a.batch;
+    const bool f32 = a.out_dtype == MA_F32;
+    if (a.d == 64) return f32 ? run_pipe<64, float>(a, prm, ps) : run_pipe<64, uint16_t>(a, prm, ps);
+    return f32 ? run_pipe<128, float>(a, prm, ps) : run_pipe<128, uint16_t>(a, prm, ps);
+  }
   switch (a.d) {
     case 64: return run_d<64>(a, prm, sh);
     case 128: return run_d<128>(a, prm, sh);
