@@ -332,6 +332,26 @@ ma_status attn_verify_tree(const void *q, int64_t total_q, int32_t hq, const voi
                            int32_t out_dtype, float scale, void *workspace, size_t ws_bytes,
                            void *out, float *lse, void *stream);
 
+/* attn_verify_tree without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The scratch it needs lives in the
+ * library: one 64 MiB device array per GPU, held until the process ends
+ * (its address is looked up once per device on the first call there).
+ * Arguments, results and errors are those of attn_verify_tree; bounds whose
+ * attn_verify_tree_workspace exceeds 64 MiB are MA_ERR_SIZE.  The call
+ * allocates nothing (no hipMalloc, no hipFree) and needs no cleared memory:
+ * every scratch byte a launch reads it has written first.  All calls on one
+ * GPU share its scratch, so calls that can overlap on one GPU (on different
+ * streams without ordering between them) race; order them, e.g. on one
+ * stream. */
+ma_status attn_verify_tree_noalloc(const void *q, int64_t total_q, int32_t hq, const void *k_cache,
+                                   const void *v_cache, int32_t hkv, int32_t d, int32_t page_size,
+                                   const int64_t kv_strides[3], const int32_t *page_table, int32_t max_pages,
+                                   const int32_t *cu_seqlens_q, const int32_t *kv_lens, int32_t batch,
+                                   int32_t max_q, int32_t max_kv, int32_t mask_kind, const void *mask,
+                                   int64_t mask_numel, int32_t in_dtype, int32_t out_dtype, float scale, void *out,
+                                   float *lse, void *stream);
+
 /* Workspace bytes attn_decode needs for these bounds (the same bound serves
  * every mask kind; 0 when one split covers every context). */
 size_t attn_decode_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq, int32_t hkv,

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     BF16, F32, KIND, LIB, LIB_PATH, MaskAttnError, Plan, RANGE_BI_CAUSAL, RANGE_CAUSAL,
     RANGE_CHUNK_CAUSAL, RANGE_FULL, RANGE_INV_CAUSAL, TILE_FULL, TILE_PARTIAL, TILE_SKIP,
     attn_backward_masked, attn_backward_workspace, attn_prefill_masked_fp8, attn_decode, attn_decode_kv8, attn_decode_workspace, attn_prefill_masked, attn_verify_tree, attn_verify_tree_workspace,
+    attn_verify_tree_noalloc,
     mask_compile,
     mask_compile_host,
 )

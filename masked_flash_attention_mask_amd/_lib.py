@@ -24,6 +24,7 @@ TILE_SKIP, TILE_FULL, TILE_PARTIAL = 0, 1, 2
 EXPORTS = ["mask_compile", "mask_compile_host", "mask_plan_upload", "mask_plan_destroy",
            "mask_plan_info_get", "mask_plan_export", "mask_plan_serialize", "attn_prefill_masked",
            "attn_prefill_masked_fp8", "attn_backward_workspace", "attn_backward_masked", "attn_verify_tree_workspace", "attn_verify_tree",
+           "attn_verify_tree_noalloc",
            "attn_decode_workspace", "attn_decode", "attn_decode_kv8",
            "ma_status_string", "ma_last_error"]
 
@@ -80,6 +81,8 @@ def _load():
         "attn_verify_tree_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
         "attn_verify_tree": (i32, [vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp, i32, i32, i32,
                                    i32, vp, i64, i32, i32, f32, vp, sz, vp, vp, vp]),
+        "attn_verify_tree_noalloc": (i32, [vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp, i32, i32, i32,
+                                           i32, vp, i64, i32, i32, f32, vp, vp, vp]),
         "attn_decode_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
         "attn_decode": (i32, [vp, i64, i32, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                               vp, vp, i64, i32, i32, f32, vp, sz, vp, vp, vp]),
@@ -368,6 +371,33 @@ def attn_verify_tree(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, mas
         _dtype_code(out.dtype), float(scale), ws_ptr, ws_bytes, out.data_ptr(),
         lse.data_ptr() if lse is not False else None, _stream(stream))
     check(st, "attn_verify_tree")
+    return out, lse
+
+
+def attn_verify_tree_noalloc(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, mask, mask_kind, max_q,
+                             max_kv, scale, out=None, lse=None, out_dtype=None, stream=None):
+    """attn_verify_tree on the library's own per-GPU scratch (no workspace
+    argument; the library allocates nothing during the call)."""
+    import torch
+    total_q, hq, d = q.shape
+    hkv, page_size = k_cache.shape[2], k_cache.shape[1]
+    batch = kv_lens.shape[0]
+    strides = _cache_args(k_cache, v_cache)
+    for t in (q, page_table, cu_seqlens_q, kv_lens, mask):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("verify tensors must be contiguous device tensors")
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((total_q, hq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device)
+    st = LIB.attn_verify_tree_noalloc(
+        q.data_ptr(), total_q, hq, k_cache.data_ptr(), v_cache.data_ptr(), hkv, d, page_size, strides,
+        page_table.data_ptr(), page_table.shape[1], cu_seqlens_q.data_ptr(), kv_lens.data_ptr(), batch,
+        int(max_q), int(max_kv), KIND[mask_kind], mask.data_ptr(), mask.numel(), _dtype_code(q.dtype),
+        _dtype_code(out.dtype), float(scale), out.data_ptr(), lse.data_ptr() if lse is not False else None,
+        _stream(stream))
+    check(st, "attn_verify_tree_noalloc")
     return out, lse
 
 

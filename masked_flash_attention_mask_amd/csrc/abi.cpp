@@ -578,4 +578,29 @@ ma_status attn_verify_tree(const void *q, int64_t total_q, int32_t hq, const voi
                      workspace, ws_bytes, out, lse, stream);
 }
 
+ma_status attn_verify_tree_noalloc(const void *q, int64_t total_q, int32_t hq, const void *k_cache,
+                                   const void *v_cache, int32_t hkv, int32_t d, int32_t page_size,
+                                   const int64_t kv_strides[3], const int32_t *page_table, int32_t max_pages,
+                                   const int32_t *cu_seqlens_q, const int32_t *kv_lens, int32_t batch,
+                                   int32_t max_q, int32_t max_kv, int32_t mask_kind, const void *mask,
+                                   int64_t mask_numel, int32_t in_dtype, int32_t out_dtype, float scale, void *out,
+                                   float *lse, void *stream) {
+  clear_error();
+  ma_status st = check_small_q(q, k_cache, v_cache, out, page_table, hq, hkv, page_size, kv_strides, max_pages,
+                               scale, cu_seqlens_q, kv_lens, batch, max_q, max_kv, in_dtype, out_dtype, d, total_q);
+  if (st != MA_OK) return st;
+  if (mask_kind != MA_KIND_DENSE_BOOL && mask_kind != MA_KIND_PACKED_U64)
+    return set_error(MA_ERR_CONFLICT, "tree verify takes a custom mask (dense or packed), got kind %d", mask_kind);
+  if ((st = check_mask_rows(mask, mask_numel, total_q)) != MA_OK) return st;
+  const size_t need = verify_workspace(batch, max_q, max_kv, hq, hkv, d);
+  if (need > kVerifyScratchBytes)
+    return set_error(MA_ERR_SIZE, "these bounds need %zu bytes of scratch, the library holds %zu per GPU", need,
+                     kVerifyScratchBytes);
+  void *ws = nullptr;
+  if (need > 0 && (st = verify_scratch(&ws)) != MA_OK) return st;
+  return run_small_q(q, hq, k_cache, v_cache, hkv, d, page_size, kv_strides, page_table, max_pages, cu_seqlens_q,
+                     kv_lens, batch, max_q, max_kv, mask_kind, 0, nullptr, mask, mask_numel, out_dtype, scale, ws,
+                     need, out, lse, stream);
+}
+
 }  // extern "C"

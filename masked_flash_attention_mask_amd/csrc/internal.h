@@ -179,6 +179,11 @@ struct VerifyArgs {
 };
 size_t verify_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq, int32_t hkv,
                         int32_t d);
+// The library's own scratch for attn_verify_tree_noalloc: kVerifyScratchBytes
+// of device memory per GPU (a static device array), its address on the
+// current device in *out.
+constexpr size_t kVerifyScratchBytes = (size_t)64 << 20;
+ma_status verify_scratch(void **out);
 ma_status launch_verify(const VerifyArgs &a);
 
 }  // namespace maskattn

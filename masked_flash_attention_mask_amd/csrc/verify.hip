@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "internal.h"
@@ -1341,6 +1342,36 @@ ma_status run_pipe(const VerifyArgs &a, VerifyParams prm, const PipeShape &ps) {
 }
 
 }  // namespace
+
+// Scratch for callers that cannot allocate (attn_verify_tree_noalloc): one
+// array of kVerifyScratchBytes per GPU, held until the process ends.  Host
+// code never uses the array's name as an address: it asks the runtime for
+// each device's copy once (hipGetSymbolAddress, with that device current)
+// and passes that pointer to the kernels.
+static __device__ __align__(256) unsigned char scratch[kVerifyScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+ma_status verify_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return set_error(MA_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return set_error(MA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MA_OK;
+}
 
 size_t verify_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32_t hq, int32_t hkv, int32_t d) {
   const Shape sh = shape_for(batch, hq, hkv, d, max_q, max_walk_tiles(kDense, 0, max_q, max_kv));

@@ -216,3 +216,19 @@ def test_single_hip_runtime_in_process():
     assert r.returncode == 0, r.stderr
     libs = eval(r.stdout.strip().splitlines()[-1])
     assert len(libs) == 1, libs
+
+
+def test_verify_noalloc_refuses_bounds_beyond_its_scratch():
+    """The allocation-free tree verify holds 64 MiB of scratch per GPU:
+    bounds that need more are MA_ERR_SIZE before any HIP call; bad arguments
+    fail as for attn_verify_tree."""
+    need = ma.attn_verify_tree_workspace(64, 64, 1 << 20, 32, 8, 128)
+    assert need > 64 << 20
+    st = (ctypes.c_int64 * 3)(2048, 128, 128)
+    f = FAKE
+    args = lambda kind, numel: (f, 64 * 64, 32, f, f, 8, 128, 16, st, f, 65536, f, f, 64, 64, 1 << 20, kind, f,
+                                numel, L.BF16, L.F32, 0.1, f, None, None)
+    assert L.LIB.attn_verify_tree_noalloc(*args(L.KIND["packed"], 1 << 30)) == L.MA_ERR_SIZE
+    assert "scratch" in L.LIB.ma_last_error().decode()
+    assert L.LIB.attn_verify_tree_noalloc(*args(L.KIND["causal"], 1 << 30)) == L.MA_ERR_CONFLICT
+    assert L.LIB.attn_verify_tree_noalloc(*args(L.KIND["packed"], 100)) == L.MA_ERR_SIZE   # < one word per row
