@@ -113,7 +113,7 @@ ma_status mask_plan_upload(ma_plan *plan, void *stream) {
 
 ma_status mask_plan_destroy(ma_plan *plan) {
   if (!plan) return MA_OK;
-  if (plan->dbuf || plan->kbuf) plan_free_device(plan);
+  if (plan->dbuf || plan->kbuf || plan->staging) plan_free_device(plan);
   delete plan;
   return MA_OK;
 }

@@ -66,8 +66,14 @@ struct ma_plan {
   bool device_built = false;  // entries / word blocks laid out by the device classifier
   int device_id = -1;
   void *dbuf = nullptr;
-  size_t dbytes = 0;
+  size_t dbytes = 0;       // bytes the plan's layout uses
+  size_t dbuf_bytes = 0;   // bytes of the buffer (a reused buffer may be larger)
   size_t off_seqs = 0, off_aux = 0, off_items = 0, off_entries = 0, off_words = 0;
+  size_t off_extra = 0;          // scratch after the words (device classification: class bytes)
+  // pinned host staging of the last upload, kept until the plan is destroyed
+  // so that uploads are stream-ordered without waiting for them
+  void *staging = nullptr;
+  size_t staging_bytes = 0;
   int64_t cap_entries = 0, cap_wblk = 0;
 
   // k-major transpose for the backward (built on first use): one item per
@@ -87,7 +93,9 @@ void clear_error();
 ma_status validate_desc(const ma_mask_desc *d);
 ma_status plan_shape(const ma_mask_desc *d, ma_plan *p);
 ma_status compile_host(const ma_mask_desc *d, ma_plan *p);
-ma_status plan_alloc_device(ma_plan *p, int64_t cap_entries, int64_t cap_wblk);
+ma_status plan_alloc_device(ma_plan *p, int64_t cap_entries, int64_t cap_wblk, size_t extra = 0);
+// A pinned host buffer of at least `bytes` owned by the plan (p->staging).
+ma_status plan_staging(ma_plan *p, size_t bytes);
 ma_status plan_upload(ma_plan *p, void *stream);
 void fill_seqinfo(const ma_plan *p, int32_t kind, std::vector<SeqInfo> &s, std::vector<SeqAux> &aux);
 ma_status plan_fetch_host_view(const ma_plan *p, std::vector<Item> &items,

@@ -3,20 +3,25 @@
 // trip for the mask itself.  An HBM scan: the mask is read once, coalesced,
 // and only PARTIAL tiles' words are written.
 //
-// One workgroup (4 waves) per q-tile row, walking the row's k-tiles in chunks
-// of 64.  Per chunk:
-//  1. the words of every (row, tile) go to LDS.  Packed rows: a wave reads 64
-//     consecutive words of one row per load (512 B).  Dense rows: lanes 2i and
-//     2i + 1 read the two 32-byte halves of wave row i's 64 bytes of a tile,
-//     turn them into bits (SWAR), and two shuffles give row i's word to lane
-//     i; eight tiles are in flight per wave.
-//  2. each wave scans a quarter of the rows of all 64 tiles in LDS for "some
-//     bit set" and "every in-bounds row full"; wave 0 combines the quarters
-//     into FULL / SKIP / PARTIAL and appends the non-SKIP tiles, in ascending
-//     k order, to the row's entry list.
-//  3. the workgroup writes the PARTIAL tiles' word blocks (tile_q words each,
-//     one block per tile position).
+// Pass 1: one workgroup (4 waves) per (q-tile row, chunk of 64 k-tiles), all
+// chunks of all rows at once, gives each tile position its class byte and
+// writes the PARTIAL tiles' word blocks (tile_q words each, one block per
+// tile position):
+//  * packed rows (classify_packed_kernel): wave w takes 32 rows of the
+//    q-tile, lane l tile l of the chunk; a lane loads its tile's 32 words (a
+//    row's 64 words are one 512-byte load across the wave) and reduces them
+//    in registers; the four row groups combine through LDS flags.
+//  * dense rows (classify_kernel): lanes 2i and 2i + 1 read the two 32-byte
+//    halves of wave row i's 64 bytes of a tile, turn them into bits (SWAR),
+//    and two shuffles give row i's word to lane i (eight tiles in flight per
+//    wave); the words go through LDS, where each wave scans a quarter of the
+//    rows for "some bit set" and "every in-bounds row full".
+// Pass 2 (compact_kernel): one wave per q-tile row appends the row's non-SKIP
+// tiles, in ascending k order, to its entry list.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
 
 #include "internal.h"
 #include "kernels_common.h"
@@ -79,149 +84,244 @@ __device__ __forceinline__ uint32_t dense_half(const uint8_t *m8, int64_t base, 
   return bits;
 }
 
-__global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p) {
+// The sequence holding q-tile row r (aux row bases ascend): binary search.
+__device__ __forceinline__ int seq_of_row(const ClassifyParams &p, int r) {
+  int lo = 0, hi = p.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.aux[mid].row_base <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Pass 1 (dense masks): workgroup (q-tile row r, chunk ch) classifies k-tiles [64 ch,
+// 64 ch + 64) of row r: their classes go to cls (one byte per tile position)
+// and the PARTIAL tiles' word blocks to their tile positions.  Every chunk of
+// every row runs at once, so the whole mask is in flight.
+__global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p, uint8_t *cls) {
   extern __shared__ uint64_t wl[];                 // [kTiles][tile_q + 1] words of the chunk
   __shared__ uint32_t any_q[4][kTiles], full_q[4][kTiles];
   __shared__ uint8_t cls_s[kTiles];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.x;
-  int b = 0;
-  while (b + 1 < p.batch && r >= p.aux[b + 1].row_base) ++b;
+  const int b = seq_of_row(p, r);
   const SeqInfo sq = p.seqs[b];
   const SeqAux ax = p.aux[b];
   const int a = r - ax.row_base;
   const int nkt = sq.nkt, kv = sq.kv_len;
+  const int c0 = blockIdx.y * kTiles;
+  if (c0 >= nkt) return;
   const int tq = p.tile_q, ws = p.tile_q + 1;      // LDS row stride (words), padded
   const int ngroups = tq / 32;
   const int rows_in = min(tq, sq.q_len - a * tq);  // in-bounds rows of this q-tile
-  const int64_t ebase = ax.tile_base + (int64_t)a * nkt;  // entries / word blocks of this row
+  const int64_t ebase = ax.tile_base + (int64_t)a * nkt;  // tile positions of this row
   const int64_t nw = (kv + 63) / 64;
   const uint8_t *m8 = (const uint8_t *)p.mask;
   const uint64_t *m64 = (const uint64_t *)p.mask;
-  int32_t count = 0;
-
-  for (int c0 = 0; c0 < nkt; c0 += kTiles) {
-    const int cn = min(kTiles, nkt - c0);
-    // ---- 1. words of the chunk -> LDS
-    for (int rg = wave; rg < ngroups; rg += 4) {
-      const int row0 = a * tq + rg * 32;
-      if (p.packed) {
-        // lane l: tile c0 + l of row row0 + i, for the wave's 32 rows
-        const int c = c0 + lane;
-        const int keys = kv - 64 * c;
-        const uint64_t inb = keys >= 64 ? ~0ull : (keys <= 0 ? 0ull : ((1ull << keys) - 1ull));
-        // all 32 loads in flight before the first LDS store
-        uint64_t w[32];
+  const int cn = min(kTiles, nkt - c0);
+  // ---- 1. words of the chunk -> LDS
+  for (int rg = wave; rg < ngroups; rg += 4) {
+    const int row0 = a * tq + rg * 32;
+    if (p.packed) {
+      // lane l: tile c0 + l of row row0 + i, for the wave's 32 rows
+      const int c = c0 + lane;
+      const int keys = kv - 64 * c;
+      const uint64_t inb = keys >= 64 ? ~0ull : (keys <= 0 ? 0ull : ((1ull << keys) - 1ull));
+      // all 32 loads in flight before the first LDS store
+      uint64_t w[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int row = row0 + i;
-          const int64_t idx = ax.moff + (int64_t)row * nw + c;
-          w[i] = (lane < cn && row < sq.q_len && idx < p.mask_numel) ? m64[idx] : 0ull;
-        }
-        if (lane < cn) {
-#pragma unroll
-          for (int i = 0; i < 32; ++i)
-            wl[lane * ws + rg * 32 + i] = w[i] & inb & band_bits(row0 + i, c, sq.q_len, kv, p.window);
-        }
-      } else {
-        const int i = lane >> 1, half = lane & 1;
+      for (int i = 0; i < 32; ++i) {
         const int row = row0 + i;
-        const bool rv = row < sq.q_len;
-        const int64_t rbase = ax.moff + (int64_t)row * kv + 32 * half;
-        for (int ci0 = 0; ci0 < cn; ci0 += kDenseBatch) {
-          // Interior halves: two 16-byte loads each, all issued before any
-          // is used (other lanes load the mask's last 32 bytes and discard
-          // them).  Halves cut by kv_len, and masks under 32 bytes, take the
-          // byte loop.
-          dev::u32x4 v0[kDenseBatch], v1[kDenseBatch];
-          bool fast[kDenseBatch];
-          const bool can_fast = p.mask_numel >= 32;
-          const uint8_t *dummy = m8 + (can_fast ? p.mask_numel - 32 : 0);
-#pragma unroll
-          for (int u = 0; u < kDenseBatch; ++u) {
-            const int c = c0 + ci0 + u;
-            const int64_t base = rbase + 64 * c;
-            fast[u] = can_fast && rv && ci0 + u < cn && kv - 64 * c - 32 * half >= 32 && base + 32 <= p.mask_numel;
-            if (can_fast) {
-              const uint8_t *src = fast[u] ? m8 + base : dummy;
-              __builtin_memcpy(&v0[u], src, 16);
-              __builtin_memcpy(&v1[u], src + 16, 16);
-            } else {
-              v0[u] = dev::u32x4{0, 0, 0, 0};
-              v1[u] = dev::u32x4{0, 0, 0, 0};
-            }
-          }
-          uint32_t bits[kDenseBatch];
-#pragma unroll
-          for (int u = 0; u < kDenseBatch; ++u) {
-            uint32_t x = 0;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              x |= nonzero_bytes4(v0[u][c]) << (4 * c);
-              x |= nonzero_bytes4(v1[u][c]) << (16 + 4 * c);
-            }
-            bits[u] = fast[u] ? x : 0u;
-            const int c = c0 + ci0 + u;
-            const int nb = min(32, kv - 64 * c - 32 * half);
-            if (!fast[u] && rv && ci0 + u < cn && nb > 0) bits[u] = dense_half(m8, rbase + 64 * c, nb, p.mask_numel);
-          }
-#pragma unroll
-          for (int u = 0; u < kDenseBatch; ++u) {
-            const int src = 2 * (lane & 31);
-            const uint32_t lo = __shfl(bits[u], src, 64), hi = __shfl(bits[u], src + 1, 64);
-            if (lane < 32 && ci0 + u < cn)
-              wl[(ci0 + u) * ws + rg * 32 + lane] =
-                  (((uint64_t)hi << 32) | lo) & band_bits(row0 + lane, c0 + ci0 + u, sq.q_len, kv, p.window);
-          }
-        }
+        const int64_t idx = ax.moff + (int64_t)row * nw + c;
+        w[i] = (lane < cn && row < sq.q_len && idx < p.mask_numel) ? m64[idx] : 0ull;
       }
-    }
-    __syncthreads();
-    // ---- 2. per tile: some bit set / every in-bounds row full (wave = row quarter)
-    {
-      const int t = lane;
-      uint32_t any = 0, full = 1;
-      if (t < cn) {
-        const int keys = kv - 64 * (c0 + t);
-        const uint64_t inb = keys >= 64 ? ~0ull : ((1ull << keys) - 1ull);
-        const int q0 = wave * (tq / 4), q1 = min(q0 + tq / 4, rows_in);
-        for (int q = q0; q < q1; ++q) {
-          const uint64_t w = wl[t * ws + q];
-          any |= w != 0 ? 1u : 0u;
-          full &= w == inb ? 1u : 0u;
-        }
-      }
-      any_q[wave][t] = any;
-      full_q[wave][t] = full;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      int cls = MA_TILE_SKIP;
       if (lane < cn) {
-        const bool any = (any_q[0][lane] | any_q[1][lane] | any_q[2][lane] | any_q[3][lane]) != 0;
-        const bool full = (full_q[0][lane] & full_q[1][lane] & full_q[2][lane] & full_q[3][lane]) != 0;
-        cls = !any ? MA_TILE_SKIP : (full ? MA_TILE_FULL : MA_TILE_PARTIAL);
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          wl[lane * ws + rg * 32 + i] = w[i] & inb & band_bits(row0 + i, c, sq.q_len, kv, p.window);
       }
-      cls_s[lane] = (uint8_t)cls;
-      const uint64_t bal = __ballot(cls != MA_TILE_SKIP);
-      if (cls != MA_TILE_SKIP) {
-        const int c = c0 + lane;
-        const int before = __popcll(bal & ((1ull << lane) - 1ull));
-        p.entries[ebase + count + before] =
-            Entry{c | (cls << kClsShift), cls == MA_TILE_PARTIAL ? (int32_t)(ebase + c) : -1};
+    } else {
+      const int i = lane >> 1, half = lane & 1;
+      const int row = row0 + i;
+      const bool rv = row < sq.q_len;
+      const int64_t rbase = ax.moff + (int64_t)row * kv + 32 * half;
+      for (int ci0 = 0; ci0 < cn; ci0 += kDenseBatch) {
+        // Interior halves: two 16-byte loads each, all issued before any is
+        // used (other lanes load the mask's last 32 bytes and discard them).
+        // Halves cut by kv_len, and masks under 32 bytes, take the byte loop.
+        dev::u32x4 v0[kDenseBatch], v1[kDenseBatch];
+        bool fast[kDenseBatch];
+        const bool can_fast = p.mask_numel >= 32;
+        const uint8_t *dummy = m8 + (can_fast ? p.mask_numel - 32 : 0);
+#pragma unroll
+        for (int u = 0; u < kDenseBatch; ++u) {
+          const int c = c0 + ci0 + u;
+          const int64_t base = rbase + 64 * c;
+          fast[u] = can_fast && rv && ci0 + u < cn && kv - 64 * c - 32 * half >= 32 && base + 32 <= p.mask_numel;
+          if (can_fast) {
+            const uint8_t *src = fast[u] ? m8 + base : dummy;
+            __builtin_memcpy(&v0[u], src, 16);
+            __builtin_memcpy(&v1[u], src + 16, 16);
+          } else {
+            v0[u] = dev::u32x4{0, 0, 0, 0};
+            v1[u] = dev::u32x4{0, 0, 0, 0};
+          }
+        }
+        uint32_t bits[kDenseBatch];
+#pragma unroll
+        for (int u = 0; u < kDenseBatch; ++u) {
+          uint32_t x = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            x |= nonzero_bytes4(v0[u][c]) << (4 * c);
+            x |= nonzero_bytes4(v1[u][c]) << (16 + 4 * c);
+          }
+          bits[u] = fast[u] ? x : 0u;
+          const int c = c0 + ci0 + u;
+          const int nb = min(32, kv - 64 * c - 32 * half);
+          if (!fast[u] && rv && ci0 + u < cn && nb > 0) bits[u] = dense_half(m8, rbase + 64 * c, nb, p.mask_numel);
+        }
+#pragma unroll
+        for (int u = 0; u < kDenseBatch; ++u) {
+          const int src = 2 * (lane & 31);
+          const uint32_t lo = __shfl(bits[u], src, 64), hi = __shfl(bits[u], src + 1, 64);
+          if (lane < 32 && ci0 + u < cn)
+            wl[(ci0 + u) * ws + rg * 32 + lane] =
+                (((uint64_t)hi << 32) | lo) & band_bits(row0 + lane, c0 + ci0 + u, sq.q_len, kv, p.window);
+        }
       }
-      count += __popcll(bal);
     }
-    __syncthreads();
-    // ---- 3. word blocks of the PARTIAL tiles
-    for (int idx = tid; idx < cn * tq; idx += kThreads) {
-      const int t = idx / tq, q = idx - t * tq;
-      if (cls_s[t] == MA_TILE_PARTIAL) p.words[(ebase + c0 + t) * tq + q] = wl[t * ws + q];
-    }
-    __syncthreads();
   }
-  if (tid == 0)
-    p.items[p.num_rows - 1 - r] = Item{b, a, (int32_t)ebase, (int32_t)(ebase + count)};
+  __syncthreads();
+  // ---- 2. per tile: some bit set / every in-bounds row full (wave = row quarter)
+  {
+    const int t = lane;
+    uint32_t any = 0, full = 1;
+    if (t < cn) {
+      const int keys = kv - 64 * (c0 + t);
+      const uint64_t inb = keys >= 64 ? ~0ull : ((1ull << keys) - 1ull);
+      const int q0 = wave * (tq / 4), q1 = min(q0 + tq / 4, rows_in);
+      for (int q = q0; q < q1; ++q) {
+        const uint64_t w = wl[t * ws + q];
+        any |= w != 0 ? 1u : 0u;
+        full &= w == inb ? 1u : 0u;
+      }
+    }
+    any_q[wave][t] = any;
+    full_q[wave][t] = full;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int c = MA_TILE_SKIP;
+    if (lane < cn) {
+      const bool any = (any_q[0][lane] | any_q[1][lane] | any_q[2][lane] | any_q[3][lane]) != 0;
+      const bool full = (full_q[0][lane] & full_q[1][lane] & full_q[2][lane] & full_q[3][lane]) != 0;
+      c = !any ? MA_TILE_SKIP : (full ? MA_TILE_FULL : MA_TILE_PARTIAL);
+      cls[ebase + c0 + lane] = (uint8_t)c;
+    }
+    cls_s[lane] = (uint8_t)c;
+  }
+  __syncthreads();
+  // ---- 3. word blocks of the PARTIAL tiles
+  for (int idx = tid; idx < cn * tq; idx += kThreads) {
+    const int t = idx / tq, q = idx - t * tq;
+    if (cls_s[t] == MA_TILE_PARTIAL) p.words[(ebase + c0 + t) * tq + q] = wl[t * ws + q];
+  }
+}
+
+// Pass 1 for packed masks, without LDS staging: workgroup (q-tile row r,
+// chunk ch), wave w takes the rows [32 w, 32 w + 32) of the q-tile and lane l
+// tile 64 ch + l: the lane loads its tile's 32 words (row-contiguous across
+// lanes: one 512-byte load per row) and reduces them in registers to "some
+// bit set" / "every in-bounds row full"; the row quarters combine through a
+// few LDS flags, and the lanes of PARTIAL tiles write their words from
+// registers.
+__global__ __launch_bounds__(kThreads) void classify_packed_kernel(ClassifyParams p, uint8_t *cls) {
+  __shared__ uint32_t any_q[4][kTiles], full_q[4][kTiles];
+  __shared__ uint8_t cls_s[kTiles];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.x;
+  const int b = seq_of_row(p, r);
+  const SeqInfo sq = p.seqs[b];
+  const SeqAux ax = p.aux[b];
+  const int a = r - ax.row_base;
+  const int nkt = sq.nkt, kv = sq.kv_len;
+  const int c0 = blockIdx.y * kTiles;
+  if (c0 >= nkt) return;
+  const int tq = p.tile_q;
+  const int cn = min(kTiles, nkt - c0);
+  const int64_t ebase = ax.tile_base + (int64_t)a * nkt;
+  const int64_t nw = (kv + 63) / 64;
+  const uint64_t *m64 = (const uint64_t *)p.mask;
+  const int c = c0 + lane;
+  const int keys = kv - 64 * c;
+  const uint64_t inb = keys >= 64 ? ~0ull : (keys <= 0 ? 0ull : ((1ull << keys) - 1ull));
+  const int row0 = a * tq + wave * 32;
+  const bool wave_rows = wave * 32 < tq;
+  uint64_t w[32];
+  uint32_t any = 0, full = 1;
+  if (wave_rows) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int row = row0 + i;
+      const int64_t idx = ax.moff + (int64_t)row * nw + c;
+      w[i] = (lane < cn && row < sq.q_len && idx < p.mask_numel) ? m64[idx] : 0ull;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      w[i] &= inb & band_bits(row0 + i, c, sq.q_len, kv, p.window);
+      if (row0 + i < sq.q_len) {
+        any |= w[i] != 0 ? 1u : 0u;
+        full &= w[i] == inb ? 1u : 0u;
+      }
+    }
+  }
+  any_q[wave][lane] = any;
+  full_q[wave][lane] = full;
+  __syncthreads();
+  if (wave == 0) {
+    int k = MA_TILE_SKIP;
+    if (lane < cn) {
+      const bool an = (any_q[0][lane] | any_q[1][lane] | any_q[2][lane] | any_q[3][lane]) != 0;
+      const bool fu = (full_q[0][lane] & full_q[1][lane] & full_q[2][lane] & full_q[3][lane]) != 0;
+      k = !an ? MA_TILE_SKIP : (fu ? MA_TILE_FULL : MA_TILE_PARTIAL);
+      cls[ebase + c] = (uint8_t)k;
+    }
+    cls_s[lane] = (uint8_t)k;
+  }
+  __syncthreads();
+  if (wave_rows && lane < cn && cls_s[lane] == MA_TILE_PARTIAL) {
+    uint64_t *dst = p.words + (ebase + c) * tq + wave * 32;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) dst[i] = w[i];
+  }
+}
+
+// Pass 2: one wave per q-tile row appends the row's non-SKIP tiles, in
+// ascending k order, to its entry list and writes its work item (rows in
+// reverse order: the longest rows of causal-like masks first).
+__global__ __launch_bounds__(64) void compact_kernel(ClassifyParams p, const uint8_t *cls) {
+  const int lane = threadIdx.x;
+  const int r = blockIdx.x;
+  const int b = seq_of_row(p, r);
+  const SeqInfo sq = p.seqs[b];
+  const SeqAux ax = p.aux[b];
+  const int a = r - ax.row_base;
+  const int nkt = sq.nkt;
+  const int64_t ebase = ax.tile_base + (int64_t)a * nkt;
+  int32_t count = 0;
+  for (int c0 = 0; c0 < nkt; c0 += 64) {
+    const int c = c0 + lane;
+    const int k = c < nkt ? cls[ebase + c] : MA_TILE_SKIP;
+    const uint64_t bal = __ballot(k != MA_TILE_SKIP);
+    if (k != MA_TILE_SKIP) {
+      const int before = __popcll(bal & ((1ull << lane) - 1ull));
+      p.entries[ebase + count + before] = Entry{c | (k << kClsShift), k == MA_TILE_PARTIAL ? (int32_t)(ebase + c) : -1};
+    }
+    count += __popcll(bal);
+  }
+  if (lane == 0) p.items[p.num_rows - 1 - r] = Item{b, a, (int32_t)ebase, (int32_t)(ebase + count)};
 }
 
 }  // namespace
@@ -229,19 +329,25 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p) {
 ma_status launch_classify(ma_plan *p, const void *mask, int32_t kind, int64_t mask_numel, int32_t window,
                           void *stream) {
   if (p->num_tiles > INT32_MAX) return set_error(MA_ERR_UNSUPPORTED, "too many tiles for a device-built plan");
-  ma_status st = plan_alloc_device(p, p->num_tiles, p->num_tiles);
+  // one class byte per tile position after the word blocks (pass 1 -> pass 2)
+  ma_status st = plan_alloc_device(p, p->num_tiles, p->num_tiles, (size_t)p->num_tiles);
   if (st != MA_OK) return st;
   std::vector<SeqInfo> seqs;
   std::vector<SeqAux> aux;
   fill_seqinfo(p, kind, seqs, aux);
+  // The metadata goes through a pinned staging buffer the plan keeps until
+  // it is destroyed: the copy is stream-ordered and nothing waits for it.
+  const size_t meta = sizeof(SeqInfo) * seqs.size() + sizeof(SeqAux) * aux.size();
+  if ((st = plan_staging(p, meta)) != MA_OK) return st;
+  char *h = (char *)p->staging;
+  memcpy(h, seqs.data(), sizeof(SeqInfo) * seqs.size());
+  memcpy(h + sizeof(SeqInfo) * seqs.size(), aux.data(), sizeof(SeqAux) * aux.size());
   hipStream_t s = (hipStream_t)stream;
   char *base = (char *)p->dbuf;
-  hipError_t e = hipMemcpyAsync(base + p->off_seqs, seqs.data(), sizeof(SeqInfo) * seqs.size(),
-                                hipMemcpyHostToDevice, s);
+  hipError_t e = hipMemcpyAsync(base + p->off_seqs, h, sizeof(SeqInfo) * seqs.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
-    e = hipMemcpyAsync(base + p->off_aux, aux.data(), sizeof(SeqAux) * aux.size(), hipMemcpyHostToDevice, s);
-  // The host vectors die with this call: wait for the two small copies.
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
+    e = hipMemcpyAsync(base + p->off_aux, h + sizeof(SeqInfo) * seqs.size(), sizeof(SeqAux) * aux.size(),
+                       hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "plan metadata upload: %s", hipGetErrorString(e));
   p->on_device = true;
   p->device_built = true;
@@ -259,14 +365,25 @@ ma_status launch_classify(ma_plan *p, const void *mask, int32_t kind, int64_t ma
   prm.tile_q = p->tile_q;
   prm.packed = kind == MA_KIND_PACKED_U64 ? 1 : 0;
   prm.window = window;
-  const size_t lds = (size_t)kTiles * (p->tile_q + 1) * sizeof(uint64_t);
-  e = hipSuccess;
-  if (lds > 64 * 1024)
-    e = hipFuncSetAttribute((const void *)classify_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
-  hipLaunchKernelGGL(classify_kernel, dim3(p->num_rows), dim3(kThreads), lds, s, prm);
+  uint8_t *cls = (uint8_t *)(base + p->off_extra);
+  int32_t max_nkt = 1;
+  for (int b = 0; b < p->batch; ++b) max_nkt = std::max(max_nkt, p->nkt[b]);
+  const dim3 grid(p->num_rows, (max_nkt + kTiles - 1) / kTiles);
+  if (prm.packed) {
+    hipLaunchKernelGGL(classify_packed_kernel, grid, dim3(kThreads), 0, s, prm, cls);
+  } else {
+    const size_t lds = (size_t)kTiles * (p->tile_q + 1) * sizeof(uint64_t);
+    e = hipSuccess;
+    if (lds > 64 * 1024)
+      e = hipFuncSetAttribute((const void *)classify_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+    hipLaunchKernelGGL(classify_kernel, grid, dim3(kThreads), lds, s, prm, cls);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "classify launch: %s", hipGetErrorString(e));
+  hipLaunchKernelGGL(compact_kernel, dim3(p->num_rows), dim3(64), 0, s, prm, (const uint8_t *)cls);
+  e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MA_ERR_HIP, "classify compaction launch: %s", hipGetErrorString(e));
   return MA_OK;
 }
 

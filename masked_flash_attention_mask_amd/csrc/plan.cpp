@@ -13,6 +13,8 @@
 // byte-identical plans.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
@@ -503,7 +505,91 @@ ma_status compile_host(const ma_mask_desc *d, ma_plan *p) {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-ma_status plan_alloc_device(ma_plan *p, int64_t cap_entries, int64_t cap_wblk) {
+// Buffers of destroyed plans are kept for the next plans (device buffers per
+// device, pinned host staging buffers), so that compiling a mask in steady
+// state allocates nothing: a device-classified plan reserves a word block per
+// tile (as much memory as the packed mask), and hipMalloc / hipHostMalloc /
+// hipFree of that size cost far more than the classification itself.  A
+// buffer is only returned to the cache after a device synchronisation (the
+// plan's destruction waits, as hipFree did), and is reused for a request of
+// at least half its size.  At most kCacheEntries buffers of each kind and
+// kCacheBytes of device memory are held; the rest is freed.
+namespace {
+constexpr size_t kCacheEntries = 4;
+constexpr size_t kCacheBytes = (size_t)2 << 30;
+struct CachedBuf {
+  void *ptr;
+  size_t bytes;
+  int dev;   // -1: pinned host memory
+};
+std::mutex g_cache_mu;
+std::vector<CachedBuf> g_cache;
+
+void *cache_take(size_t bytes, int dev, size_t *got) {
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  int best = -1;
+  for (size_t i = 0; i < g_cache.size(); ++i) {
+    const CachedBuf &c = g_cache[i];
+    if (c.dev == dev && c.bytes >= bytes && c.bytes <= 2 * bytes + (1 << 20) &&
+        (best < 0 || c.bytes < g_cache[best].bytes))
+      best = (int)i;
+  }
+  if (best < 0) return nullptr;
+  void *ptr = g_cache[best].ptr;
+  *got = g_cache[best].bytes;
+  g_cache.erase(g_cache.begin() + best);
+  return ptr;
+}
+
+void release(void *ptr, int dev) {
+  if (dev < 0) {
+    (void)hipHostFree(ptr);
+    return;
+  }
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  if (cur != dev) (void)hipSetDevice(dev);
+  (void)hipFree(ptr);
+  if (cur != dev) (void)hipSetDevice(cur);
+}
+
+// The caller has synchronised the device the buffer was last used on.
+void cache_put(void *ptr, size_t bytes, int dev) {
+  std::vector<CachedBuf> drop;
+  {
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    g_cache.push_back(CachedBuf{ptr, bytes, dev});
+    size_t dev_bytes = 0, n_dev = 0, n_host = 0;
+    for (const CachedBuf &c : g_cache) {
+      if (c.dev >= 0) {
+        dev_bytes += c.bytes;
+        ++n_dev;
+      } else {
+        ++n_host;
+      }
+    }
+    // drop the oldest entries beyond the limits
+    for (size_t i = 0; i < g_cache.size();) {
+      const bool is_dev = g_cache[i].dev >= 0;
+      if ((is_dev && (n_dev > kCacheEntries || dev_bytes > kCacheBytes)) || (!is_dev && n_host > kCacheEntries)) {
+        if (is_dev) {
+          --n_dev;
+          dev_bytes -= g_cache[i].bytes;
+        } else {
+          --n_host;
+        }
+        drop.push_back(g_cache[i]);
+        g_cache.erase(g_cache.begin() + i);
+      } else {
+        ++i;
+      }
+    }
+  }
+  for (const CachedBuf &c : drop) release(c.ptr, c.dev);
+}
+}  // namespace
+
+ma_status plan_alloc_device(ma_plan *p, int64_t cap_entries, int64_t cap_wblk, size_t extra) {
   size_t off = 0;
   p->off_seqs = off;
   off = align_up(off + sizeof(SeqInfo) * p->batch, 256);
@@ -515,7 +601,10 @@ ma_status plan_alloc_device(ma_plan *p, int64_t cap_entries, int64_t cap_wblk) {
   off = align_up(off + sizeof(Entry) * (size_t)std::max<int64_t>(cap_entries, 1), 256);
   p->off_words = off;
   off = align_up(off + sizeof(uint64_t) * (size_t)p->tile_q * (size_t)std::max<int64_t>(cap_wblk, 1), 256);
-  if (p->dbuf && p->dbytes >= off) {
+  p->off_extra = off;
+  off = align_up(off + extra, 256);
+  if (p->dbuf && p->dbuf_bytes >= off) {
+    p->dbytes = off;
     p->cap_entries = cap_entries;
     p->cap_wblk = cap_wblk;
     return MA_OK;
@@ -527,13 +616,19 @@ ma_status plan_alloc_device(ma_plan *p, int64_t cap_entries, int64_t cap_wblk) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  e = hipMalloc(&p->dbuf, off);
-  if (e != hipSuccess) {
-    p->dbuf = nullptr;
-    return set_error(MA_ERR_NOMEM, "hipMalloc(%zu) for the plan: %s", off, hipGetErrorString(e));
+  size_t got = 0;
+  p->dbuf = cache_take(off, dev, &got);
+  if (!p->dbuf) {
+    e = hipMalloc(&p->dbuf, off);
+    if (e != hipSuccess) {
+      p->dbuf = nullptr;
+      return set_error(MA_ERR_NOMEM, "hipMalloc(%zu) for the plan: %s", off, hipGetErrorString(e));
+    }
+    got = off;
   }
   p->device_id = dev;
   p->dbytes = off;
+  p->dbuf_bytes = got;
   p->cap_entries = cap_entries;
   p->cap_wblk = cap_wblk;
   return MA_OK;
@@ -551,19 +646,42 @@ void fill_seqinfo(const ma_plan *p, int32_t kind, std::vector<SeqInfo> &s, std::
   }
 }
 
+ma_status plan_staging(ma_plan *p, size_t bytes) {
+  if (p->staging && p->staging_bytes >= bytes) return MA_OK;
+  if (p->staging) {
+    // an earlier upload may still read it
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+    (void)hipHostFree(p->staging);
+    p->staging = nullptr;
+    p->staging_bytes = 0;
+  }
+  size_t got = 0;
+  p->staging = cache_take(bytes, -1, &got);
+  if (!p->staging) {
+    hipError_t e = hipHostMalloc(&p->staging, bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      p->staging = nullptr;
+      return set_error(MA_ERR_NOMEM, "hipHostMalloc(%zu): %s", bytes, hipGetErrorString(e));
+    }
+    got = bytes;
+  }
+  p->staging_bytes = got;
+  return MA_OK;
+}
+
 ma_status plan_upload(ma_plan *p, void *stream) {
   if (p->on_device) return MA_OK;
   if (!p->host_valid) return set_error(MA_ERR_INVALID, "plan has neither a host nor a device copy");
   ma_status st = plan_alloc_device(p, (int64_t)p->entries.size(), p->num_wblk);
   if (st != MA_OK) return st;
-  // Stage the whole plan in one pinned host buffer so one copy moves it.
+  // Stage the whole plan in one pinned host buffer (kept by the plan until it
+  // is destroyed) so one stream-ordered copy moves it and nothing waits.
   std::vector<SeqInfo> seqs;
   std::vector<SeqAux> aux;
   fill_seqinfo(p, MA_KIND_PACKED_U64, seqs, aux);
-  void *staging = nullptr;
-  hipError_t e = hipHostMalloc(&staging, p->dbytes, hipHostMallocDefault);
-  if (e != hipSuccess) return set_error(MA_ERR_NOMEM, "hipHostMalloc(%zu): %s", p->dbytes, hipGetErrorString(e));
-  char *h = (char *)staging;
+  if ((st = plan_staging(p, p->dbytes)) != MA_OK) return st;
+  char *h = (char *)p->staging;
   memset(h, 0, p->dbytes);
   memcpy(h + p->off_seqs, seqs.data(), sizeof(SeqInfo) * seqs.size());
   memcpy(h + p->off_aux, aux.data(), sizeof(SeqAux) * aux.size());
@@ -571,9 +689,7 @@ ma_status plan_upload(ma_plan *p, void *stream) {
   memcpy(h + p->off_entries, p->entries.data(), sizeof(Entry) * p->entries.size());
   memcpy(h + p->off_words, p->words.data(), sizeof(uint64_t) * p->words.size());
   hipStream_t s = (hipStream_t)stream;
-  e = hipMemcpyAsync(p->dbuf, staging, p->dbytes, hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);  // staging is freed below
-  (void)hipHostFree(staging);
+  hipError_t e = hipMemcpyAsync(p->dbuf, h, p->dbytes, hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "plan upload: %s", hipGetErrorString(e));
   p->on_device = true;
   return MA_OK;
@@ -667,11 +783,17 @@ void plan_free_device(ma_plan *p) {
   (void)hipGetDevice(&cur);
   const bool other = p->device_id >= 0 && p->device_id != cur;
   if (other) (void)hipSetDevice(p->device_id);
-  if (p->dbuf) (void)hipFree(p->dbuf);
+  // nothing queued may still use the buffers once they are handed on
+  (void)hipDeviceSynchronize();
+  if (p->dbuf) cache_put(p->dbuf, p->dbuf_bytes ? p->dbuf_bytes : p->dbytes, p->device_id);
   if (p->kbuf) (void)hipFree(p->kbuf);
+  if (p->staging) cache_put(p->staging, p->staging_bytes, -1);
   if (other) (void)hipSetDevice(cur);
   p->dbuf = nullptr;
   p->kbuf = nullptr;
+  p->staging = nullptr;
+  p->staging_bytes = 0;
+  p->dbuf_bytes = 0;
 }
 
 }  // namespace maskattn

@@ -322,3 +322,22 @@ def test_config3b_full_size_sampled_and_not_vacuous():
     g1, _, _ = run_prefill(w1, device_inputs(w1), "causal")
     ref1, _ = oracle(w1, "causal", heads=[3], rows=rows)
     assert max_abs_err(g1, ref1) <= TOL_BF16
+
+
+def test_device_classify_full_size_block_mask():
+    """The 32768 x 29576 block mask with 50 triangles, classified on the GPU
+    from its packed and dense forms (every k-tile chunk of every q-tile row at
+    once), gives the host compiler's classes and words bit for bit."""
+    w = W.config5()
+    q, k = int(w.q_lens[0]), int(w.kv_lens[0])
+    words = w.masks["custom_packed"].data
+    host = ma.mask_compile_host("packed", w.cu_seqlens_q, w.kv_lens, mask=words)
+    hc, hw = host.export()
+    dense = np.unpackbits(words.view(np.uint8).reshape(q, -1), axis=1, bitorder="little")[:, :k]
+    for kind, data in (("packed", words.view(np.int64)), ("dense", np.ascontiguousarray(dense).reshape(-1))):
+        _say("full-size device classify", kind)
+        p = ma.mask_compile(kind, w.cu_seqlens_q, w.kv_lens, mask=torch.from_numpy(np.ascontiguousarray(data)).cuda())
+        dc, dw = p.export()
+        assert np.array_equal(dc, hc), kind
+        assert np.array_equal(dw, hw), kind
+        del p
