@@ -746,6 +746,30 @@ def fp8_lines(steps, warmup):
                           "flops_per_step": 4.0 * d * hq * n_unmasked,
                           "kernel": "prefill_fp8_kernel<128,bf16>"}), flush=True)
         del plan
+    # the Gemma2-like layers (d 256): window 4096 and global causal
+    for layer in (0, 1):
+        w3 = W.config3b(layer)
+        name = "window" if layer == 0 else "causal"
+        g8 = W.fp8_inputs(w3)
+        dev3 = {k: torch.from_numpy(np.ascontiguousarray(g8[k])).cuda() for k in ("q8", "k8", "v8")}
+        pt3 = torch.from_numpy(w3.page_table).cuda().contiguous()
+        out3 = torch.empty(dev3["q8"].shape, dtype=torch.bfloat16, device="cuda")
+        lse3 = torch.empty(dev3["q8"].shape[:2], dtype=torch.float32, device="cuda")
+        kind, kw = plan_kwargs(w3, name)
+        plan = ma.mask_compile(kind, w3.cu_seqlens_q, w3.kv_lens, **kw)
+
+        def step3():
+            ma.attn_prefill_masked_fp8(plan, dev3["q8"], dev3["k8"], dev3["v8"], pt3, w3.scale, g8["q_s"], g8["k_s"],
+                                       g8["v_s"], out=out3, lse=lse3)
+        ms = time_steps(step3, steps, warmup, stream)
+        n_unmasked = count_unmasked(w3, name)
+        tf = 4.0 * w3.d * w3.hq * n_unmasked / (ms * 1e-3) / 1e12
+        print(json.dumps({"workload": f"prefill_fp8_gemma2_l{layer}_16k", "mask": name, "ms": round(ms, 4),
+                          "tflops": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                          "pct_of_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+                          "flops_per_step": 4.0 * w3.d * w3.hq * n_unmasked,
+                          "kernel": "prefill_fp8_kernel<256,bf16>"}), flush=True)
+        del plan, dev3
 
 
 def classify_lines(steps):

@@ -150,8 +150,15 @@ struct Fp8Lds {
   static constexpr int BYTES = 4 * SLOT;
 };
 
+// Waves per SIMD: two; one at d = 256, whose O accumulators alone take 128
+// registers per lane.
+template <int D>
+constexpr int fp8_occupancy() {
+  return D == 256 ? 1 : 2;
+}
+
 template <int D, typename OutT>
-__global__ __launch_bounds__(256, 2) void prefill_fp8_kernel(Fp8Params p) {
+__global__ __launch_bounds__(256, (fp8_occupancy<D>())) void prefill_fp8_kernel(Fp8Params p) {
   constexpr int BQ = 128, NW = 4;
   using St = Fp8Stage<D>;
   using L = Fp8Lds<D>;
@@ -345,7 +352,9 @@ ma_status launch_d(const Fp8Params &prm, int grid, void *stream) {
 
 }  // namespace
 
-int32_t fp8_rows_per_gather(int32_t d) { return d == 64 ? Fp8Stage<64>::RPI : Fp8Stage<128>::RPI; }
+int32_t fp8_rows_per_gather(int32_t d) {
+  return d == 64 ? Fp8Stage<64>::RPI : (d == 128 ? Fp8Stage<128>::RPI : Fp8Stage<256>::RPI);
+}
 
 ma_status launch_prefill_fp8(const Fp8Args &a) {
   const ma_plan *pl = a.plan;
@@ -378,8 +387,9 @@ ma_status launch_prefill_fp8(const Fp8Args &a) {
   switch (a.d) {
     case 64: return f32 ? launch_d<64, float>(prm, grid, a.stream) : launch_d<64, uint16_t>(prm, grid, a.stream);
     case 128: return f32 ? launch_d<128, float>(prm, grid, a.stream) : launch_d<128, uint16_t>(prm, grid, a.stream);
+    case 256: return f32 ? launch_d<256, float>(prm, grid, a.stream) : launch_d<256, uint16_t>(prm, grid, a.stream);
   }
-  return set_error(MA_ERR_UNSUPPORTED, "fp8 head_dim %d (supported: 64, 128)", a.d);
+  return set_error(MA_ERR_UNSUPPORTED, "fp8 head_dim %d (supported: 64, 128, 256)", a.d);
 }
 
 }  // namespace maskattn

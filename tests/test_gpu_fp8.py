@@ -66,7 +66,7 @@ def _check(w, wd, name, out, lse, heads=None, rows=None):
     return worst
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fp8_mask_kinds(d):
     w = W.backward_small(seed=90 + d, d=d, hq=4, hkv=2)
     f8 = W.fp8_inputs(w)
@@ -122,17 +122,17 @@ def test_fp8_full_size_sampled():
     _say("worst err / bound", worst)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fp8_page_sizes_bit_identical(d):
-    """Pages of the minimum size (one gather instruction's rows: 8 keys at
-    d 128, 16 at d 64), 16, 32 and 64 keys (one page per wave's run from 16
+    """Pages of the minimum size (one gather instruction's rows: 4 keys at
+    d 256, 8 at d 128, 16 at d 64), 16, 32 and 64 keys (one page per wave's run from 16
     keys on): the page layout does not enter the arithmetic, so the outputs
     are bit-identical; the first is also held to the oracle bound."""
     base = W.backward_small(seed=97 + d, d=d, hq=4, hkv=2)
     f8 = W.fp8_inputs(base)
     name = "ranges"
     outs = {}
-    for ps in (1024 // d, 16, 32, 64):
+    for ps in sorted({1024 // d, 16, 32, 64}):
         w = base if ps == base.page_size else repage(base, ps, 700 + ps)
         g8 = W.fp8_inputs(w)
         assert g8["k_s"] == f8["k_s"] and g8["v_s"] == f8["v_s"]   # same values, other layout
@@ -143,3 +143,19 @@ def test_fp8_page_sizes_bit_identical(d):
     for ps in outs:
         assert torch.equal(outs[ps][0], outs[first][0]) and torch.equal(outs[ps][1], outs[first][1]), ps
     _check(base, fp8_dequantized(base, f8), name, outs[16][0], outs[16][1])
+
+
+def test_fp8_gemma2_global_sampled():
+    """The Gemma2-like global layer (16384 tokens, causal, 8 query heads over
+    4 K/V heads, d 256, random page order) in fp8, oracle on sampled heads
+    and rows."""
+    w = W.config3b(1)
+    f8 = W.fp8_inputs(w)
+    wd = fp8_dequantized(w, f8)
+    dev = _dev8(w, f8)
+    _say("fp8 d 256 global layer")
+    out, lse = _run(w, f8, dev, "causal")
+    n = int(w.kv_lens[0])
+    rows = {0: np.array([0, 1, 63, 64, 127, 128, 4095, 4096, 9000, n - 2, n - 1])}
+    worst = _check(w, wd, "causal", out, lse, heads=[0, 5], rows=rows)
+    _say("worst err / bound", worst)
