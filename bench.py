@@ -713,6 +713,29 @@ def backward_lines(steps, warmup):
                           "flops_per_step": 10.0 * d * hq * n_unmasked,
                           "kernels": "bwd_prep, bwd_dq<128,128>, bwd_dkdv<128>"}), flush=True)
         del plan
+    # the Gemma2-like global layer (d 256, causal, 8 / 4 heads)
+    w3 = W.config3b(1)
+    dev3 = device_inputs(w3)
+    do3 = torch.from_numpy(W.upstream_grad(w3, 4003)).cuda().to(torch.bfloat16).contiguous()
+    kind, kw = plan_kwargs(w3, "causal")
+    plan = ma.mask_compile(kind, w3.cu_seqlens_q, w3.kv_lens, **kw)
+    out3, lse3 = ma.attn_prefill_masked(plan, dev3["q"], dev3["k"], dev3["v"], dev3["pt"], w3.scale)
+    dq3 = torch.empty(dev3["q"].shape, dtype=torch.float32, device="cuda")
+    dk3 = torch.zeros(dev3["k"].shape, dtype=torch.float32, device="cuda")
+    dv3 = torch.zeros_like(dk3)
+    ws3 = torch.empty(ma.attn_backward_workspace(plan, w3.hq), dtype=torch.uint8, device="cuda")
+
+    def step3():
+        ma.attn_backward_masked(plan, dev3["q"], dev3["k"], dev3["v"], dev3["pt"], out3, lse3, do3, w3.scale, dq=dq3,
+                                dk_cache=dk3, dv_cache=dv3, workspace=ws3)
+    ms = time_steps(step3, steps, warmup, stream)
+    n3 = 16384 * 16385 // 2
+    tf = 10.0 * w3.d * w3.hq * n3 / (ms * 1e-3) / 1e12
+    print(json.dumps({"workload": "backward_gemma2_global_16k_d256", "mask": "causal", "ms": round(ms, 4),
+                      "tflops": round(tf, 2), "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                      "flops_per_step": 10.0 * w3.d * w3.hq * n3,
+                      "kernels": "bwd_prep, bwd_dq<256,128>, bwd_dkdv<256>"}), flush=True)
+    del plan
 
 
 def fp8_lines(steps, warmup):

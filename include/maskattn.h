@@ -244,7 +244,7 @@ ma_status attn_prefill_masked(const ma_plan *plan, const void *q, int64_t total_
  * attn_prefill_masked (strides in elements = bytes).  Per-tensor descale
  * factors: the attention is softmax(scale * q_descale * k_descale * Q8 K8^T
  * + mask) (v_descale * V8), Q8 / K8 / V8 the decoded bytes.
- *  out_dtype BF16 or F32; d in {64, 128}; plans with tile 128 x 64; page
+ *  out_dtype BF16 or F32; d in {64, 128, 256}; plans with tile 128 x 64; page
  *  size at least 1024 / d keys (one gather instruction's rows in one page);
  *  a page's bytes (page stride) below 2^32 and page_size * slot stride below
  *  2^31.
@@ -282,7 +282,7 @@ size_t attn_backward_workspace(const ma_plan *plan, int32_t hq);
  *           when no query sees the key); other slots are not touched.  No two
  *           sequences may map keys to the same slot.
  *  workspace device, >= attn_backward_workspace(plan, hq) bytes, scratch.
- * Supported: d in {64, 128}; plans with tile_k 64 and tile_q 64 or 128.
+ * Supported: d in {64, 128, 256}; plans with tile_k 64 and tile_q 64 or 128.
  * The first call on a plan builds its key-major transpose (one device
  * allocation, held until mask_plan_destroy; synchronises `stream` once);
  * later calls only launch.  Arithmetic: bf16 matrix products (P and dS

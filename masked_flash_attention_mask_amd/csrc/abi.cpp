@@ -352,7 +352,8 @@ ma_status attn_backward_masked(ma_plan *plan, const void *q, int64_t total_q, in
     if ((int64_t)max_pages * page_size < plan->kv_len[b])
       return set_error(MA_ERR_INVALID, "page table (max_pages %d x page_size %d) shorter than kv_len %d",
                        max_pages, page_size, plan->kv_len[b]);
-  if (d != 64 && d != 128) return set_error(MA_ERR_UNSUPPORTED, "backward head_dim %d (supported: 64, 128)", d);
+  if (d != 64 && d != 128 && d != 256)
+    return set_error(MA_ERR_UNSUPPORTED, "backward head_dim %d (supported: 64, 128, 256)", d);
   if (out_dtype != MA_BF16 && out_dtype != MA_F32)
     return set_error(MA_ERR_UNSUPPORTED, "out dtype %d", out_dtype);
   if (kv_strides[2] < d) return set_error(MA_ERR_INVALID, "head stride %lld < head_dim", (long long)kv_strides[2]);

@@ -186,8 +186,16 @@ struct SwzQ {
   __device__ static constexpr int f(int r) { return QBlk<D>::f(r); }
 };
 
+// Waves per SIMD of the dQ kernel: two for 128-row tiles at d <= 128; one
+// for 64-row tiles and at d = 256 (Q, dO and the dQ accumulators of a 32-row
+// block take 256 registers per lane there).
+template <int D, int BQ>
+constexpr int dq_occupancy() {
+  return BQ == 128 && D <= 128 ? 2 : 1;
+}
+
 template <int D, int BQ, bool FAST>
-__global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(BQ * 2, (dq_occupancy<D, BQ>())) void bwd_dq(BwdParams p) {
   using QB = QBlk<D>;
   constexpr int NW = BQ / 32, CH = D / 8, NI = CH / NW;   // gather instructions per wave per matrix
   constexpr int TILE = 64 * D;                             // elements of one 64-key matrix
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(BQ * 2, BQ == 128 ? 2 : 1) void bwd_dq(BwdParams p)
 // ---------------------------------------------------------------------------
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv(BwdParams p) {
+__global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void bwd_dkdv(BwdParams p) {
   using QB = QBlk<D>;
   constexpr int CH = D / 8, NI = CH / 4;   // gather instructions per wave per matrix
   extern __shared__ __align__(16) uint16_t lds[];
@@ -973,8 +981,13 @@ ma_status run(const BackwardArgs &a, const BwdParams &prm) {
     st = fast ? launch(bwd_dq<D, 64, true>, prm.num_items * a.hq, 128, dq_lds, prm, a.stream, "backward dQ")
               : launch(bwd_dq<D, 64, false>, prm.num_items * a.hq, 128, dq_lds, prm, a.stream, "backward dQ");
   if (st != MA_OK) return st;
-  if (prm.tile_q == 128)
-    return launch(bwd_dkdv_wide<D>, prm.num_kitems * a.hkv, 256, QBlkW<D>::LDS, prm, a.stream, "backward dK dV");
+  // d 256: the 32-keys-per-wave form (the wide form's dK / dV sums of 64
+  // keys would need 512 registers per lane); it walks 128-row q-tiles as two
+  // 64-row blocks
+  if constexpr (D <= 128) {
+    if (prm.tile_q == 128)
+      return launch(bwd_dkdv_wide<D>, prm.num_kitems * a.hkv, 256, QBlkW<D>::LDS, prm, a.stream, "backward dK dV");
+  }
   return launch(bwd_dkdv<D>, prm.num_kitems * a.hkv, 256, QBlk<D>::BYTES, prm, a.stream, "backward dK dV");
 }
 
@@ -1027,6 +1040,7 @@ ma_status launch_backward(const BackwardArgs &a) {
   switch (a.d) {
     case 64: return run<64>(a, prm);
     case 128: return run<128>(a, prm);
+    case 256: return run<256>(a, prm);
   }
   return set_error(MA_ERR_UNSUPPORTED, "backward head_dim %d", a.d);
 }

@@ -190,7 +190,7 @@ def test_backward_validation_before_hip():
     assert _backward(plan, dout=None) == L.MA_ERR_INVALID
     assert _backward(plan, lse=None) == L.MA_ERR_INVALID
     assert _backward(plan, total_q=9) == L.MA_ERR_PLAN_MISMATCH
-    assert _backward(plan, d=256) == L.MA_ERR_UNSUPPORTED
+    assert _backward(plan, d=96) == L.MA_ERR_UNSUPPORTED
     assert _backward(plan, out_dt=7) == L.MA_ERR_UNSUPPORTED
     assert _backward(plan, ws_bytes=need - 1) == L.MA_ERR_SIZE
     assert _backward(plan, ws=None) == L.MA_ERR_SIZE

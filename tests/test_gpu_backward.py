@@ -47,7 +47,7 @@ def _ref(w, do, name):
                                  oracle_masks(w, name), w.scale, do)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_backward_mask_kinds(d):
     """Oracle forward outputs in, every gradient against the oracle's."""
     w, do, dev = _setup(d)
@@ -61,7 +61,7 @@ def test_backward_mask_kinds(d):
             assert err <= TOL_GRAD, (name, what, err)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_backward_tile_q64_and_mha(d):
     """64-row q-tiles, and one K/V head per query head."""
     w, do, dev = _setup(d, hq=2, hkv=2, seed=17)
@@ -181,7 +181,7 @@ def test_backward_full_size_sampled():
             assert err <= TOL_GRAD, (h, what, err)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_backward_page_sizes_bit_identical(d):
     """Pages of 1 and 4 keys take the per-lane gather of the dQ pass, 16 the
     per-instruction scalar base, 64 one base per wave; the page layout does not
@@ -210,3 +210,44 @@ def test_backward_page_sizes_bit_identical(d):
         for b in range(len(base.kv_lens)):
             assert np.array_equal(res[ps][1][b][0], res[16][1][b][0]), ("dk", ps, b)
             assert np.array_equal(res[ps][1][b][1], res[16][1][b][1]), ("dv", ps, b)
+
+
+def test_backward_gemma2_global_sampled():
+    """The backward of the Gemma2-like global layer (16384 tokens, causal,
+    8 query heads over 4 K/V heads, d 256, random page order) at full size;
+    the library's forward (fp32 output) feeds it; the oracle takes exact
+    gradients for two heads at sampled query rows and keys."""
+    from oracle import masks as OM
+    from oracle import attention as OA
+    w = W.config3b(1)
+    dev = device_inputs(w)
+    do = W.upstream_grad(w, 4003)
+    dev["do"] = torch.from_numpy(do).cuda().to(torch.bfloat16).contiguous()
+    _say("backward d 256 global layer")
+    out, lse, plan = run_prefill(w, dev, "causal", out_dtype=torch.float32)
+    dq, dk, dv = ma.attn_backward_masked(plan, dev["q"], dev["k"], dev["v"], dev["pt"], out, lse, dev["do"], w.scale)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+    n = int(w.kv_lens[0])
+    rng = np.random.default_rng(46)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 4095, 4096, 8191, n - 2, n - 1], rng.integers(0, n, 15)]))
+    keys = np.unique(np.concatenate([[0, 63, 64, 4095, 4096, 8192, n - 64, n - 1], rng.integers(0, n, 16)]))
+    mask = OM.causal(n, n)
+    page = w.page_size
+    slots = (w.page_table[0, keys // page], keys % page)
+    # K/V head 0 serves query heads 0 and 1: their dQ rows, and dK / dV summed
+    k = OA.gather_paged(w.k_cache, w.page_table[0], n, 0)
+    v = OA.gather_paged(w.v_cache, w.page_table[0], n, 0)
+    rk = rv = 0
+    for h in (0, 1):
+        _say("oracle head", h)
+        rq, rk_h, rv_h = OB.attend_backward_sampled(w.q[:, h], k, v, mask, w.scale, do[:, h], rows, keys)
+        rk = rk + rk_h
+        rv = rv + rv_h
+        errq = float(np.abs(dq[rows, h] - rq).max() / np.sqrt((rq ** 2).mean()))
+        _say("dq max err / rms", errq)
+        assert errq <= 2.0 ** -3, (h, errq)
+    for gr, r, what in ((dk[slots[0], slots[1], 0], rk, "dk"), (dv[slots[0], slots[1], 0], rv, "dv")):
+        err = grad_err(torch.from_numpy(gr), r)
+        _say(what, "row metric", err)
+        assert err <= TOL_GRAD, (what, err)
