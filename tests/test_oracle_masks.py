@@ -85,6 +85,32 @@ def test_range_types_small():
     assert np.array_equal(wide, np.array([[1, 1, 1, 1, 0], [1, 1, 1, 1, 1]], bool))
 
 
+@pytest.mark.parametrize("lq,lk", [(1, 1), (4, 4), (7, 7), (5, 9), (9, 5), (3, 16), (16, 3)])
+def test_inv_and_bi_causal_relations(lq, lk):
+    """Relations the reading of INV_CAUSAL / BI_CAUSAL (MagiAttention issue
+    316 names them: a band aligned the other way, and the intersection of
+    both) must satisfy, on squares and rectangles: BI = CAUSAL AND INV; on a
+    square INV is CAUSAL transposed; INV is top-left aligned (row i starts at
+    key i, sees every key after it), CAUSAL bottom-right aligned; on squares
+    and wide rectangles CAUSAL OR INV covers every entry.  (Parity stays unpinned beyond these relations: the page
+    gives no matrix for either type.)"""
+    C = M.range_block(lq, lk, M.CAUSAL)
+    I = M.range_block(lq, lk, M.INV_CAUSAL)
+    B = M.range_block(lq, lk, M.BI_CAUSAL)
+    assert np.array_equal(B, C & I)
+    if lq == lk:
+        assert np.array_equal(I, C.T)
+        assert np.array_equal(B, np.eye(lq, dtype=bool))
+    i = np.arange(lq)[:, None]
+    jj = np.arange(lk)[None, :]
+    assert np.array_equal(I, jj >= i)                       # top-left aligned
+    assert np.array_equal(C, jj <= i + (lk - lq))           # bottom-right aligned
+    # on squares and wide rectangles the two half-lines of a row overlap, so
+    # CAUSAL | INV covers every entry
+    if lk >= lq:
+        assert (C | I).all()
+
+
 def test_ranges_union_and_bounds():
     m = M.ranges(4, 6, [(0, 2, 0, 2, M.FULL, 0), (1, 4, 3, 6, M.FULL, 0)])
     exp = np.zeros((4, 6), bool)
