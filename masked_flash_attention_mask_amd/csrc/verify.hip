@@ -196,6 +196,8 @@ __device__ __forceinline__ uint64_t row_word(const VerifyParams &p, int64_t moff
 // Bits (LSB = lowest address) of the nonzero bytes of a dword: per byte the
 // high bit is set iff the byte is nonzero (SWAR), then one multiply moves the
 // four high bits to bits 21..24 (distinct partial products, no carries).
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 __device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t x) {
   const uint32_t t = ((((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) >> 7) & 0x01010101u;
   return ((t * 0x00204081u) >> 21) & 0xFu;
@@ -763,22 +765,6 @@ constexpr int kPipeRows = 256;   // row slots of a unit
 constexpr int kPipeWaves = 8;
 constexpr int kPipeStages = 4;
 
-// Tiles of every unit of sequence b (its head blocks share them); a
-// sequence with queries but no keys keeps one tile so that its rows are
-// written (O = 0, LSE = -inf).
-__device__ __forceinline__ int seq_tiles(const VerifyParams &p, int b) {
-  const int q0 = p.cu_seqlens_q[b];
-  if (seq_q_len(p, b, q0) <= 0) return 0;
-  const int kv = min(p.kv_lens[b], p.max_kv);
-  return kv > 0 ? (kv + 63) / 64 : 1;
-}
-
-// Packed mask words of sequence b (true lengths: the caller's layout).
-__device__ __forceinline__ int64_t seq_words(const VerifyParams &p, int b) {
-  const int64_t ql = p.cu_seqlens_q[b + 1] - p.cu_seqlens_q[b], kv = p.kv_lens[b];
-  return ql * ((kv + 63) / 64);
-}
-
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T v, int lane) {
 #pragma unroll
@@ -813,15 +799,32 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 struct Piece {
   int b, hb, kt0, kt1, n, k, npieces;
   int64_t moff;
+  int q0, q_len, kv_len;   // the sequence's first query row, rows (seq_q_len), keys
 };
 
 // Every lane returns the same (scalar) values.  Batches of up to 64
-// sequences keep each sequence's tile count in its lane for the whole search;
-// larger ones reread them per chunk.
+// sequences keep each sequence's lengths in its lane for the whole search,
+// loaded at once (one round trip); larger ones reread them per chunk.
 __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
   const bool one_chunk = p.batch <= 64;
-  const int n_lane = lane < p.batch ? seq_tiles(p, lane) : 0;
-  auto tiles_at = [&](int b) { return one_chunk ? (b < p.batch ? n_lane : 0) : (b < p.batch ? seq_tiles(p, b) : 0); };
+  // lane's sequence from its three lengths, all loaded before any is used:
+  // its tiles (every unit of the sequence has them; a sequence with queries
+  // but no keys keeps one tile so that its rows are written, O = 0 and
+  // LSE = -inf) and its packed mask words (true lengths: the caller's layout)
+  struct Lens {
+    int n, q0, ql, kv;
+    int64_t words;
+  };
+  auto lens = [&](int b) -> Lens {
+    if (b >= p.batch) return Lens{0, 0, 0, 0, 0};
+    const int q0 = p.cu_seqlens_q[b], q1 = p.cu_seqlens_q[b + 1], kv_true = p.kv_lens[b];
+    const int ql = max(0, min(q1 - q0, p.qs));
+    const int kv = min(kv_true, p.max_kv);
+    return Lens{ql <= 0 ? 0 : (kv > 0 ? (kv + 63) / 64 : 1), q0, ql, kv_true,
+                (int64_t)(q1 - q0) * ((kv_true + 63) / 64)};
+  };
+  const Lens mine = one_chunk ? lens(lane) : Lens{0, 0, 0, 0, 0};
+  auto tiles_at = [&](int b) { return one_chunk ? (b < p.batch ? mine.n : 0) : lens(b).n; };
   // Smallest T in [1, max n_b] with sum_b nhb * ceil(n_b / T) <= G (T = max
   // n_b always fits: the host sizes G to at least the number of units).
   int maxn = 0;
@@ -833,7 +836,7 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
     int need = 0;
     for (int c0 = 0; c0 < p.batch; c0 += 64) {
       const int n = tiles_at(c0 + lane);
-      need += wave_sum(p.nhb * ((n + mid - 1) / mid));
+      need += wave_sum(p.nhb * (int)(((unsigned)n + (unsigned)mid - 1u) / (unsigned)mid));
     }
     if (need <= p.grid) hi_t = mid;
     else lo_t = mid + 1;
@@ -842,12 +845,13 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
   // the sequence whose units hold workgroup wg: prefix sums of nhb * k_b
   int base = 0;
   int64_t mbase = 0;
-  Piece r{-1, 0, 0, 0, 0, 0, 0, 0};
+  Piece r{-1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   for (int c0 = 0; c0 < p.batch; c0 += 64) {
     const int b = c0 + lane;
-    const int n = tiles_at(b);
+    const Lens ln = one_chunk ? (b < p.batch ? mine : Lens{0, 0, 0, 0, 0}) : lens(b);
+    const int n = ln.n;
+    const int64_t me = ln.words;
     const int wgs = p.nhb * ((n + T - 1) / T);
-    const int64_t me = b < p.batch ? seq_words(p, b) : 0;
     const int incl = wave_incl_scan(wgs, lane);
     const int64_t mincl = wave_incl_scan(me, lane);
     if (r.b < 0) {
@@ -862,6 +866,9 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
         r.hb = off / r.npieces;
         r.k = off - r.hb * r.npieces;
         r.moff = mbase + __shfl(mincl - me, l, 64);
+        r.q0 = __shfl(ln.q0, l, 64);
+        r.q_len = __shfl(ln.ql, l, 64);
+        r.kv_len = __shfl(ln.kv, l, 64);
       }
     }
     base += __shfl(incl, 63, 64);
@@ -873,8 +880,27 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
   r.hb = __builtin_amdgcn_readfirstlane(r.hb);
   r.k = __builtin_amdgcn_readfirstlane(r.k);
   r.moff = uniform64(r.moff);
+  r.q0 = __builtin_amdgcn_readfirstlane(r.q0);
+  r.q_len = __builtin_amdgcn_readfirstlane(r.q_len);
+  r.kv_len = __builtin_amdgcn_readfirstlane(r.kv_len);
   r.kt0 = r.k * r.n / r.npieces;
   r.kt1 = (r.k + 1) * r.n / r.npieces;
+  return r;
+}
+
+__device__ __forceinline__ Piece uniform_piece(const Piece &x) {
+  Piece r;
+  r.b = __builtin_amdgcn_readfirstlane(x.b);
+  r.hb = __builtin_amdgcn_readfirstlane(x.hb);
+  r.kt0 = __builtin_amdgcn_readfirstlane(x.kt0);
+  r.kt1 = __builtin_amdgcn_readfirstlane(x.kt1);
+  r.n = __builtin_amdgcn_readfirstlane(x.n);
+  r.k = __builtin_amdgcn_readfirstlane(x.k);
+  r.npieces = __builtin_amdgcn_readfirstlane(x.npieces);
+  r.moff = uniform64(x.moff);
+  r.q0 = __builtin_amdgcn_readfirstlane(x.q0);
+  r.q_len = __builtin_amdgcn_readfirstlane(x.q_len);
+  r.kv_len = __builtin_amdgcn_readfirstlane(x.kv_len);
   return r;
 }
 
@@ -907,7 +933,8 @@ struct PipeStage {
 };
 
 template <int D, typename OutT>
-__global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyParams p, CutUnit *cuts) {
+__global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyParams p, CutUnit *cuts,
+                                                                          int32_t *unit_slot) {
   extern __shared__ __align__(16) uint16_t lds[];
   constexpr int NW = kPipeWaves;
   using KV = dma::KvDma<D, NW>;
@@ -918,7 +945,15 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
   const int l32 = lane & 31, hi = lane >> 5;
   const int wg = pipe_logical(blockIdx.x, p.grid);
 
-  const Piece pc = locate_piece(p, wg, lane);
+  // One wave finds the piece (the other waves would only share its SIMDs
+  // doing the same search) and hands it on through LDS.
+  __shared__ Piece piece_lds;
+  if (wave == 0) {
+    const Piece w0 = locate_piece(p, wg, lane);
+    if (lane == 0) piece_lds = w0;
+  }
+  __syncthreads();
+  const Piece pc = uniform_piece(piece_lds);
   if (pc.b < 0) {
     if (tid == 0) cuts[wg] = CutUnit{-1, 0, 0, 0, 0, 0, 0, 0};
     return;
@@ -937,11 +972,13 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
   const int rd = 64 * (wave & 3) + lane;    // the row whose word half this lane's DMA moves
   const uint64_t *mask64 = (const uint64_t *)p.mask;
 
-  const int q0 = p.cu_seqlens_q[b], q_len = seq_q_len(p, b, q0);
-  if (tid == 0)
+  const int q0 = pc.q0, q_len = pc.q_len;
+  if (tid == 0) {
     cuts[wg] = pc.k == 0 && pc.npieces > 1 ? CutUnit{b, hb, pc.npieces, q0, q_len, 0, 0, 0}
                                            : CutUnit{-1, 0, 0, 0, 0, 0, 0, 0};
-  const int kv_true = p.kv_lens[b];
+    if (pc.k == 0) unit_slot[b * p.nhb + hb] = wg;
+  }
+  const int kv_true = pc.kv_len;
   const int kv = min(kv_true, p.max_kv);
   const int nwords = (kv_true + 63) / 64;
   const int hh = min(r / p.qs, p.gh - 1), t = r % p.qs;
@@ -966,11 +1003,13 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
     const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)g * p.s_head;
     const int32_t *pt = p.page_table + (int64_t)b * p.max_pages;
     const int nt = kt1 - kt0;
+    // Page ids of tile kt0 + j (scalar loads, read a step before their
+    // gathers: next to the gathers' inline asm each would be waited for)
+    auto pages = [&](int j) { return KV::pages_uniform(pt, p.page_shift, kt0 + j, kv, wave); };
     // Tile kt0 + j into stage j % 4: K, V and one half of 64 rows' words.
-    auto issue = [&](int j) {
+    auto issue = [&](int j, const typename KV::Pages &pg) {
       const int kt = kt0 + j;
       const uint32_t st = lds0 + (uint32_t)(j & 3) * PS::BYTES;
-      const typename KV::Pages pg = KV::pages_uniform(pt, p.page_shift, kt, kv, wave);
       if (kt * 64 + 64 <= kv) {
         if (p.page_shift >= kPageRunShift) {
           dma::issue_mat_page<D, NW, dma::SwzK<D>>(kbase, pg.id[0], lgk, p.page_shift, page_bytes, slot_bytes, kt,
@@ -1003,10 +1042,14 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
       return ok ? ((uint64_t)hi_w << 32) | lo_w : 0ull;
     };
     f32x16 sa[2], sb[2];
-    issue(0);
-    if (nt > 1) issue(1);
+    typename KV::Pages pg0 = pages(0), pg1, pg2, pgn;
+    if (nt > 1) pg1 = pages(1);
+    if (nt > 2) pg2 = pages(2);
+    if (nt > 3) pgn = pages(3);
+    issue(0, pg0);
+    if (nt > 1) issue(1, pg1);
     if (nt > 2) {
-      issue(2);
+      issue(2, pg2);
       wait_vmem_n<N_TILE>();   // tiles 0 and 1 have landed
     } else {
       dma::wait_vmem();
@@ -1017,7 +1060,10 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
     auto step = [&](f32x16 (&scur)[2], f32x16 (&snxt)[2], int j) {
       const int kt = kt0 + j;
       const uint64_t wcur = word_cur;
-      if (j + 3 < nt) issue(j + 3);
+      if (j + 3 < nt) {
+        issue(j + 3, pgn);
+        if (j + 4 < nt) pgn = pages(j + 4);
+      }
       const int kin = kv - kt * 64;
       const uint64_t inb = low_bits(kin);
       const uint64_t wm = wcur & inb;
@@ -1058,25 +1104,43 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
     store_row<D, OutT>((OutT *)p.out + (tok * p.hq + h) * D, oacc, inv, hi);
     if (p.lse && hi == 0) p.lse[tok * p.hq + h] = lse;
   } else {
+    // partial O in the output's type: a bf16 output is rounded to bf16 at
+    // the end anyway, so its partials need not carry more (and move half the
+    // bytes); an fp32 output keeps fp32 partials
     const int64_t row = (int64_t)wg * kPipeRows + r;
-    store_row<D, float>(p.ws_o + row * D, oacc, inv, hi);
+    store_row<D, OutT>((OutT *)p.ws_o + row * D, oacc, inv, hi);
     if (hi == 0) p.ws_lse[row] = lse;
   }
 }
 
-// Merges the pieces of a cut unit: block (i, c) with workgroup i the unit's
-// first piece takes 256 (row, 4 columns) items of the unit's 256 x D outputs
-// (item = c * 256 + thread, D / 4 items per row) and merges the pieces i,
-// i + 1, ... in order:
+// Merges the pieces of a cut unit: block (u, c) takes unit u's first piece
+// i from unit_slot[u] and 256 (row, 4 columns) items of the unit's 256 x D
+// outputs (item = c * 256 + thread, D / 4 items per row) and merges the
+// pieces i, i + 1, ... in order:
 // O = sum_s exp(LSE_s - M) O_s / sum_s exp(LSE_s - M), LSE = M + ln(sum).
+// unit_slot keeps entries of earlier launches for units that have no piece
+// in this one; the cut record of slot i, which every workgroup rewrites on
+// every launch, tells a current entry from a stale one (and is b < 0 when
+// the unit's single piece wrote its output itself).
 // Each pass issues the loads of kMergeBatch pieces before using them.
 constexpr int kMergeBatch = 8;
 
+// Four consecutive partial values as fp32 (bf16 widened exactly).
+__device__ __forceinline__ f32x4 load4f(const float *src) { return *(const f32x4 *)src; }
+__device__ __forceinline__ f32x4 load4f(const uint16_t *src) {
+  const u32x2 v = *(const u32x2 *)src;
+  return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u), __uint_as_float(v[1] << 16),
+               __uint_as_float(v[1] & 0xFFFF0000u)};
+}
+
 template <int D, typename OutT>
-__global__ __launch_bounds__(256) void verify_pipe_combine(VerifyParams p, const CutUnit *cuts) {
-  const int wg = pipe_logical(blockIdx.x, p.grid);
+__global__ __launch_bounds__(256) void verify_pipe_combine(VerifyParams p, const CutUnit *cuts,
+                                                           const int32_t *unit_slot) {
+  const int u = blockIdx.x;
+  const int wg = unit_slot[u];
+  if (wg < 0 || wg >= p.grid) return;
   const CutUnit cu = cuts[wg];
-  if (cu.b < 0) return;
+  if (cu.b != u / p.nhb || cu.hb != u % p.nhb) return;
   const int hb = cu.hb, np = cu.npieces, q0 = cu.q0, q_len = cu.q_len;
   const int item = blockIdx.y * 256 + threadIdx.x;
   const int r = item / (D / 4), c4 = item % (D / 4);
@@ -1093,7 +1157,7 @@ __global__ __launch_bounds__(256) void verify_pipe_combine(VerifyParams p, const
       const bool has = k0 + k < np;
       const int64_t row = (int64_t)(wg + k0 + k) * kPipeRows + r;
       lse_k[k] = has ? p.ws_lse[row] : neg_inf();
-      o_k[k] = has ? *(const f32x4 *)(p.ws_o + row * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      o_k[k] = has ? load4f((const OutT *)p.ws_o + row * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float mx = m_run;
 #pragma unroll
@@ -1125,30 +1189,53 @@ __global__ __launch_bounds__(256) void verify_pipe_combine(VerifyParams p, const
 // Only rows below max_q are written (the kernel reads no others), and no
 // word at or past `cap`.
 __global__ __launch_bounds__(256) void dense_to_words(VerifyParams p, uint64_t *words, int64_t cap) {
-  const int b = blockIdx.y;
+  const int b = blockIdx.y, lane = threadIdx.x & 63;
+  // this sequence's lengths and the earlier sequences', 64 per pass, one per
+  // lane: independent loads, then a wave sum (a serial walk would wait for
+  // each in turn)
+  const int qb0 = p.cu_seqlens_q[b], qb1 = p.cu_seqlens_q[b + 1], kv = p.kv_lens[b];
   int64_t doff = 0, woff = 0;
-  for (int i = 0; i < b; ++i) {
-    const int64_t ql = p.cu_seqlens_q[i + 1] - p.cu_seqlens_q[i], kv = p.kv_lens[i];
-    doff += ql * kv;
-    woff += ql * ((kv + 63) / 64);
+  for (int c0 = 0; c0 < b; c0 += 64) {
+    const int i = c0 + lane;
+    int64_t dn = 0, wn = 0;
+    if (i < b) {
+      const int64_t ql = p.cu_seqlens_q[i + 1] - p.cu_seqlens_q[i], kv = p.kv_lens[i];
+      dn = ql * kv;
+      wn = ql * ((kv + 63) / 64);
+    }
+    doff += __shfl(wave_incl_scan(dn, lane), 63, 64);
+    woff += __shfl(wave_incl_scan(wn, lane), 63, 64);
   }
-  const int q_len = seq_q_len(p, b, p.cu_seqlens_q[b]), kv = p.kv_lens[b];
+  const int q_len = max(0, min(qb1 - qb0, p.qs));   // seq_q_len
   const int nw = (kv + 63) / 64;
   const uint8_t *m8 = (const uint8_t *)p.mask;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < (int64_t)q_len * nw;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int t = (int)(idx / nw), w = (int)(idx % nw);
+  // 32-bit item indices (words at or past cap, the only ones such a bound
+  // could drop, are never written)
+  const int items = (int)min((int64_t)q_len * nw, (int64_t)INT32_MAX);
+  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < items; idx += gridDim.x * blockDim.x) {
+    const int t = idx / nw, w = idx - t * nw;
     const int64_t base = doff + (int64_t)t * kv + 64 * w;
     const int nb = min(64, kv - 64 * w);
     uint64_t bits = 0;
-    if (nb == 64 && base + 64 <= p.mask_numel) {
+    // Rows start at any byte (their stride is kv_len bytes): the 64 bytes
+    // are read as 17 dword-aligned dwords and shifted into place with
+    // v_alignbyte (16-byte loads at unaligned addresses are slow).  The
+    // 17th dword must lie inside the mask.
+    const int64_t a4 = base & ~(int64_t)3;
+    if (nb == 64 && a4 + 68 <= p.mask_numel) {
+      const uint32_t sh = (uint32_t)(base & 3);
+      const u32x4a4 *w4 = (const u32x4a4 *)(m8 + a4);
+      uint32_t dw[17];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        u32x4 v;
-        __builtin_memcpy(&v, m8 + base + 16 * q, 16);
+        const u32x4a4 v = w4[q];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bits |= (uint64_t)nonzero_bytes4(v[e]) << (16 * q + 4 * e);
+        for (int e = 0; e < 4; ++e) dw[4 * q + e] = v[e];
       }
+      dw[16] = ((const uint32_t *)(m8 + a4))[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        bits |= (uint64_t)nonzero_bytes4(__builtin_amdgcn_alignbyte(dw[i + 1], dw[i], sh)) << (4 * i);
     } else {
       for (int j = 0; j < nb; ++j)
         if (base + j < p.mask_numel && m8[base + j] != 0) bits |= 1ull << j;
@@ -1287,18 +1374,19 @@ PipeShape pipe_shape(int batch, int hq, int hkv, int d, int max_q, int max_kv, i
 // Workspace of a balanced launch: one partial (O, LSE) slot of 256 rows per
 // workgroup, and room for a dense mask converted to packed words.
 struct PipeWs {
-  size_t o, lse, cuts, words, total;
+  size_t o, lse, cuts, units, words, total;
 };
 
 PipeWs pipe_ws(const PipeShape &s, int32_t batch, int32_t max_q, int32_t max_kv, int32_t d) {
-  PipeWs w{0, 0, 0, 0, 0};
+  PipeWs w{0, 0, 0, 0, 0, 0};
   if (!s.ok) return w;
   const size_t slots = (size_t)s.grid;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   w.o = 0;
   w.lse = up(slots * kPipeRows * d * sizeof(float));
   w.cuts = w.lse + up(slots * kPipeRows * sizeof(float));
-  w.words = w.cuts + up(slots * sizeof(CutUnit));
+  w.units = w.cuts + up(slots * sizeof(CutUnit));
+  w.words = w.units + up((size_t)batch * s.nhb * sizeof(int32_t));
   w.total = w.words + (size_t)batch * max_q * ((max_kv + 63) / 64) * sizeof(uint64_t);
   return w;
 }
@@ -1311,6 +1399,7 @@ ma_status run_pipe(const VerifyArgs &a, VerifyParams prm, const PipeShape &ps) {
   prm.ws_o = (float *)(ws + w.o);
   prm.ws_lse = (float *)(ws + w.lse);
   CutUnit *cuts = (CutUnit *)(ws + w.cuts);
+  int32_t *unit_slot = (int32_t *)(ws + w.units);
   hipError_t e = hipSuccess;
   if (prm.mode == kDense) {
     // the dense rows become packed words first; the main kernel reads words
@@ -1331,11 +1420,11 @@ ma_status run_pipe(const VerifyArgs &a, VerifyParams prm, const PipeShape &ps) {
     e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
   }
-  hipLaunchKernelGGL(kern, dim3(ps.grid), dim3(kPipeWaves * 64), lds, s, prm, cuts);
+  hipLaunchKernelGGL(kern, dim3(ps.grid), dim3(kPipeWaves * 64), lds, s, prm, cuts, unit_slot);
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify launch: %s", hipGetErrorString(e));
-  hipLaunchKernelGGL((verify_pipe_combine<D, OutT>), dim3(ps.grid, kPipeRows * (D / 4) / 256), dim3(256), 0, s, prm,
-                     (const CutUnit *)cuts);
+  hipLaunchKernelGGL((verify_pipe_combine<D, OutT>), dim3(a.batch * ps.nhb, kPipeRows * (D / 4) / 256), dim3(256), 0,
+                     s, prm, (const CutUnit *)cuts, (const int32_t *)unit_slot);
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify combine launch: %s", hipGetErrorString(e));
   return MA_OK;

@@ -11,7 +11,7 @@ import torch
 
 import masked_flash_attention_mask_amd as ma
 import workloads as W
-from helpers import TOL_BF16, device_inputs, lse_err, max_abs_err, oracle, repage
+from helpers import TOL_BF16, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle, repage
 
 pytestmark = pytest.mark.gpu
 
@@ -75,5 +75,8 @@ def test_balanced_verify_matches_oracle(case):
     ref_o, ref_l = oracle(w, "packed")
     assert max_abs_err(o_p, ref_o) <= TOL_BF16
     assert lse_err(l_p, ref_l) <= 1e-2
+    # a bf16 output merges bf16 partials: against the oracle after the output
+    # rounding, and within two bf16 roundings of the fp32 output
     ob, _ = _run(w, dev, "packed", max_q, out_dtype=torch.bfloat16)
+    assert bf16_out_err(ob, ref_o) <= TOL_BF16
     assert (ob.float() - o_p).abs().max().item() <= 2 ** -7 * max(1.0, o_p.abs().max().item())
