@@ -566,6 +566,7 @@ def verify_case(form, steps, warmup, w2=None, dev=None):
         n = sum(64 * int(c) for c in w2.info["ctx"]) + sum(
             int(np.sum([len(_anc(p, i)) for i in range(64)])) for p in w2.info["parents"])
     ms = time_steps(step, steps, warmup, stream)
+    cold = cold_steps(step, min(steps, 20), stream)
     flops = 4.0 * w2.d * w2.hq * n
     tf = flops / (ms * 1e-3) / 1e12
     kv_bytes = 2 * int(w2.kv_lens.sum()) * w2.hkv * w2.d * 2
@@ -573,7 +574,30 @@ def verify_case(form, steps, warmup, w2=None, dev=None):
     bound_us = max(flops / (PEAK_BF16_TFLOPS * 1e12), (kv_bytes + qo_bytes) / (PEAK_HBM_GBS * 1e9)) * 1e6
     return {"ms": round(ms, 4), "tflops": round(tf, 2), "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
             "roofline_us": round(bound_us, 2), "frac_of_roofline": round(bound_us / (ms * 1e3), 4),
+            "cold_ms": round(cold, 4), "cold_frac_of_roofline": round(bound_us / (cold * 1e3), 4),
             "flops": flops, "bytes": kv_bytes + qo_bytes}
+
+
+FLUSH_BYTES = 512 << 20   # more than the 256 MB of last-level cache (MALL)
+
+
+def cold_steps(step, reps, stream):
+    """Mean ms of `reps` single steps, each after a write of FLUSH_BYTES
+    (outside the timed region) that evicts the caches: the cold time."""
+    import torch
+    buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    total = 0.0
+    for i in range(reps):
+        buf.fill_(i & 0xFF)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        total += a.elapsed_time(b)
+    del buf
+    return total / reps
 
 
 def extra(args):
