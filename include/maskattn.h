@@ -310,7 +310,11 @@ size_t attn_verify_tree_workspace(int32_t batch, int32_t max_q, int32_t max_kv, 
  * round trip):
  *  cu_seqlens_q device int32 [batch+1], kv_lens device int32 [batch];
  *  max_q >= every q_len (<= 64), max_kv >= every kv_len (host bounds used for
- *  the launch shape and the workspace).
+ *  the launch shape and the workspace).  The host cannot check these bounds
+ *  against the device lengths: a sequence with more than max_q queries has
+ *  only its first max_q rows computed (its other rows of out and lse are not
+ *  written), keys at or past max_kv are not visited, and nothing outside the
+ *  launch's workspace, splits or buffers is read or written.
  * The GQA group of a K/V head is processed together (the group's query heads
  * share each K/V tile) and long contexts are split over several workgroups
  * whose partial results are merged in a fixed order.  Requires in_dtype BF16
@@ -369,7 +373,10 @@ size_t attn_decode_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32
  *            DENSE_BOOL / PACKED_U64  rows as for attn_verify_tree;
  * the same definitions as the prefill masks of the same kinds (RANGES:
  * pass the rows, MA_ERR_UNSUPPORTED otherwise).  Lengths stay on the device
- * as for attn_verify_tree.  The query heads of a K/V head's GQA group and
+ * as for attn_verify_tree, with the same max_q / max_kv bounds; a sequence
+ * with more than max_q queries is outside the contract: only its first
+ * max_q rows are written (positioned as if it had max_q queries) and nothing
+ * outside the buffers is read or written.  The query heads of a K/V head's GQA group and
  * their queries share each gathered K/V tile; long contexts are split over
  * workgroups and merged in a fixed order; a sliding window only walks the
  * tiles it can see.  A row that sees no key gets O = 0 and LSE = -inf.

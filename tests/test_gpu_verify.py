@@ -88,3 +88,41 @@ def test_short_mask_reads_missing_elements_as_masked(form):
     assert lse_err(lse, ref_l) <= 1e-2
     # the last sequence lost whole rows: they are empty
     assert torch.isneginf(lse[-1]).all() and (out[-1] == 0).all()
+
+
+@pytest.mark.parametrize("max_q,form", [(32, "packed"), (48, "packed"), (48, "dense")])
+def test_rows_past_max_q_are_left_alone(max_q, form):
+    """max_q is a host bound the device lengths may break (the host checks
+    only total_q <= batch * max_q): a sequence with more queries has its first
+    max_q rows computed, the others left untouched, and nothing past the
+    workspace or the launch's splits is touched.  max_q 32 takes the split
+    kernel (4 x 32 rows per workgroup), 48 the balanced one (4 x 48 > 128)."""
+    q_lens, kv_lens = [64, 10, 12], [700, 300, 950]
+    rng = W.rng_for(91)
+    w = W.gen._build("maxq", rng, "bf16", q_lens, kv_lens, 8, 2, 128, permute=True)
+    rows = []
+    for ql, kl in zip(q_lens, kv_lens):
+        m = np.zeros((ql, kl), dtype=bool)
+        m[:, :kl - ql] = True
+        m[:, kl - ql:] = rng.random((ql, ql)) < 0.5
+        m[np.arange(ql), kl - ql + np.arange(ql)] = True
+        rows.append(m)
+    w.masks["dense"] = W.gen.MaskInput("dense", data=np.concatenate([r.astype(np.uint8).reshape(-1) for r in rows]))
+    w.masks["packed"] = W.gen.MaskInput("packed", data=np.concatenate([W.pack_rows(r).reshape(-1) for r in rows]))
+    print("[case] rows past max_q", max_q, form, flush=True)
+    dev = device_inputs(w)
+    mi = w.masks[form]
+    data = mi.data if mi.kind == "dense" else mi.data.view(np.int64)
+    mask = torch.from_numpy(np.ascontiguousarray(data)).cuda()
+    out = torch.full(dev["q"].shape, 7.0, dtype=torch.float32, device="cuda")
+    lse = torch.full(dev["q"].shape[:2], 7.0, dtype=torch.float32, device="cuda")
+    ma.attn_verify_tree(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], mask, mi.kind,
+                        max_q, int(w.kv_lens.max()), w.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle(w, form)
+    t = np.concatenate([np.arange(n) for n in q_lens])
+    keep = t < max_q
+    done = torch.from_numpy(keep).cuda()
+    assert max_abs_err(out[done], ref_o[keep]) <= TOL_BF16
+    assert lse_err(lse[done], ref_l[keep]) <= 1e-2
+    assert (out[~done] == 7.0).all() and (lse[~done] == 7.0).all()
