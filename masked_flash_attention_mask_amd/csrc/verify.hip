@@ -1219,7 +1219,7 @@ __global__ __launch_bounds__(256) void dense_to_words(VerifyParams p, uint64_t *
     uint64_t bits = 0;
     // Rows start at any byte (their stride is kv_len bytes): the 64 bytes
     // are read as 17 dword-aligned dwords and shifted into place with
-    // v_alignbyte (16-byte loads at unaligned addresses are slow).  The
+    // v_alignbyte, so every load is aligned whatever the row's start.  The
     // 17th dword must lie inside the mask.
     const int64_t a4 = base & ~(int64_t)3;
     if (nb == 64 && a4 + 68 <= p.mask_numel) {
