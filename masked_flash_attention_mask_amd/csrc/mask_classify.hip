@@ -65,10 +65,14 @@ __device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t x) {
   return ((t * 0x00204081u) >> 21) & 0xFu;
 }
 
-// 32 bits for the bytes [base, base + nb) of a dense mask (nb <= 32).
+// 32 bits for the bytes [base, base + nb) of a dense mask (nb <= 32).  A
+// short run (a row's last) reads the same 32 bytes when they lie inside the
+// mask and masks off those past the row; only at the end of the mask are
+// bytes read one by one (predicated, all in flight at once).
 __device__ __forceinline__ uint32_t dense_half(const uint8_t *m8, int64_t base, int nb, int64_t numel) {
   uint32_t bits = 0;
-  if (nb == 32 && base + 32 <= numel) {
+  if (nb <= 0) return 0;
+  if (base + 32 <= numel) {
     dev::u32x4 v0, v1;
     __builtin_memcpy(&v0, m8 + base, 16);
     __builtin_memcpy(&v1, m8 + base + 16, 16);
@@ -77,9 +81,11 @@ __device__ __forceinline__ uint32_t dense_half(const uint8_t *m8, int64_t base, 
       bits |= nonzero_bytes4(v0[c]) << (4 * c);
       bits |= nonzero_bytes4(v1[c]) << (16 + 4 * c);
     }
+    if (nb < 32) bits &= (1u << nb) - 1u;
   } else {
-    for (int j = 0; j < nb; ++j)
-      if (base + j < numel && m8[base + j] != 0) bits |= 1u << j;
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if (j < nb && base + j < numel && m8[base + j] != 0) bits |= 1u << j;
   }
   return bits;
 }
@@ -149,7 +155,8 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p, ui
       for (int ci0 = 0; ci0 < cn; ci0 += kDenseBatch) {
         // Interior halves: two 16-byte loads each, all issued before any is
         // used (other lanes load the mask's last 32 bytes and discard them).
-        // Halves cut by kv_len, and masks under 32 bytes, take the byte loop.
+        // Halves cut by kv_len, and masks under 32 bytes, go through
+        // dense_half.
         dev::u32x4 v0[kDenseBatch], v1[kDenseBatch];
         bool fast[kDenseBatch];
         const bool can_fast = p.mask_numel >= 32;

@@ -219,7 +219,11 @@ __device__ __forceinline__ uint64_t fetch_word(const VerifyParams &p, int64_t mo
     const uint8_t *m8 = (const uint8_t *)p.mask;
     const int64_t base = moff + (int64_t)ti * kv + 64 * kt + 32 * half;
     const int nb = min(32, kv - 64 * kt - 32 * half);   // this half's bytes inside the row
-    if (nb == 32 && base + 32 <= p.mask_numel) {
+    if (nb <= 0) {
+      // the half lies past the row's last key
+    } else if (base + 32 <= p.mask_numel) {
+      // a short half (the row's last) reads the same 32 bytes and masks off
+      // those past the row
       u32x4 v0, v1;
       __builtin_memcpy(&v0, m8 + base, 16);
       __builtin_memcpy(&v1, m8 + base + 16, 16);
@@ -228,9 +232,11 @@ __device__ __forceinline__ uint64_t fetch_word(const VerifyParams &p, int64_t mo
         bits |= nonzero_bytes4(v0[c]) << (4 * c);
         bits |= nonzero_bytes4(v1[c]) << (16 + 4 * c);
       }
+      if (nb < 32) bits &= (1u << nb) - 1u;
     } else {
-      for (int j = 0; j < nb; ++j)
-        if (base + j < p.mask_numel && m8[base + j] != 0) bits |= 1u << j;
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if (j < nb && base + j < p.mask_numel && m8[base + j] != 0) bits |= 1u << j;
     }
   }
   const int src = 2 * (lane & 31);
@@ -1220,9 +1226,11 @@ __global__ __launch_bounds__(256) void dense_to_words(VerifyParams p, uint64_t *
     // Rows start at any byte (their stride is kv_len bytes): the 64 bytes
     // are read as 17 dword-aligned dwords and shifted into place with
     // v_alignbyte, so every load is aligned whatever the row's start.  The
-    // 17th dword must lie inside the mask.
+    // 17th dword must lie inside the mask.  A row's last word reads the same
+    // 64 bytes (those past the row belong to the next row, or the next
+    // sequence, and are masked off) rather than one byte at a time.
     const int64_t a4 = base & ~(int64_t)3;
-    if (nb == 64 && a4 + 68 <= p.mask_numel) {
+    if (a4 + 68 <= p.mask_numel) {
       const uint32_t sh = (uint32_t)(base & 3);
       const u32x4a4 *w4 = (const u32x4a4 *)(m8 + a4);
       uint32_t dw[17];
@@ -1236,9 +1244,13 @@ __global__ __launch_bounds__(256) void dense_to_words(VerifyParams p, uint64_t *
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         bits |= (uint64_t)nonzero_bytes4(__builtin_amdgcn_alignbyte(dw[i + 1], dw[i], sh)) << (4 * i);
+      if (nb < 64) bits &= (1ull << nb) - 1ull;
     } else {
-      for (int j = 0; j < nb; ++j)
-        if (base + j < p.mask_numel && m8[base + j] != 0) bits |= 1ull << j;
+      // the end of the mask buffer: predicated byte loads, all in flight
+      // at once
+#pragma unroll
+      for (int j = 0; j < 64; ++j)
+        if (j < nb && base + j < p.mask_numel && m8[base + j] != 0) bits |= 1ull << j;
     }
     if (woff + idx < cap) words[woff + idx] = bits;
   }
