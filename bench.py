@@ -44,9 +44,6 @@ KERNEL_SOURCES = ["masked_flash_attention_mask_amd/csrc/attn_fwd.hip",
                   "masked_flash_attention_mask_amd/csrc/tile_bf16.h",
                   "masked_flash_attention_mask_amd/csrc/tile_dma_bf16.h",
                   "masked_flash_attention_mask_amd/csrc/kernels_common.h"]
-VERIFY_SOURCES = ["masked_flash_attention_mask_amd/csrc/verify.hip",
-                  "masked_flash_attention_mask_amd/csrc/tile_dma_bf16.h",
-                  "masked_flash_attention_mask_amd/csrc/kernels_common.h"]
 PROFILES = os.path.join(ROOT, "profiles")
 # Counter summaries (key = value lines) of the kernels the lines report, each
 # tied to the kernel sources it was taken with.
