@@ -374,11 +374,16 @@ def _case(name):
         w = W.config3a()
         mask = name[6:]
         return w, mask, count_unmasked(w, mask)
+    if name.startswith("cfg1_"):
+        w = W.config1()
+        mask = name[5:]
+        return w, mask, count_unmasked(w, mask)
     raise ValueError(name)
 
 
 CASES = ["cfg5_ranges", "cfg5_packed", "cfg5_causal", "cfg4_chunk2", "cfg4_causal", "cfg3a_prefix_lm",
-         "cfg3a_causal", "cfg3b_window", "cfg3b_causal", "cfg2_packed", "cfg2_dense", "cfg2_causal"]
+         "cfg3a_causal", "cfg3b_window", "cfg3b_causal", "cfg2_packed", "cfg2_dense", "cfg2_causal",
+         "cfg1_causal", "cfg1_custom"]
 
 
 def only_case(name, steps, warmup):
@@ -389,10 +394,12 @@ def only_case(name, steps, warmup):
         print(json.dumps({"only": name, **r}), flush=True)
         return
     w, mask, n = _case(name)
-    ms, _, _ = run_config(w, mask, steps, warmup, torch.bfloat16)
+    f32 = w.dtype == "f32"   # config 1: fp32 in and out, against the fp32 peak
+    ms, _, _ = run_config(w, mask, steps, warmup, torch.float32 if f32 else torch.bfloat16)
     tf = 4.0 * w.d * w.hq * n / (ms * 1e-3) / 1e12
-    print(json.dumps({"only": name, "ms": round(ms, 4), "tflops": round(tf, 2),
-                      "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
+    print(json.dumps({"only": name, "ms": round(ms, 5 if f32 else 4), "tflops": round(tf, 4 if f32 else 2),
+                      "pct_of_peak": round(100 * tf / (PEAK_FP32_TFLOPS if f32 else PEAK_BF16_TFLOPS), 3)}),
+          flush=True)
 
 
 def main():
