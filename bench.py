@@ -261,12 +261,14 @@ def sampled_units(w, budget_flops=3e11, row_block=512):
     return units
 
 
-def oracle_line(w, name, budget_flops=3e11):
+def oracle_line(w, name, budget_flops=1e12):
     """cpu_baseline-style oracle timing for one workload and mask."""
     from oracle import masks as OM
     mi = w.masks[name]
     masks = []
-    for b in range(w.batch):
+    if mi.kind in ("packed", "dense"):
+        masks = (OM.packed_from_flat if mi.kind == "packed" else OM.dense_from_flat)(mi.data, w.q_lens, w.kv_lens)
+    for b in range(w.batch if not masks else 0):
         ql, kl = int(w.q_lens[b]), int(w.kv_lens[b])
         if mi.kind == "causal":
             masks.append(OM.causal(ql, kl))
@@ -622,10 +624,10 @@ def extra(args):
                           "pct_of_fp32_peak": round(100 * tf / PEAK_FP32_TFLOPS, 3), "compile_ms": round(cms, 3),
                           "unmasked_per_head": n}), flush=True)
     rows = []
-    w = W.config4()
+    w4 = W.config4()
     for name in ("chunk4", "chunk16", "chunk2_full", "causal"):
-        ms, cms, plan = run_config(w, name, args.steps, args.warmup, torch.bfloat16)
-        rows.append(("cfg4", name, ms, cms, w))
+        ms, cms, plan = run_config(w4, name, args.steps, args.warmup, torch.bfloat16)
+        rows.append(("cfg4", name, ms, cms, w4))
     w3a = W.config3a()
     for name in ("prefix_lm", "causal"):
         ms, cms, plan = run_config(w3a, name, args.steps, args.warmup, torch.bfloat16)
@@ -648,7 +650,8 @@ def extra(args):
         print(json.dumps({"workload": "cfg2", "mask": "tree_" + form if form != "causal" else "causal", **r}),
               flush=True)
     if not args.no_cpu:
-        for wl, name in ((w1, "causal"), (w3a, "prefix_lm"), (W.config3b(0), "window"), (w, "chunk2")):
+        for wl, name in ((w1, "causal"), (w2, "tree_packed"), (w3a, "prefix_lm"), (W.config3b(0), "window"),
+                         (w4, "chunk2")):
             print(json.dumps({"workload": wl.name, "mask": name, "cpu_oracle": oracle_line(wl, name)}), flush=True)
 
 

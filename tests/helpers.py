@@ -1,6 +1,9 @@
 """Shared plumbing for the GPU parity tests: device copies of a workload, the
 library calls, the oracle's masks for the same inputs, and error metrics."""
 
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -17,6 +20,17 @@ TOL_BF16 = 1.5e-2   # bf16 inputs, fp32 accumulation, fp32 output
 # leaves room for the max over a row against the row's RMS.  A wrong index,
 # sign, scale or a dropped term moves a row by O(1) of its RMS.
 TOL_GRAD = 2.0 ** -5
+
+
+def parity_report(tag, **vals):
+    """Appends one JSON line (the case and its measured errors) to the file
+    that MASKATTN_PARITY_REPORT names, when it is set; does nothing
+    otherwise.  The full-size cases call it so that one run of the GPU tests
+    yields every configuration's error against the oracle."""
+    path = os.environ.get("MASKATTN_PARITY_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"case": tag, **{k: float(v) for k, v in vals.items()}}) + "\n")
 
 
 def compile_plan(w, mask_name, tile_q=128, device_mask=True):

@@ -7,7 +7,8 @@ import torch
 
 import masked_flash_attention_mask_amd as ma
 import workloads as W
-from helpers import (TOL_BF16, TOL_F32, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle, repage,
+from helpers import (TOL_BF16, TOL_F32, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle, parity_report,
+                     repage,
                      run_prefill)
 
 pytestmark = pytest.mark.gpu
@@ -26,6 +27,7 @@ def test_config1_fp32(mask, tile_q):
     d = device_inputs(w)
     out, lse, _ = run_prefill(w, d, mask, tile_q=tile_q)
     ref_o, ref_l = oracle(w, mask)
+    parity_report(f"cfg1 {mask} tile_q {tile_q}", max_abs_err=max_abs_err(out, ref_o), lse_err=lse_err(lse, ref_l))
     assert max_abs_err(out, ref_o) <= TOL_F32
     assert lse_err(lse, ref_l) <= TOL_F32
 
@@ -252,6 +254,8 @@ def test_config4_full_size_sampled():
     for cs in (2, 16):
         assert torch.equal(outs[f"chunk{cs}"][0], outs[f"chunk{cs}_full"][0])
         ref_o, ref_l = oracle(w, f"chunk{cs}", heads=[0, 7, 15], rows=rows)
+        parity_report(f"cfg4 chunk{cs} sampled", max_abs_err=max_abs_err(outs[f"chunk{cs}"][0], ref_o),
+                      lse_err=lse_err(outs[f"chunk{cs}"][1], ref_l))
         assert max_abs_err(outs[f"chunk{cs}"][0], ref_o) <= TOL_BF16
         assert lse_err(outs[f"chunk{cs}"][1], ref_l) <= 1e-2
 
@@ -266,6 +270,7 @@ def test_config5_full_size_sampled():
     o2, l2, _ = run_prefill(w, dev, "custom_packed")
     assert torch.equal(o1, o2)
     ref_o, ref_l = oracle(w, "custom_ranges", heads=[0, 13, 31], rows={0: rows})
+    parity_report("cfg5 ranges = packed, sampled", max_abs_err=max_abs_err(o1, ref_o), lse_err=lse_err(l1, ref_l))
     assert max_abs_err(o1, ref_o) <= TOL_BF16
     assert lse_err(l1, ref_l) <= 1e-2
 
@@ -279,6 +284,7 @@ def test_config3a_full_size_sampled():
     o2, _, _ = run_prefill(w, dev, "prefix_lm_ranges")
     assert torch.equal(o1, o2)
     ref_o, ref_l = oracle(w, "prefix_lm", heads=[0, 31], rows=rows)
+    parity_report("cfg3a prefix_lm = ranges, sampled", max_abs_err=max_abs_err(o1, ref_o), lse_err=lse_err(l1, ref_l))
     assert max_abs_err(o1, ref_o) <= TOL_BF16
     assert lse_err(l1, ref_l) <= 1e-2
 
@@ -311,6 +317,7 @@ def test_config3b_full_size_sampled_and_not_vacuous():
     local, _, _ = run_prefill(w0, dev, "window")
     glob, _, _ = run_prefill(w0, dev, "causal")
     ref_o, _ = oracle(w0, "window", heads=[0, 5], rows=rows)
+    parity_report("cfg3b window 4096, sampled", max_abs_err=max_abs_err(local, ref_o))
     assert max_abs_err(local, ref_o) <= TOL_BF16
     # the window bites: local and global outputs differ far beyond tolerance
     assert (local - glob).abs().max().item() > 0.1
@@ -321,6 +328,7 @@ def test_config3b_full_size_sampled_and_not_vacuous():
     w1 = W.config3b(1)
     g1, _, _ = run_prefill(w1, device_inputs(w1), "causal")
     ref1, _ = oracle(w1, "causal", heads=[3], rows=rows)
+    parity_report("cfg3b causal, sampled", max_abs_err=max_abs_err(g1, ref1))
     assert max_abs_err(g1, ref1) <= TOL_BF16
 
 

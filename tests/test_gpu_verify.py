@@ -7,7 +7,7 @@ import torch
 
 import masked_flash_attention_mask_amd as ma
 import workloads as W
-from helpers import TOL_BF16, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle
+from helpers import TOL_BF16, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle, parity_report
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +30,8 @@ def test_config2_full():
     o_d, l_d = _run(w, dev, "tree_dense")
     assert torch.equal(o_p, o_d) and torch.equal(l_p, l_d)
     ref_o, ref_l = oracle(w, "tree_packed")
+    parity_report("cfg2 tree packed = dense, every element", max_abs_err=max_abs_err(o_p, ref_o),
+                  lse_err=lse_err(l_p, ref_l))
     assert max_abs_err(o_p, ref_o) <= TOL_BF16
     assert lse_err(l_p, ref_l) <= 1e-2
     o2, l2 = _run(w, dev, "tree_packed")
