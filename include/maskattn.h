@@ -230,7 +230,8 @@ ma_status mask_plan_serialize(const ma_plan *plan, void *dst, size_t *bytes);
  * in_dtype F32 with d in {64, 128} and out_dtype F32.  Arithmetic: fp32
  * accumulation; bf16 inputs use bf16 matrix products, fp32 inputs fp32 ones.
  * Launches are stream-ordered; the call does not synchronise.  Results are
- * deterministic (no atomics touch accumulators). */
+ * deterministic (no atomics touch accumulators).  A plan with no query rows
+ * (total_q 0) launches nothing; q and out may then be NULL. */
 ma_status attn_prefill_masked(const ma_plan *plan, const void *q, int64_t total_q, int32_t hq,
                               const void *k_cache, const void *v_cache, int32_t hkv, int32_t d,
                               int32_t page_size, const int64_t kv_strides[3],
@@ -282,6 +283,8 @@ size_t attn_backward_workspace(const ma_plan *plan, int32_t hq);
  *           when no query sees the key); other slots are not touched.  No two
  *           sequences may map keys to the same slot.
  *  workspace device, >= attn_backward_workspace(plan, hq) bytes, scratch.
+ * With no query rows (total_q 0) q, out, dout, lse, dq and the workspace may
+ * be NULL; dK and dV are still written (zeros) for every key below kv_len.
  * Supported: d in {64, 128, 256}; plans with tile_k 64 and tile_q 64 or 128.
  * The first call on a plan builds its key-major transpose (one device
  * allocation, held until mask_plan_destroy; synchronises `stream` once);

@@ -23,10 +23,11 @@ int log2i(int64_t x) {
   return s;
 }
 
+// q and out are required when there are query rows (rows = total_q > 0).
 ma_status check_paged(const void *q, const void *k, const void *v, const void *out,
                       const int32_t *page_table, int32_t hq, int32_t hkv, int32_t page_size,
-                      const int64_t *strides, int32_t max_pages, float scale) {
-  if (!q || !k || !v || !out || !page_table || !strides)
+                      const int64_t *strides, int32_t max_pages, float scale, bool rows) {
+  if (!k || !v || !page_table || !strides || (rows && (!q || !out)))
     return set_error(MA_ERR_INVALID, "q, k_cache, v_cache, page_table, kv_strides and out are required");
   if (hq < 1 || hkv < 1 || hq % hkv != 0)
     return set_error(MA_ERR_INVALID, "Hq (%d) must be a positive multiple of Hkv (%d)", hq, hkv);
@@ -214,7 +215,7 @@ ma_status attn_prefill_masked(const ma_plan *plan, const void *q, int64_t total_
   clear_error();
   if (!plan) return set_error(MA_ERR_INVALID, "plan is NULL");
   ma_status st = check_paged(q, k_cache, v_cache, out, page_table, hq, hkv, page_size, kv_strides,
-                             max_pages, scale);
+                             max_pages, scale, total_q > 0);
   if (st != MA_OK) return st;
   if (total_q != plan->total_q)
     return set_error(MA_ERR_PLAN_MISMATCH, "total_q %lld differs from the plan's %lld",
@@ -272,7 +273,7 @@ ma_status attn_prefill_masked_fp8(const ma_plan *plan, const void *q, int64_t to
   clear_error();
   if (!plan) return set_error(MA_ERR_INVALID, "plan is NULL");
   ma_status st = check_paged(q, k_cache, v_cache, out, page_table, hq, hkv, page_size, kv_strides,
-                             max_pages, scale);
+                             max_pages, scale, total_q > 0);
   if (st != MA_OK) return st;
   for (float f : {q_descale, k_descale, v_descale})
     if (!std::isfinite(f) || !(f > 0.f)) return set_error(MA_ERR_INVALID, "descale factors must be positive and finite");
@@ -339,9 +340,9 @@ ma_status attn_backward_masked(ma_plan *plan, const void *q, int64_t total_q, in
   clear_error();
   if (!plan) return set_error(MA_ERR_INVALID, "plan is NULL");
   ma_status st = check_paged(q, k_cache, v_cache, out, page_table, hq, hkv, page_size, kv_strides,
-                             max_pages, scale);
+                             max_pages, scale, total_q > 0);
   if (st != MA_OK) return st;
-  if (!dout || !lse || !dq || !dk_cache || !dv_cache)
+  if (!dk_cache || !dv_cache || (total_q > 0 && (!dout || !lse || !dq)))
     return set_error(MA_ERR_INVALID, "dout, lse, dq, dk_cache and dv_cache are required");
   if (total_q != plan->total_q)
     return set_error(MA_ERR_PLAN_MISMATCH, "total_q %lld differs from the plan's %lld",
@@ -357,9 +358,10 @@ ma_status attn_backward_masked(ma_plan *plan, const void *q, int64_t total_q, in
   if (out_dtype != MA_BF16 && out_dtype != MA_F32)
     return set_error(MA_ERR_UNSUPPORTED, "out dtype %d", out_dtype);
   if (kv_strides[2] < d) return set_error(MA_ERR_INVALID, "head stride %lld < head_dim", (long long)kv_strides[2]);
-  if (total_q == 0 || plan->num_rows == 0) return MA_OK;
+  // No early return for a plan without query rows: dK / dV of its keys are
+  // still written (zeros); the passes over query rows then have empty grids.
   const size_t need = backward_workspace(total_q, hq);
-  if (!workspace || ws_bytes < need)
+  if (need > 0 && (!workspace || ws_bytes < need))
     return set_error(MA_ERR_SIZE, "workspace of %zu bytes is below the %zu required", ws_bytes, need);
   if (!plan->on_device) {
     st = plan_upload(plan, stream);
@@ -406,8 +408,9 @@ static ma_status check_small_q(const void *q, const void *k_cache, const void *v
                                const int32_t *cu_seqlens_q, const int32_t *kv_lens, int32_t batch,
                                int32_t max_q, int32_t max_kv, int32_t in_dtype, int32_t out_dtype, int32_t d,
                                int64_t total_q) {
+  // q and out are always required here: the rows are counted on the device
   ma_status st = check_paged(q, k_cache, v_cache, out, page_table, hq, hkv, page_size, kv_strides,
-                             max_pages, scale);
+                             max_pages, scale, true);
   if (st != MA_OK) return st;
   if (!cu_seqlens_q || !kv_lens) return set_error(MA_ERR_INVALID, "cu_seqlens_q and kv_lens are required");
   if (batch < 1) return set_error(MA_ERR_INVALID, "batch must be >= 1");

@@ -107,6 +107,45 @@ def test_backward_slots_contract():
     assert grad_err(torch.from_numpy(np.where(used[..., None, None], dkn, 0.0)), rk) <= TOL_GRAD
 
 
+def test_backward_empty_sequences():
+    """A sequence without queries gets its keys' slots written 0, one whose
+    queries have no keys gets dQ = 0 for its rows, the rest matches the
+    oracle; a batch without any query row still writes dK = dV = 0 for every
+    key below kv_len (dQ, dO, O, LSE and the workspace empty) and leaves the
+    other slots as passed."""
+    sentinel = 7.0
+    for q_lens, kv_lens in (([0, 50, 40], [70, 0, 130]), ([0, 0], [5, 0])):
+        _say("backward empty", q_lens, kv_lens)
+        w = W.gen._build("bwd_empty", W.rng_for(60 + len(q_lens)), "bf16", q_lens, kv_lens, 4, 2, 128,
+                         permute=True)
+        w.masks["causal"] = W.MaskInput("causal")
+        do = W.upstream_grad(w, 61)
+        dev = device_inputs(w)
+        dev["do"] = torch.from_numpy(do).cuda().to(torch.bfloat16).contiguous()
+        out, lse = _fwd_oracle(w, "causal")
+        dk0 = torch.full(dev["k"].shape, sentinel, dtype=torch.float32, device="cuda")
+        dv0 = torch.full(dev["k"].shape, sentinel, dtype=torch.float32, device="cuda")
+        dq, dk, dv = _bwd(w, dev, "causal", out, lse, dk=dk0, dv=dv0)
+        used = np.zeros(w.k_cache.shape[:2], bool)
+        for b, kl in enumerate(w.kv_lens):
+            j = np.arange(int(kl))
+            used[w.page_table[b, j // w.page_size], j % w.page_size] = True
+        dkn, dvn = dk.cpu().numpy(), dv.cpu().numpy()
+        assert np.all(dkn[~used] == sentinel) and np.all(dvn[~used] == sentinel)
+        # keys of the first sequence: no query sees them
+        j = np.arange(int(kv_lens[0]))
+        pg, sl = w.page_table[0, j // w.page_size], j % w.page_size
+        assert np.all(dkn[pg, sl] == 0) and np.all(dvn[pg, sl] == 0)
+        if sum(q_lens) == 0:
+            assert dq.shape[0] == 0
+            continue
+        assert torch.all(dq[:50] == 0)
+        rq, rk, rv = _ref(w, do, "causal")
+        assert grad_err(dq, rq) <= TOL_GRAD
+        assert grad_err(torch.from_numpy(np.where(used[..., None, None], dkn, 0.0)), rk) <= TOL_GRAD
+        assert grad_err(torch.from_numpy(np.where(used[..., None, None], dvn, 0.0)), rv) <= TOL_GRAD
+
+
 def test_backward_after_gpu_forward():
     """End to end: the library's own forward (bf16 output) feeds the backward.
     D = rowsum(dO * O) then carries O's bf16 rounding, |dD| <= 2^-9

@@ -108,6 +108,36 @@ def test_bf16_ragged_kinds(d, tile_q):
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
+def test_empty_sequences_and_keyless_rows(d):
+    """Sequences without queries, one whose 50 queries have no keys (their
+    rows come out O = 0, LSE = -inf), under every host-described kind and a
+    device-resident custom mask; then a batch without any query row, which
+    launches nothing and accepts the empty tensors' NULL pointers."""
+    q_lens, kv_lens = [0, 50, 0, 3, 40], [10, 0, 0, 70, 130]
+    w = _ragged(400 + d, d, 4, 2, q_lens, kv_lens)
+    w.masks["causal"] = W.MaskInput("causal")
+    w.masks["window"] = W.MaskInput("window", window=9)
+    w.masks["prefix"] = W.MaskInput("prefix_lm", prefix_len=np.array([4, 0, 0, 5, 64], np.int32))
+    w.masks["ranges"] = W.MaskInput("ranges", ranges=[[], [], [], [(0, 3, 0, 70, W.R_FULL, 0)],
+                                                       [(0, 40, 0, 130, W.R_CAUSAL, 0)]])
+    rng = np.random.default_rng(d)
+    dense = [rng.random((q, k)) < 0.5 for q, k in zip(q_lens, kv_lens)]
+    w.masks["custom"] = W.MaskInput("dense", data=np.concatenate([m.astype(np.uint8).reshape(-1) for m in dense]))
+    dev = device_inputs(w)
+    for mask in ("causal", "window", "prefix", "ranges", "custom"):
+        _say("empty sequences", d, mask)
+        out, lse, _ = run_prefill(w, dev, mask)
+        ref_o, ref_l = oracle(w, mask)
+        assert max_abs_err(out, ref_o) <= TOL_BF16, mask
+        assert lse_err(lse, ref_l) <= 1e-2, mask
+        assert torch.all(out[:50] == 0) and torch.all(torch.isneginf(lse[:50])), mask
+    e = _ragged(500 + d, d, 4, 2, [0, 0], [5, 0])
+    e.masks["causal"] = W.MaskInput("causal")
+    out, lse, _ = run_prefill(e, device_inputs(e), "causal")
+    assert out.shape == (0, 4, d) and lse.shape == (0, 4)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_bf16_page_sizes_and_gather_modes(d):
     """Pages of 512 / d keys or more take the direct-to-LDS gather (one page
     id per instruction, or per wave once pages hold a wave's whole run of
