@@ -107,6 +107,57 @@ def test_bf16_ragged_kinds(d, tile_q):
     assert torch.all(out[200] == 0) and torch.all(torch.isneginf(lse[200]))
 
 
+@pytest.mark.parametrize("tile_q", [128, 64])
+def test_degenerate_masks(tile_q):
+    """Cases that reduce to something exact: a window of 1 key leaves each
+    row its own key, P = 1 and O = that key's V row bit for bit; an all-true
+    custom mask and a prefix covering every key are full attention (the
+    FULL range's plan, so identical outputs); an all-false custom mask
+    empties every row (O = 0, LSE = -inf); a window at least as long as the
+    keys is causal; causal with more queries than keys leaves the first
+    q_len - kv_len rows empty (bottom-right alignment)."""
+    q_lens, kv_lens = [100, 130, 70], [40, 130, 200]
+    w = _ragged(600 + tile_q, 128, 4, 2, q_lens, kv_lens)
+    w.masks["causal"] = W.MaskInput("causal")
+    w.masks["w1"] = W.MaskInput("window", window=1)
+    w.masks["w_long"] = W.MaskInput("window", window=256)
+    w.masks["full"] = W.MaskInput("ranges", ranges=[[(0, q, 0, k, W.R_FULL, 0)] for q, k in zip(q_lens, kv_lens)])
+    w.masks["prefix_all"] = W.MaskInput("prefix_lm", prefix_len=np.array(kv_lens, np.int32))
+    n = sum(q * k for q, k in zip(q_lens, kv_lens))
+    w.masks["ones"] = W.MaskInput("dense", data=np.ones(n, np.uint8))
+    w.masks["zeros"] = W.MaskInput("dense", data=np.zeros(n, np.uint8))
+    dev = device_inputs(w)
+    res = {}
+    for mask in ("causal", "w1", "w_long", "full", "prefix_all", "ones", "zeros"):
+        _say("degenerate", tile_q, mask)
+        res[mask] = run_prefill(w, dev, mask, tile_q=tile_q)[:2]
+    for mask in ("causal", "w1", "full"):
+        ref_o, ref_l = oracle(w, mask)
+        assert max_abs_err(res[mask][0], ref_o) <= TOL_BF16, mask
+        assert lse_err(res[mask][1], ref_l) <= 1e-2, mask
+    for a, b in (("ones", "full"), ("prefix_all", "full"), ("w_long", "causal")):
+        assert torch.equal(res[a][0], res[b][0]) and torch.equal(res[a][1], res[b][1]), (a, b)
+    o0, l0 = res["zeros"]
+    assert torch.all(o0 == 0) and torch.all(torch.isneginf(l0))
+    # window 1: row t of a sequence sees key t + kv_len - q_len only
+    o1 = res["w1"][0].cpu().numpy()
+    t0 = 0
+    for b, (q, k) in enumerate(zip(q_lens, kv_lens)):
+        for t in range(q):
+            key = t + k - q
+            if key < 0:
+                assert np.all(o1[t0 + t] == 0)
+                continue
+            page, slot = w.page_table[b, key // w.page_size], key % w.page_size
+            v = w.v_cache[page, slot].astype(np.float32)            # [Hkv, d], bf16 values
+            want = np.repeat(v, w.hq // w.hkv, axis=0)
+            assert np.array_equal(o1[t0 + t], want), (b, t)
+        t0 += q
+    # causal with 100 queries over 40 keys: rows 0..59 see nothing
+    oc, lc = res["causal"]
+    assert torch.all(oc[:60] == 0) and torch.all(torch.isneginf(lc[:60]))
+    assert torch.all(torch.isfinite(lc[60:100]))
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_empty_sequences_and_keyless_rows(d):
     """Sequences without queries, one whose 50 queries have no keys (their
