@@ -1120,8 +1120,8 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
 }
 
 // Merges the pieces of a cut unit: block (u, c) takes unit u's first piece
-// i from unit_slot[u] and 256 (row, 4 columns) items of the unit's 256 x D
-// outputs (item = c * 256 + thread, D / 4 items per row) and merges the
+// i from unit_slot[u] and 256 (row, 8 columns) items of the unit's 256 x D
+// outputs (item = c * 256 + thread, D / 8 items per row) and merges the
 // pieces i, i + 1, ... in order:
 // O = sum_s exp(LSE_s - M) O_s / sum_s exp(LSE_s - M), LSE = M + ln(sum).
 // unit_slot keeps entries of earlier launches for units that have no piece
@@ -1149,21 +1149,22 @@ __global__ __launch_bounds__(256) void verify_pipe_combine(VerifyParams p, const
   if (cu.b != u / p.nhb || cu.hb != u % p.nhb) return;
   const int hb = cu.hb, np = cu.npieces, q0 = cu.q0, q_len = cu.q_len;
   const int item = blockIdx.y * 256 + threadIdx.x;
-  const int r = item / (D / 4), c4 = item % (D / 4);
+  const int r = item / (D / 8), c8 = item % (D / 8);
   const int t = r % p.qs;
   if (r / p.qs >= p.gh || t >= q_len) return;
   const int h = hb * p.gh + r / p.qs;
   float m_run = neg_inf(), l_run = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < np; k0 += kMergeBatch) {
     float lse_k[kMergeBatch];
-    f32x4 o_k[kMergeBatch];
+    f32x4 o_k[kMergeBatch], o2_k[kMergeBatch];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
       const bool has = k0 + k < np;
       const int64_t row = (int64_t)(wg + k0 + k) * kPipeRows + r;
       lse_k[k] = has ? p.ws_lse[row] : neg_inf();
-      o_k[k] = has ? load4f((const OutT *)p.ws_o + row * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      o_k[k] = has ? load4f((const OutT *)p.ws_o + row * D + 8 * c8) : f32x4{0.f, 0.f, 0.f, 0.f};
+      o2_k[k] = has ? load4f((const OutT *)p.ws_o + row * D + 8 * c8 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float mx = m_run;
 #pragma unroll
@@ -1172,19 +1173,23 @@ __global__ __launch_bounds__(256) void verify_pipe_combine(VerifyParams p, const
     const float sc = __expf(m_run - mx);   // 0 while nothing was merged
     l_run *= sc;
     acc *= sc;
+    acc2 *= sc;
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
       const float wgt = __expf(lse_k[k] - mx);
       l_run += wgt;
       acc += wgt * o_k[k];
+      acc2 += wgt * o2_k[k];
     }
     m_run = mx;
   }
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   const int64_t tok = (int64_t)q0 + t;
-  store4<OutT>((OutT *)p.out + (tok * p.hq + h) * D + 4 * c4, acc[0] * inv, acc[1] * inv, acc[2] * inv,
+  store4<OutT>((OutT *)p.out + (tok * p.hq + h) * D + 8 * c8, acc[0] * inv, acc[1] * inv, acc[2] * inv,
                acc[3] * inv);
-  if (p.lse && c4 == 0) p.lse[tok * p.hq + h] = l_run > 0.f ? m_run + __logf(l_run) : neg_inf();
+  store4<OutT>((OutT *)p.out + (tok * p.hq + h) * D + 8 * c8 + 4, acc2[0] * inv, acc2[1] * inv, acc2[2] * inv,
+               acc2[3] * inv);
+  if (p.lse && c8 == 0) p.lse[tok * p.hq + h] = l_run > 0.f ? m_run + __logf(l_run) : neg_inf();
 }
 
 // Dense mask rows -> packed words (key j of a row -> bit j % 64 of word
@@ -1435,7 +1440,7 @@ ma_status run_pipe(const VerifyArgs &a, VerifyParams prm, const PipeShape &ps) {
   hipLaunchKernelGGL(kern, dim3(ps.grid), dim3(kPipeWaves * 64), lds, s, prm, cuts, unit_slot);
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify launch: %s", hipGetErrorString(e));
-  hipLaunchKernelGGL((verify_pipe_combine<D, OutT>), dim3(a.batch * ps.nhb, kPipeRows * (D / 4) / 256), dim3(256), 0,
+  hipLaunchKernelGGL((verify_pipe_combine<D, OutT>), dim3(a.batch * ps.nhb, kPipeRows * (D / 8) / 256), dim3(256), 0,
                      s, prm, (const CutUnit *)cuts, (const int32_t *)unit_slot);
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify combine launch: %s", hipGetErrorString(e));
