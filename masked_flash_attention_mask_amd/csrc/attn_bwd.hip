@@ -28,37 +28,6 @@ using namespace dev;
 
 namespace {
 
-// LDS rows of K, V, Q and dO in the backward: stride d + 8 (4 banks modulo
-// 64), conflict-free for the row reads of the A operands; the transposed
-// reads (ds_read_b64_tr_b16) of the dQ / dK / dV products accept some
-// conflicts on this stride.
-template <int D>
-struct BwdStage {
-  static constexpr int S = D + 8;
-  static constexpr int TILE = 64 * S;   // elements of one 64-row matrix
-};
-
-// The lane's 8-element operand of rows [r0, r0 + 32) of a row-major matrix
-// (rows = the MFMA's 32 rows, K-slots d 16 k + 8 hi .. + 7).
-template <int D>
-__device__ __forceinline__ bf16x8 row_op(const uint16_t *m, int l32, int hi, int k) {
-  return __builtin_bit_cast(bf16x8, *(const u32x4 *)(m + l32 * BwdStage<D>::S + 8 * hi + 16 * k));
-}
-
-// Transposed operand of d-block n and 16-row step u of a row-major matrix
-// (A = M^T: lane = d, K-slots = rows base + 8 (e / 4) + 4 (l / 32) + e % 4,
-// base = 16 u), read with ds_read_b64_tr_b16 as in the forward's V^T.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_op(const uint16_t *m, int lane, int u, int n) {
-  constexpr int S = BwdStage<D>::S;
-  const uint16_t *p = m + (4 * (lane >> 5) + ((lane & 15) >> 2)) * S + 16 * ((lane >> 4) & 1) + 4 * (lane & 3) +
-                      16 * u * S + 32 * n;
-  const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)p);
-  const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p + 8 * S));
-  const i16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16 &s, int half) {
   f32x8 v;
 #pragma unroll
