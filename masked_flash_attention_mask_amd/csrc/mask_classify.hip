@@ -68,7 +68,7 @@ __device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t x) {
 // 32 bits for the bytes [base, base + nb) of a dense mask (nb <= 32).  A
 // short run (a row's last) reads the same 32 bytes when they lie inside the
 // mask and masks off those past the row; only at the end of the mask are
-// bytes read one by one (predicated, all in flight at once).
+// bytes read one by one.
 __device__ __forceinline__ uint32_t dense_half(const uint8_t *m8, int64_t base, int nb, int64_t numel) {
   uint32_t bits = 0;
   if (nb <= 0) return 0;
@@ -83,9 +83,8 @@ __device__ __forceinline__ uint32_t dense_half(const uint8_t *m8, int64_t base, 
     }
     if (nb < 32) bits &= (1u << nb) - 1u;
   } else {
-#pragma unroll
-    for (int j = 0; j < 32; ++j)
-      if (j < nb && base + j < numel && m8[base + j] != 0) bits |= 1u << j;
+    for (int j = 0; j < nb; ++j)
+      if (base + j < numel && m8[base + j] != 0) bits |= 1u << j;
   }
   return bits;
 }

@@ -234,9 +234,9 @@ __device__ __forceinline__ uint64_t fetch_word(const VerifyParams &p, int64_t mo
       }
       if (nb < 32) bits &= (1u << nb) - 1u;
     } else {
-#pragma unroll
-      for (int j = 0; j < 32; ++j)
-        if (j < nb && base + j < p.mask_numel && m8[base + j] != 0) bits |= 1u << j;
+      // the end of the mask buffer only: byte by byte
+      for (int j = 0; j < nb; ++j)
+        if (base + j < p.mask_numel && m8[base + j] != 0) bits |= 1u << j;
     }
   }
   const int src = 2 * (lane & 31);
@@ -1251,11 +1251,9 @@ __global__ __launch_bounds__(256) void dense_to_words(VerifyParams p, uint64_t *
         bits |= (uint64_t)nonzero_bytes4(__builtin_amdgcn_alignbyte(dw[i + 1], dw[i], sh)) << (4 * i);
       if (nb < 64) bits &= (1ull << nb) - 1ull;
     } else {
-      // the end of the mask buffer: predicated byte loads, all in flight
-      // at once
-#pragma unroll
-      for (int j = 0; j < 64; ++j)
-        if (j < nb && base + j < p.mask_numel && m8[base + j] != 0) bits |= 1ull << j;
+      // the end of the mask buffer only: byte by byte
+      for (int j = 0; j < nb; ++j)
+        if (base + j < p.mask_numel && m8[base + j] != 0) bits |= 1ull << j;
     }
     if (woff + idx < cap) words[woff + idx] = bits;
   }
