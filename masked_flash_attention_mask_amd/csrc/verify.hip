@@ -136,6 +136,10 @@ struct VerifyParams {
   // balanced tree verify (verify_pipe_kernel): head blocks per sequence,
   // workgroups, sequences
   int32_t nhb, grid, batch;
+  // dense rows that verify_pipe_kernel turns into `mask` (the packed words)
+  // itself, piece by piece; NULL when the mask is packed
+  const void *dense;
+  int64_t dense_numel;
 };
 
 __device__ __forceinline__ int64_t mask_offset(const VerifyParams &p, int b) {
@@ -193,14 +197,49 @@ __device__ __forceinline__ uint64_t row_word(const VerifyParams &p, int64_t moff
   }
 }
 
+// Four dwords that need only dword alignment (a 16-byte load from any
+// dword address).
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 // Bits (LSB = lowest address) of the nonzero bytes of a dword: per byte the
 // high bit is set iff the byte is nonzero (SWAR), then one multiply moves the
 // four high bits to bits 21..24 (distinct partial products, no carries).
-typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
-
 __device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t x) {
   const uint32_t t = ((((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) >> 7) & 0x01010101u;
   return ((t * 0x00204081u) >> 21) & 0xFu;
+}
+
+// The packed word of dense mask bytes [base, base + nb), 1 <= nb <= 64 (byte
+// j -> bit j); bytes at or past numel read as 0.  Rows start at any byte
+// (their stride is kv_len bytes): the 64 bytes are read as 17 dword-aligned
+// dwords and shifted into place with v_alignbyte, so every load is aligned
+// whatever the row's start.  A row's last word reads the same 64 bytes
+// (those past the row belong to the next row, or the next sequence) and
+// masks off the bits past nb; only at the end of the buffer, where the 17th
+// dword would lie past it, are bytes read one by one.
+__device__ __forceinline__ uint64_t dense_word(const uint8_t *m8, int64_t numel, int64_t base, int nb) {
+  uint64_t bits = 0;
+  const int64_t a4 = base & ~(int64_t)3;
+  if (a4 + 68 <= numel) {
+    const uint32_t sh = (uint32_t)(base & 3);
+    const u32x4a4 *w4 = (const u32x4a4 *)(m8 + a4);
+    uint32_t dw[17];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4a4 v = w4[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dw[4 * q + e] = v[e];
+    }
+    dw[16] = ((const uint32_t *)(m8 + a4))[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      bits |= (uint64_t)nonzero_bytes4(__builtin_amdgcn_alignbyte(dw[i + 1], dw[i], sh)) << (4 * i);
+    if (nb < 64) bits &= (1ull << nb) - 1ull;
+  } else {
+    for (int j = 0; j < nb; ++j)
+      if (base + j < numel && m8[base + j] != 0) bits |= 1ull << j;
+  }
+  return bits;
 }
 
 // The lane's row word for k-tile kt.  A dense mask is read by lane pairs:
@@ -806,6 +845,7 @@ struct Piece {
   int b, hb, kt0, kt1, n, k, npieces;
   int64_t moff;
   int q0, q_len, kv_len;   // the sequence's first query row, rows (seq_q_len), keys
+  int64_t doff;            // the sequence's first byte in the dense layout
 };
 
 // Every lane returns the same (scalar) values.  Batches of up to 64
@@ -816,20 +856,21 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
   // lane's sequence from its three lengths, all loaded before any is used:
   // its tiles (every unit of the sequence has them; a sequence with queries
   // but no keys keeps one tile so that its rows are written, O = 0 and
-  // LSE = -inf) and its packed mask words (true lengths: the caller's layout)
+  // LSE = -inf), its packed mask words and its dense mask bytes (true
+  // lengths: the caller's layouts)
   struct Lens {
     int n, q0, ql, kv;
-    int64_t words;
+    int64_t words, bytes;
   };
   auto lens = [&](int b) -> Lens {
-    if (b >= p.batch) return Lens{0, 0, 0, 0, 0};
+    if (b >= p.batch) return Lens{0, 0, 0, 0, 0, 0};
     const int q0 = p.cu_seqlens_q[b], q1 = p.cu_seqlens_q[b + 1], kv_true = p.kv_lens[b];
     const int ql = max(0, min(q1 - q0, p.qs));
     const int kv = min(kv_true, p.max_kv);
     return Lens{ql <= 0 ? 0 : (kv > 0 ? (kv + 63) / 64 : 1), q0, ql, kv_true,
-                (int64_t)(q1 - q0) * ((kv_true + 63) / 64)};
+                (int64_t)(q1 - q0) * ((kv_true + 63) / 64), (int64_t)(q1 - q0) * kv_true};
   };
-  const Lens mine = one_chunk ? lens(lane) : Lens{0, 0, 0, 0, 0};
+  const Lens mine = one_chunk ? lens(lane) : Lens{0, 0, 0, 0, 0, 0};
   auto tiles_at = [&](int b) { return one_chunk ? (b < p.batch ? mine.n : 0) : lens(b).n; };
   // Smallest T in [1, max n_b] with sum_b nhb * ceil(n_b / T) <= G (T = max
   // n_b always fits: the host sizes G to at least the number of units).
@@ -850,16 +891,17 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
   const int T = __builtin_amdgcn_readfirstlane(lo_t);
   // the sequence whose units hold workgroup wg: prefix sums of nhb * k_b
   int base = 0;
-  int64_t mbase = 0;
-  Piece r{-1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  int64_t mbase = 0, dbase = 0;
+  Piece r{-1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   for (int c0 = 0; c0 < p.batch; c0 += 64) {
     const int b = c0 + lane;
-    const Lens ln = one_chunk ? (b < p.batch ? mine : Lens{0, 0, 0, 0, 0}) : lens(b);
+    const Lens ln = one_chunk ? (b < p.batch ? mine : Lens{0, 0, 0, 0, 0, 0}) : lens(b);
     const int n = ln.n;
-    const int64_t me = ln.words;
+    const int64_t me = ln.words, de = ln.bytes;
     const int wgs = p.nhb * ((n + T - 1) / T);
     const int incl = wave_incl_scan(wgs, lane);
     const int64_t mincl = wave_incl_scan(me, lane);
+    const int64_t dincl = wave_incl_scan(de, lane);
     if (r.b < 0) {
       const uint64_t hit = __ballot(b < p.batch && base + incl > wg);
       if (hit) {
@@ -872,6 +914,7 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
         r.hb = off / r.npieces;
         r.k = off - r.hb * r.npieces;
         r.moff = mbase + __shfl(mincl - me, l, 64);
+        r.doff = dbase + __shfl(dincl - de, l, 64);
         r.q0 = __shfl(ln.q0, l, 64);
         r.q_len = __shfl(ln.ql, l, 64);
         r.kv_len = __shfl(ln.kv, l, 64);
@@ -879,6 +922,7 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
     }
     base += __shfl(incl, 63, 64);
     mbase += __shfl(mincl, 63, 64);
+    dbase += __shfl(dincl, 63, 64);
   }
   r.b = __builtin_amdgcn_readfirstlane(r.b);
   r.n = __builtin_amdgcn_readfirstlane(r.n);
@@ -886,6 +930,7 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
   r.hb = __builtin_amdgcn_readfirstlane(r.hb);
   r.k = __builtin_amdgcn_readfirstlane(r.k);
   r.moff = uniform64(r.moff);
+  r.doff = uniform64(r.doff);
   r.q0 = __builtin_amdgcn_readfirstlane(r.q0);
   r.q_len = __builtin_amdgcn_readfirstlane(r.q_len);
   r.kv_len = __builtin_amdgcn_readfirstlane(r.kv_len);
@@ -904,6 +949,7 @@ __device__ __forceinline__ Piece uniform_piece(const Piece &x) {
   r.k = __builtin_amdgcn_readfirstlane(x.k);
   r.npieces = __builtin_amdgcn_readfirstlane(x.npieces);
   r.moff = uniform64(x.moff);
+  r.doff = uniform64(x.doff);
   r.q0 = __builtin_amdgcn_readfirstlane(x.q0);
   r.q_len = __builtin_amdgcn_readfirstlane(x.q_len);
   r.kv_len = __builtin_amdgcn_readfirstlane(x.kv_len);
@@ -966,7 +1012,16 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
   }
   const int b = pc.b, hb = pc.hb, kt0 = pc.kt0, kt1 = pc.kt1;
   const bool complete = pc.npieces == 1;
-  const int64_t moff = pc.moff;
+  const int kv_true = pc.kv_len;
+  const int kv = min(kv_true, p.max_kv);
+  // The words' layout: the caller's packed rows (the sequence's first word,
+  // ceil(kv_len / 64) per row), or for dense rows, which the workgroup turns
+  // into words itself, a fixed one (sequence b at b * max_q * W, W words per
+  // row, W = ceil(max_kv / 64)) that the workspace always holds, whatever
+  // the device lengths.
+  const int64_t wmax = (p.max_kv + 63) / 64;
+  const int64_t moff = p.dense ? (int64_t)b * p.qs * wmax : pc.moff;
+  const int nwords = p.dense ? (int)wmax : (kv_true + 63) / 64;
 
   const dma::LaneOffsets<D> lo(lane);
   const uint32_t lds0 = dma::lds_addr(lds);
@@ -984,9 +1039,6 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
                                            : CutUnit{-1, 0, 0, 0, 0, 0, 0, 0};
     if (pc.k == 0) unit_slot[b * p.nhb + hb] = wg;
   }
-  const int kv_true = pc.kv_len;
-  const int kv = min(kv_true, p.max_kv);
-  const int nwords = (kv_true + 63) / 64;
   const int hh = min(r / p.qs, p.gh - 1), t = r % p.qs;
   const bool row_ok = r / p.qs < p.gh && t < q_len;
   const int h = hb * p.gh + hh;
@@ -1012,8 +1064,9 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
     // Page ids of tile kt0 + j (scalar loads, read a step before their
     // gathers: next to the gathers' inline asm each would be waited for)
     auto pages = [&](int j) { return KV::pages_uniform(pt, p.page_shift, kt0 + j, kv, wave); };
-    // Tile kt0 + j into stage j % 4: K, V and one half of 64 rows' words.
-    auto issue = [&](int j, const typename KV::Pages &pg) {
+    // Tile kt0 + j into stage j % 4: K and V, then one half of 64 rows'
+    // words.
+    auto issue_kv = [&](int j, const typename KV::Pages &pg) {
       const int kt = kt0 + j;
       const uint32_t st = lds0 + (uint32_t)(j & 3) * PS::BYTES;
       if (kt * 64 + 64 <= kv) {
@@ -1034,10 +1087,16 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
         dma::issue_mat_fast<D, NW, dma::SwzV<D>, true>(vbase, pg, lgv, p.page_shift, page_bytes, slot_bytes, kt, kv,
                                                        st + 2u * dma::Stage<D>::V_OFF, wave, lane);
       }
-      const int64_t idx = wrow + kt;
+    };
+    auto issue_words = [&](int j) {
+      const int64_t idx = wrow + kt0 + j;
       const uint64_t *src = rd_ok && idx < p.mask_numel ? mask64 + idx : mask64;
-      lds_load4((const uint32_t *)src + (wave >> 2),
-                st + ((wave >> 2) ? PS::WHI : PS::WLO) + 256u * (uint32_t)(wave & 3));
+      lds_load4((const uint32_t *)src + (wave >> 2), lds0 + (uint32_t)(j & 3) * PS::BYTES +
+                                                         ((wave >> 2) ? PS::WHI : PS::WLO) + 256u * (uint32_t)(wave & 3));
+    };
+    auto issue = [&](int j, const typename KV::Pages &pg) {
+      issue_kv(j, pg);
+      issue_words(j);
     };
     // This lane's row word of tile kt0 + j (after the barrier that publishes
     // its stage); rows outside the unit or past mask_numel read 0.
@@ -1052,13 +1111,40 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
     if (nt > 1) pg1 = pages(1);
     if (nt > 2) pg2 = pages(2);
     if (nt > 3) pgn = pages(3);
-    issue(0, pg0);
-    if (nt > 1) issue(1, pg1);
-    if (nt > 2) {
-      issue(2, pg2);
-      wait_vmem_n<N_TILE>();   // tiles 0 and 1 have landed
-    } else {
+    if (p.dense) {
+      // Dense rows: with K and V of the first three tiles in flight, the
+      // workgroup writes the words of the rows and tiles it reads (its own
+      // piece's; the pieces of the sequence's other head blocks write the
+      // same values).  The stores are waited for and the barrier makes them
+      // visible to every wave's word gathers.  Bytes at or past dense_numel
+      // read as 0.
+      issue_kv(0, pg0);
+      if (nt > 1) issue_kv(1, pg1);
+      if (nt > 2) issue_kv(2, pg2);
+      const uint8_t *d8 = (const uint8_t *)p.dense;
+      uint64_t *wout = (uint64_t *)p.mask;
+      for (int i = tid; i < q_len * nt; i += kPipeWaves * 64) {
+        const int t = i / nt, kt = kt0 + i % nt;
+        const int nb = min(64, kv_true - 64 * kt);
+        if (nb > 0)
+          wout[moff + (int64_t)t * nwords + kt] =
+              dense_word(d8, p.dense_numel, pc.doff + (int64_t)t * kv_true + 64 * kt, nb);
+      }
       dma::wait_vmem();
+      __syncthreads();
+      issue_words(0);
+      if (nt > 1) issue_words(1);
+      if (nt > 2) issue_words(2);
+      dma::wait_vmem();   // tiles 0 .. 2 have landed
+    } else {
+      issue(0, pg0);
+      if (nt > 1) issue(1, pg1);
+      if (nt > 2) {
+        issue(2, pg2);
+        wait_vmem_n<N_TILE>();   // tiles 0 and 1 have landed
+      } else {
+        dma::wait_vmem();
+      }
     }
     __syncthreads();
     uint64_t word_cur = word_of(0);
@@ -1190,73 +1276,6 @@ __global__ __launch_bounds__(256) void verify_pipe_combine(VerifyParams p, const
   store4<OutT>((OutT *)p.out + (tok * p.hq + h) * D + 8 * c8 + 4, acc2[0] * inv, acc2[1] * inv, acc2[2] * inv,
                acc2[3] * inv);
   if (p.lse && c8 == 0) p.lse[tok * p.hq + h] = l_run > 0.f ? m_run + __logf(l_run) : neg_inf();
-}
-
-// Dense mask rows -> packed words (key j of a row -> bit j % 64 of word
-// j / 64), in the packed layout of the same sequences; bytes at or past
-// mask_numel read as 0.  One thread per (query row, word) of sequence
-// blockIdx.y; the sequence offsets of both layouts are prefix sums over the
-// earlier sequences.
-// Only rows below max_q are written (the kernel reads no others), and no
-// word at or past `cap`.
-__global__ __launch_bounds__(256) void dense_to_words(VerifyParams p, uint64_t *words, int64_t cap) {
-  const int b = blockIdx.y, lane = threadIdx.x & 63;
-  // this sequence's lengths and the earlier sequences', 64 per pass, one per
-  // lane: independent loads, then a wave sum (a serial walk would wait for
-  // each in turn)
-  const int qb0 = p.cu_seqlens_q[b], qb1 = p.cu_seqlens_q[b + 1], kv = p.kv_lens[b];
-  int64_t doff = 0, woff = 0;
-  for (int c0 = 0; c0 < b; c0 += 64) {
-    const int i = c0 + lane;
-    int64_t dn = 0, wn = 0;
-    if (i < b) {
-      const int64_t ql = p.cu_seqlens_q[i + 1] - p.cu_seqlens_q[i], kv = p.kv_lens[i];
-      dn = ql * kv;
-      wn = ql * ((kv + 63) / 64);
-    }
-    doff += __shfl(wave_incl_scan(dn, lane), 63, 64);
-    woff += __shfl(wave_incl_scan(wn, lane), 63, 64);
-  }
-  const int q_len = max(0, min(qb1 - qb0, p.qs));   // seq_q_len
-  const int nw = (kv + 63) / 64;
-  const uint8_t *m8 = (const uint8_t *)p.mask;
-  // 32-bit item indices (words at or past cap, the only ones such a bound
-  // could drop, are never written)
-  const int items = (int)min((int64_t)q_len * nw, (int64_t)INT32_MAX);
-  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < items; idx += gridDim.x * blockDim.x) {
-    const int t = idx / nw, w = idx - t * nw;
-    const int64_t base = doff + (int64_t)t * kv + 64 * w;
-    const int nb = min(64, kv - 64 * w);
-    uint64_t bits = 0;
-    // Rows start at any byte (their stride is kv_len bytes): the 64 bytes
-    // are read as 17 dword-aligned dwords and shifted into place with
-    // v_alignbyte, so every load is aligned whatever the row's start.  The
-    // 17th dword must lie inside the mask.  A row's last word reads the same
-    // 64 bytes (those past the row belong to the next row, or the next
-    // sequence, and are masked off) rather than one byte at a time.
-    const int64_t a4 = base & ~(int64_t)3;
-    if (a4 + 68 <= p.mask_numel) {
-      const uint32_t sh = (uint32_t)(base & 3);
-      const u32x4a4 *w4 = (const u32x4a4 *)(m8 + a4);
-      uint32_t dw[17];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4a4 v = w4[q];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dw[4 * q + e] = v[e];
-      }
-      dw[16] = ((const uint32_t *)(m8 + a4))[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        bits |= (uint64_t)nonzero_bytes4(__builtin_amdgcn_alignbyte(dw[i + 1], dw[i], sh)) << (4 * i);
-      if (nb < 64) bits &= (1ull << nb) - 1ull;
-    } else {
-      // the end of the mask buffer only: byte by byte
-      for (int j = 0; j < nb; ++j)
-        if (base + j < p.mask_numel && m8[base + j] != 0) bits |= 1ull << j;
-    }
-    if (woff + idx < cap) words[woff + idx] = bits;
-  }
 }
 
 // Launches kern over the (split, head group, sequence) grid with nw waves
@@ -1416,17 +1435,15 @@ ma_status run_pipe(const VerifyArgs &a, VerifyParams prm, const PipeShape &ps) {
   CutUnit *cuts = (CutUnit *)(ws + w.cuts);
   int32_t *unit_slot = (int32_t *)(ws + w.units);
   hipError_t e = hipSuccess;
+  prm.dense = nullptr;
+  prm.dense_numel = 0;
   if (prm.mode == kDense) {
-    // the dense rows become packed words first; the main kernel reads words
-    uint64_t *words = (uint64_t *)(ws + w.words);
-    const int64_t cap = (int64_t)a.batch * a.max_q * ((a.max_kv + 63) / 64);
-    const int64_t items = (int64_t)a.max_q * ((a.max_kv + 63) / 64);
-    const int chunks = (int)((items + 255) / 256 < 64 ? (items + 255) / 256 : 64);
-    hipLaunchKernelGGL(dense_to_words, dim3(chunks, a.batch), dim3(256), 0, s, prm, words, cap);
-    e = hipGetLastError();
-    if (e != hipSuccess) return set_error(MA_ERR_HIP, "mask conversion launch: %s", hipGetErrorString(e));
-    prm.mask = words;
-    prm.mask_numel = cap;
+    // the main kernel turns the dense rows it reads into packed words in the
+    // workspace and reads those (words at or past cap are never written)
+    prm.dense = prm.mask;
+    prm.dense_numel = prm.mask_numel;
+    prm.mask = ws + w.words;
+    prm.mask_numel = (int64_t)a.batch * a.max_q * ((a.max_kv + 63) / 64);
     prm.mode = kPacked;
   }
   const size_t lds = (size_t)kPipeStages * PipeStage<D>::BYTES;
