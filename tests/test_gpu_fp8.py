@@ -49,6 +49,8 @@ def _check(w, wd, name, out, lse, heads=None, rows=None):
             continue
         q0, ql, kl = int(wd.cu_seqlens_q[b]), int(wd.q_lens[b]), int(wd.kv_lens[b])
         rs = np.arange(ql) if rows is None else np.asarray(rows[b])
+        if rs.size == 0:
+            continue   # a sequence without queries
         mk = masks(b)
         for h in (range(wd.hq) if heads is None else heads):
             k = OA.gather_paged(wd.k_cache, wd.page_table[b], kl, h // group)

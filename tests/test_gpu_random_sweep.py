@@ -1,8 +1,9 @@
 """Seeded random sweep of the GPU paths against the oracle: ragged batches
 (sequences without queries or without keys included), GQA layouts, head
 sizes, page sizes, tile heights and every mask input, drawn from fixed seeds
-so that corners the hand-written cases miss get a chance to show.  Each case
-prints its parameters before it runs."""
+so that corners the hand-written cases miss get a chance to show: prefill,
+its backward and its fp8 form, tree verify and decode.  Each case prints its
+parameters before it runs."""
 
 import numpy as np
 import pytest
@@ -10,7 +11,10 @@ import torch
 
 import masked_flash_attention_mask_amd as ma
 import workloads as W
-from helpers import TOL_BF16, device_inputs, lse_err, max_abs_err, oracle, repage, run_prefill
+from helpers import (TOL_BF16, TOL_GRAD, compile_plan, device_inputs, fp8_dequantized, grad_err, lse_err, max_abs_err,
+                     oracle, oracle_masks, repage, run_prefill)
+from oracle import backward as OB
+from test_gpu_fp8 import _check as fp8_check, _dev8, _run as fp8_run
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +54,7 @@ def _bsr(rng, q_lens, kv_lens, br, bc):
     return np.array(indptr, np.int32), np.array(indices, np.int32)
 
 
-def _prefill_case(seed):
+def _prefill_case(seed, min_window=1):
     rng = np.random.default_rng(1000 + seed)
     b = int(rng.integers(1, 5))
     q_lens = [int(x) for x in rng.integers(0, 260, b)]
@@ -66,7 +70,7 @@ def _prefill_case(seed):
     if kind == "causal":
         mi = W.MaskInput("causal")
     elif kind == "window":
-        mi = W.MaskInput("window", window=int(rng.integers(1, 300)))
+        mi = W.MaskInput("window", window=int(rng.integers(min_window, 300)))
     elif kind == "prefix":
         mi = W.MaskInput("prefix_lm", prefix_len=np.array([int(rng.integers(0, k + 1)) for k in kv_lens], np.int32))
     elif kind == "ranges":
@@ -76,7 +80,7 @@ def _prefill_case(seed):
         mi = W.MaskInput("block_sparse", bsr=(br, bc) + _bsr(rng, q_lens, kv_lens, br, bc))
     else:
         rows = [rng.random((q, k)) < float(rng.uniform(0.05, 0.95)) for q, k in zip(q_lens, kv_lens)]
-        window = int(rng.integers(1, 200)) if kind == "dense_window" else 0
+        window = int(rng.integers(min_window, 200)) if kind == "dense_window" else 0
         if kind == "packed":
             mi = W.MaskInput("packed", data=np.concatenate(
                 [W.pack_rows(r).reshape(-1) for r in rows] + [np.zeros(0, np.uint64)]))
@@ -154,3 +158,87 @@ def test_verify_random_sweep(seed):
     err = max_abs_err(outs["packed"][0], ref_o)
     assert err <= TOL_BF16, (desc, err)
     assert lse_err(outs["packed"][1], ref_l) <= 1e-2, desc
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_backward_random_sweep(seed):
+    """The prefill sweep's shapes and masks through the backward, the
+    oracle's forward outputs in.  Windows of at least 2 keys: under a 1-key
+    window every row has a single visible key, its exact dS and dQ are zero,
+    and an error relative to the gradient's own scale means nothing."""
+    w, desc = _prefill_case(seed, min_window=2)
+    _say("backward sweep", desc)
+    do = W.upstream_grad(w, 7000 + seed)
+    dev = device_inputs(w)
+    dev["do"] = torch.from_numpy(do).cuda().to(torch.bfloat16).contiguous()
+    o, l = oracle(w, "m")
+    out = torch.from_numpy(o.astype(np.float32)).cuda().contiguous()
+    lse = torch.from_numpy(l.astype(np.float32)).cuda().contiguous()
+    plan = compile_plan(w, "m", desc["tile_q"])
+    dq, dk, dv = ma.attn_backward_masked(plan, dev["q"], dev["k"], dev["v"], dev["pt"], out, lse, dev["do"], w.scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = OB.attention_backward(w.q, w.k_cache, w.v_cache, w.page_table, w.cu_seqlens_q, w.kv_lens,
+                                       oracle_masks(w, "m"), w.scale, do)
+    used = np.zeros(w.k_cache.shape[:2], bool)
+    for b, kl in enumerate(w.kv_lens):
+        j = np.arange(int(kl))
+        used[w.page_table[b, j // w.page_size], j % w.page_size] = True
+    keep = used[..., None, None]
+    for g, r, what in ((dq, rq, "dq"), (torch.from_numpy(np.where(keep, dk.cpu().numpy(), 0.0)), rk, "dk"),
+                       (torch.from_numpy(np.where(keep, dv.cpu().numpy(), 0.0)), rv, "dv")):
+        err = grad_err(g, r)
+        assert err <= TOL_GRAD, (desc, what, err)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_fp8_random_sweep(seed):
+    """The prefill sweep's shapes and masks with e4m3 inputs (pages of at
+    least 16 keys, 128-row tiles), within the derived e4m3 rounding bound."""
+    w, desc = _prefill_case(seed)
+    if w.page_size < 16:
+        w = repage(w, 16, 8000 + seed)
+        desc["page"] = 16
+    desc["tile_q"] = 128
+    _say("fp8 sweep", desc)
+    f8 = W.fp8_inputs(w)
+    out, lse = fp8_run(w, f8, _dev8(w, f8), "m")
+    fp8_check(w, fp8_dequantized(w, f8), "m", out, lse)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_decode_random_sweep(seed):
+    """The verify sweep's shapes (up to 64 queries per sequence) through
+    decode under causal, window, PrefixLM, dense and packed rows."""
+    w, desc = _verify_case(seed)
+    rng = np.random.default_rng(9000 + seed)
+    kind = ["causal", "window", "prefix", "dense", "packed"][seed % 5]
+    ql, kl = [int(x) for x in w.q_lens], [int(x) for x in w.kv_lens]
+    kw = {}
+    if kind == "causal":
+        mi = W.MaskInput("causal")
+    elif kind == "window":
+        mi = W.MaskInput("window", window=int(rng.integers(1, 400)))
+        kw["window"] = mi.window
+    elif kind == "prefix":
+        mi = W.MaskInput("prefix_lm", prefix_len=np.array([int(rng.integers(0, k + 1)) for k in kl], np.int32))
+        kw["prefix_len"] = torch.from_numpy(mi.prefix_len).cuda()
+    else:
+        rows = [rng.random((q, k)) < 0.4 for q, k in zip(ql, kl)]
+        if kind == "dense":
+            mi = W.MaskInput("dense", data=np.concatenate([r.astype(np.uint8).reshape(-1) for r in rows]))
+            kw["mask"] = torch.from_numpy(mi.data).cuda()
+        else:
+            mi = W.MaskInput("packed", data=np.concatenate(
+                [W.pack_rows(r).reshape(-1) for r in rows] + [np.zeros(0, np.uint64)]))
+            kw["mask"] = torch.from_numpy(np.ascontiguousarray(mi.data.view(np.int64))).cuda()
+    w.masks["m"] = mi
+    desc["kind"] = kind
+    _say("decode sweep", desc)
+    dev = device_inputs(w)
+    out, lse = ma.attn_decode(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], desc["max_q"],
+                              int(w.kv_lens.max()), w.scale, mask_kind=mi.kind, **kw)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle(w, "m")
+    err = max_abs_err(out, ref_o)
+    assert err <= TOL_BF16, (desc, err)
+    assert lse_err(lse, ref_l) <= 1e-2, desc
