@@ -1406,7 +1406,8 @@ PipeShape pipe_shape(int batch, int hq, int hkv, int d, int max_q, int max_kv, i
 }
 
 // Workspace of a balanced launch: one partial (O, LSE) slot of 256 rows per
-// workgroup, and room for a dense mask converted to packed words.
+// workgroup, the cut records and first-piece slots, and room for the words
+// the kernel makes from dense rows ([batch][max_q][ceil(max_kv / 64)]).
 struct PipeWs {
   size_t o, lse, cuts, units, words, total;
 };
