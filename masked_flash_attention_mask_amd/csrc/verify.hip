@@ -872,12 +872,24 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
   };
   const Lens mine = one_chunk ? lens(lane) : Lens{0, 0, 0, 0, 0, 0};
   auto tiles_at = [&](int b) { return one_chunk ? (b < p.batch ? mine.n : 0) : lens(b).n; };
-  // Smallest T in [1, max n_b] with sum_b nhb * ceil(n_b / T) <= G (T = max
-  // n_b always fits: the host sizes G to at least the number of units).
-  int maxn = 0;
-  for (int c0 = 0; c0 < p.batch; c0 += 64) maxn = max(maxn, tiles_at(c0 + lane));
+  // Smallest T in [1, max n_b] with need(T) = sum_b nhb * ceil(n_b / T) <= G
+  // (T = max n_b always fits: the host sizes G to at least the number of
+  // units).  With S = sum_b nhb * n_b and U units holding tiles, need(T) >=
+  // S / T exceeds G below ceil(S / G), and need(T) <= S / T + U is at most G
+  // from ceil(S / (G - U)) on, so the search starts in that bracket.
+  int maxn = 0, tot = 0, used = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += 64) {
+    const int n = tiles_at(c0 + lane);
+    maxn = max(maxn, n);
+    tot += n;
+    used += n > 0;
+  }
   maxn = wave_max(maxn);
-  int lo_t = 1, hi_t = max(maxn, 1);
+  tot = wave_sum(tot) * p.nhb;
+  used = wave_sum(used) * p.nhb;
+  int hi_t = max(maxn, 1);
+  if (p.grid > used) hi_t = min(hi_t, max(1, (tot + (p.grid - used) - 1) / (p.grid - used)));
+  int lo_t = max(1, min(hi_t, (tot + p.grid - 1) / p.grid));
   while (lo_t < hi_t) {
     const int mid = (lo_t + hi_t) >> 1;
     int need = 0;
@@ -956,11 +968,10 @@ __device__ __forceinline__ Piece uniform_piece(const Piece &x) {
   return r;
 }
 
-// What a workgroup leaves for the merge: the unit whose first piece it ran
-// when that unit has more pieces (b < 0 otherwise).  Every workgroup writes
-// its record on every launch.
-struct CutUnit {
-  int32_t b, hb, npieces, q0, q_len, pad0, pad1, pad2;
+// What a unit's first piece leaves for the merge: its workgroup (the pieces
+// are workgroups slot, slot + 1, ...) and how many pieces the unit has.
+struct UnitRec {
+  int32_t slot, npieces;
 };
 
 // Workgroups are dispatched to the 8 XCDs round-robin.  When the grid is a
@@ -985,8 +996,7 @@ struct PipeStage {
 };
 
 template <int D, typename OutT>
-__global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyParams p, CutUnit *cuts,
-                                                                          int32_t *unit_slot) {
+__global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyParams p, UnitRec *units) {
   extern __shared__ __align__(16) uint16_t lds[];
   constexpr int NW = kPipeWaves;
   using KV = dma::KvDma<D, NW>;
@@ -1006,10 +1016,7 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
   }
   __syncthreads();
   const Piece pc = uniform_piece(piece_lds);
-  if (pc.b < 0) {
-    if (tid == 0) cuts[wg] = CutUnit{-1, 0, 0, 0, 0, 0, 0, 0};
-    return;
-  }
+  if (pc.b < 0) return;
   const int b = pc.b, hb = pc.hb, kt0 = pc.kt0, kt1 = pc.kt1;
   const bool complete = pc.npieces == 1;
   const int kv_true = pc.kv_len;
@@ -1034,11 +1041,7 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
   const uint64_t *mask64 = (const uint64_t *)p.mask;
 
   const int q0 = pc.q0, q_len = pc.q_len;
-  if (tid == 0) {
-    cuts[wg] = pc.k == 0 && pc.npieces > 1 ? CutUnit{b, hb, pc.npieces, q0, q_len, 0, 0, 0}
-                                           : CutUnit{-1, 0, 0, 0, 0, 0, 0, 0};
-    if (pc.k == 0) unit_slot[b * p.nhb + hb] = wg;
-  }
+  if (tid == 0 && pc.k == 0) units[b * p.nhb + hb] = UnitRec{wg, pc.npieces};
   const int hh = min(r / p.qs, p.gh - 1), t = r % p.qs;
   const bool row_ok = r / p.qs < p.gh && t < q_len;
   const int h = hb * p.gh + hh;
@@ -1206,14 +1209,15 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
 }
 
 // Merges the pieces of a cut unit: block (u, c) takes unit u's first piece
-// i from unit_slot[u] and 256 (row, 8 columns) items of the unit's 256 x D
+// i from its record and 256 (row, 8 columns) items of the unit's 256 x D
 // outputs (item = c * 256 + thread, D / 8 items per row) and merges the
 // pieces i, i + 1, ... in order:
 // O = sum_s exp(LSE_s - M) O_s / sum_s exp(LSE_s - M), LSE = M + ln(sum).
-// unit_slot keeps entries of earlier launches for units that have no piece
-// in this one; the cut record of slot i, which every workgroup rewrites on
-// every launch, tells a current entry from a stale one (and is b < 0 when
-// the unit's single piece wrote its output itself).
+// The records keep entries of earlier launches for units that have no piece
+// in this one.  A unit has pieces exactly when its sequence has query rows,
+// and then its first piece rewrote the record in this launch, so the
+// sequence's row count, loaded beside the record, tells a current entry from
+// a stale one.  A unit of one piece wrote its output itself.
 // Each pass issues the loads of kMergeBatch pieces before using them.
 constexpr int kMergeBatch = 8;
 
@@ -1226,14 +1230,13 @@ __device__ __forceinline__ f32x4 load4f(const uint16_t *src) {
 }
 
 template <int D, typename OutT>
-__global__ __launch_bounds__(256) void verify_pipe_combine(VerifyParams p, const CutUnit *cuts,
-                                                           const int32_t *unit_slot) {
+__global__ __launch_bounds__(256) void verify_pipe_combine(VerifyParams p, const UnitRec *units) {
   const int u = blockIdx.x;
-  const int wg = unit_slot[u];
-  if (wg < 0 || wg >= p.grid) return;
-  const CutUnit cu = cuts[wg];
-  if (cu.b != u / p.nhb || cu.hb != u % p.nhb) return;
-  const int hb = cu.hb, np = cu.npieces, q0 = cu.q0, q_len = cu.q_len;
+  const int b = u / p.nhb, hb = u % p.nhb;
+  const UnitRec rec = units[u];
+  const int q0 = p.cu_seqlens_q[b], q_len = seq_q_len(p, b, q0);
+  const int wg = rec.slot, np = rec.npieces;
+  if (q_len == 0 || np < 2 || wg < 0 || wg > p.grid - np) return;
   const int item = blockIdx.y * 256 + threadIdx.x;
   const int r = item / (D / 8), c8 = item % (D / 8);
   const int t = r % p.qs;
@@ -1406,22 +1409,21 @@ PipeShape pipe_shape(int batch, int hq, int hkv, int d, int max_q, int max_kv, i
 }
 
 // Workspace of a balanced launch: one partial (O, LSE) slot of 256 rows per
-// workgroup, the cut records and first-piece slots, and room for the words
-// the kernel makes from dense rows ([batch][max_q][ceil(max_kv / 64)]).
+// workgroup, one record per unit, and room for the words the kernel makes
+// from dense rows ([batch][max_q][ceil(max_kv / 64)]).
 struct PipeWs {
-  size_t o, lse, cuts, units, words, total;
+  size_t o, lse, units, words, total;
 };
 
 PipeWs pipe_ws(const PipeShape &s, int32_t batch, int32_t max_q, int32_t max_kv, int32_t d) {
-  PipeWs w{0, 0, 0, 0, 0, 0};
+  PipeWs w{0, 0, 0, 0, 0};
   if (!s.ok) return w;
   const size_t slots = (size_t)s.grid;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   w.o = 0;
   w.lse = up(slots * kPipeRows * d * sizeof(float));
-  w.cuts = w.lse + up(slots * kPipeRows * sizeof(float));
-  w.units = w.cuts + up(slots * sizeof(CutUnit));
-  w.words = w.units + up((size_t)batch * s.nhb * sizeof(int32_t));
+  w.units = w.lse + up(slots * kPipeRows * sizeof(float));
+  w.words = w.units + up((size_t)batch * s.nhb * sizeof(UnitRec));
   w.total = w.words + (size_t)batch * max_q * ((max_kv + 63) / 64) * sizeof(uint64_t);
   return w;
 }
@@ -1433,8 +1435,7 @@ ma_status run_pipe(const VerifyArgs &a, VerifyParams prm, const PipeShape &ps) {
   char *ws = (char *)a.workspace;
   prm.ws_o = (float *)(ws + w.o);
   prm.ws_lse = (float *)(ws + w.lse);
-  CutUnit *cuts = (CutUnit *)(ws + w.cuts);
-  int32_t *unit_slot = (int32_t *)(ws + w.units);
+  UnitRec *units = (UnitRec *)(ws + w.units);
   hipError_t e = hipSuccess;
   prm.dense = nullptr;
   prm.dense_numel = 0;
@@ -1453,11 +1454,11 @@ ma_status run_pipe(const VerifyArgs &a, VerifyParams prm, const PipeShape &ps) {
     e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
   }
-  hipLaunchKernelGGL(kern, dim3(ps.grid), dim3(kPipeWaves * 64), lds, s, prm, cuts, unit_slot);
+  hipLaunchKernelGGL(kern, dim3(ps.grid), dim3(kPipeWaves * 64), lds, s, prm, units);
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify launch: %s", hipGetErrorString(e));
   hipLaunchKernelGGL((verify_pipe_combine<D, OutT>), dim3(a.batch * ps.nhb, kPipeRows * (D / 8) / 256), dim3(256), 0,
-                     s, prm, (const CutUnit *)cuts, (const int32_t *)unit_slot);
+                     s, prm, (const UnitRec *)units);
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(MA_ERR_HIP, "verify combine launch: %s", hipGetErrorString(e));
   return MA_OK;
