@@ -382,7 +382,11 @@ size_t attn_decode_workspace(int32_t batch, int32_t max_q, int32_t max_kv, int32
  * outside the buffers is read or written.  The query heads of a K/V head's GQA group and
  * their queries share each gathered K/V tile; long contexts are split over
  * workgroups and merged in a fixed order; a sliding window only walks the
- * tiles it can see.  A row that sees no key gets O = 0 and LSE = -inf.
+ * tiles it can see.  Under CAUSAL, PREFIX_LM, DENSE_BOOL and PACKED_U64, a
+ * launch whose rows per unit (GQA heads x max_q) exceed 128 at d <= 128 runs
+ * attn_verify_tree's balanced kernel, the positional kinds' row words
+ * computed from pos (outputs bit-identical to the same mask given as
+ * packed rows).  A row that sees no key gets O = 0 and LSE = -inf.
  * Requires in_dtype BF16 and d in {64, 128, 256}.  workspace: device, at
  * least attn_decode_workspace(...) bytes (NULL allowed when that is 0), owned
  * by the caller; its contents need no initialisation.  DENSE_BOOL /

@@ -846,6 +846,7 @@ struct Piece {
   int64_t moff;
   int q0, q_len, kv_len;   // the sequence's first query row, rows (seq_q_len), keys
   int64_t doff;            // the sequence's first byte in the dense layout
+  int plen;                // the sequence's prefix (prefix masks; 0 otherwise)
 };
 
 // Every lane returns the same (scalar) values.  Batches of up to 64
@@ -853,24 +854,26 @@ struct Piece {
 // loaded at once (one round trip); larger ones reread them per chunk.
 __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
   const bool one_chunk = p.batch <= 64;
-  // lane's sequence from its three lengths, all loaded before any is used:
-  // its tiles (every unit of the sequence has them; a sequence with queries
-  // but no keys keeps one tile so that its rows are written, O = 0 and
-  // LSE = -inf), its packed mask words and its dense mask bytes (true
-  // lengths: the caller's layouts)
+  // lane's sequence from its lengths (and its prefix under a prefix mask),
+  // all loaded before any is used: its tiles (every unit of the sequence has
+  // them; a sequence with queries but no keys keeps one tile so that its rows
+  // are written, O = 0 and LSE = -inf), its packed mask words and its dense
+  // mask bytes (true lengths: the caller's layouts)
   struct Lens {
     int n, q0, ql, kv;
     int64_t words, bytes;
+    int pl;
   };
   auto lens = [&](int b) -> Lens {
-    if (b >= p.batch) return Lens{0, 0, 0, 0, 0, 0};
+    if (b >= p.batch) return Lens{0, 0, 0, 0, 0, 0, 0};
     const int q0 = p.cu_seqlens_q[b], q1 = p.cu_seqlens_q[b + 1], kv_true = p.kv_lens[b];
+    const int pl = p.mode == kPrefix ? p.prefix_len[b] : 0;
     const int ql = max(0, min(q1 - q0, p.qs));
     const int kv = min(kv_true, p.max_kv);
     return Lens{ql <= 0 ? 0 : (kv > 0 ? (kv + 63) / 64 : 1), q0, ql, kv_true,
-                (int64_t)(q1 - q0) * ((kv_true + 63) / 64), (int64_t)(q1 - q0) * kv_true};
+                (int64_t)(q1 - q0) * ((kv_true + 63) / 64), (int64_t)(q1 - q0) * kv_true, pl};
   };
-  const Lens mine = one_chunk ? lens(lane) : Lens{0, 0, 0, 0, 0, 0};
+  const Lens mine = one_chunk ? lens(lane) : Lens{0, 0, 0, 0, 0, 0, 0};
   auto tiles_at = [&](int b) { return one_chunk ? (b < p.batch ? mine.n : 0) : lens(b).n; };
   // Smallest T in [1, max n_b] with need(T) = sum_b nhb * ceil(n_b / T) <= G
   // (T = max n_b always fits: the host sizes G to at least the number of
@@ -904,10 +907,10 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
   // the sequence whose units hold workgroup wg: prefix sums of nhb * k_b
   int base = 0;
   int64_t mbase = 0, dbase = 0;
-  Piece r{-1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  Piece r{-1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   for (int c0 = 0; c0 < p.batch; c0 += 64) {
     const int b = c0 + lane;
-    const Lens ln = one_chunk ? (b < p.batch ? mine : Lens{0, 0, 0, 0, 0, 0}) : lens(b);
+    const Lens ln = one_chunk ? (b < p.batch ? mine : Lens{0, 0, 0, 0, 0, 0, 0}) : lens(b);
     const int n = ln.n;
     const int64_t me = ln.words, de = ln.bytes;
     const int wgs = p.nhb * ((n + T - 1) / T);
@@ -930,6 +933,7 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
         r.q0 = __shfl(ln.q0, l, 64);
         r.q_len = __shfl(ln.ql, l, 64);
         r.kv_len = __shfl(ln.kv, l, 64);
+        r.plen = __shfl(ln.pl, l, 64);
       }
     }
     base += __shfl(incl, 63, 64);
@@ -946,6 +950,7 @@ __device__ Piece locate_piece(const VerifyParams &p, int wg, int lane) {
   r.q0 = __builtin_amdgcn_readfirstlane(r.q0);
   r.q_len = __builtin_amdgcn_readfirstlane(r.q_len);
   r.kv_len = __builtin_amdgcn_readfirstlane(r.kv_len);
+  r.plen = __builtin_amdgcn_readfirstlane(r.plen);
   r.kt0 = r.k * r.n / r.npieces;
   r.kt1 = (r.k + 1) * r.n / r.npieces;
   return r;
@@ -965,6 +970,7 @@ __device__ __forceinline__ Piece uniform_piece(const Piece &x) {
   r.q0 = __builtin_amdgcn_readfirstlane(x.q0);
   r.q_len = __builtin_amdgcn_readfirstlane(x.q_len);
   r.kv_len = __builtin_amdgcn_readfirstlane(x.kv_len);
+  r.plen = __builtin_amdgcn_readfirstlane(x.plen);
   return r;
 }
 
@@ -995,14 +1001,17 @@ struct PipeStage {
   static constexpr uint32_t BYTES = KV + 8 * kPipeRows;
 };
 
-template <int D, typename OutT>
+// POS: a mask given by position (causal, or causal after a per-sequence
+// prefix): each row's word is computed, not loaded, and a tile moves only K
+// and V.
+template <int D, typename OutT, bool POS>
 __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyParams p, UnitRec *units) {
   extern __shared__ __align__(16) uint16_t lds[];
   constexpr int NW = kPipeWaves;
   using KV = dma::KvDma<D, NW>;
   using PS = PipeStage<D>;
   constexpr int IPW = KV::IPW;
-  constexpr int N_TILE = 2 * IPW + 1;   // vector memory instructions per wave and tile
+  constexpr int N_TILE = 2 * IPW + (POS ? 0 : 1);   // vector memory instructions per wave and tile
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int wg = pipe_logical(blockIdx.x, p.grid);
@@ -1040,7 +1049,7 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
   const int rd = 64 * (wave & 3) + lane;    // the row whose word half this lane's DMA moves
   const uint64_t *mask64 = (const uint64_t *)p.mask;
 
-  const int q0 = pc.q0, q_len = pc.q_len;
+  const int q0 = pc.q0, q_len = pc.q_len, plen = pc.plen;
   if (tid == 0 && pc.k == 0) units[b * p.nhb + hb] = UnitRec{wg, pc.npieces};
   const int hh = min(r / p.qs, p.gh - 1), t = r % p.qs;
   const bool row_ok = r / p.qs < p.gh && t < q_len;
@@ -1092,6 +1101,7 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
       }
     };
     auto issue_words = [&](int j) {
+      if constexpr (POS) return;
       const int64_t idx = wrow + kt0 + j;
       const uint64_t *src = rd_ok && idx < p.mask_numel ? mask64 + idx : mask64;
       lds_load4((const uint32_t *)src + (wave >> 2), lds0 + (uint32_t)(j & 3) * PS::BYTES +
@@ -1104,6 +1114,11 @@ __global__ __launch_bounds__(kPipeWaves * 64, 1) void verify_pipe_kernel(VerifyP
     // This lane's row word of tile kt0 + j (after the barrier that publishes
     // its stage); rows outside the unit or past mask_numel read 0.
     auto word_of = [&](int j) -> uint64_t {
+      if constexpr (POS) {
+        // query t is key position kv - q_len + t of its sequence
+        const int pos = t + kv - q_len;
+        return row_ok ? interval_word(0, p.mode == kPrefix ? max(pos, plen - 1) : pos, kt0 + j) : 0ull;
+      }
       const uint32_t *w32 = (const uint32_t *)((const char *)lds + (uint32_t)(j & 3) * PS::BYTES);
       const uint32_t lo_w = w32[PS::WLO / 4 + r], hi_w = w32[PS::WHI / 4 + r];
       const bool ok = row_ok && lrow + kt0 + j < p.mask_numel;
@@ -1374,6 +1389,8 @@ size_t workspace_bytes(const Shape &sh, int32_t batch, int32_t max_q, int32_t hq
 }
 
 // Shape of a balanced tree-verify launch (verify_pipe_kernel): custom masks
+// (dense or packed rows) and the causal and prefix masks (computed per row;
+// a sliding window keeps the split kernels, whose walks start at the window)
 // over bf16 caches at d <= 128 whose pages hold a gather instruction's rows
 // (`pages_ok`), with GH query heads x max_q rows per unit filling more than
 // half of its eight waves (smaller row sets, e.g. decode, keep the split
@@ -1385,7 +1402,8 @@ struct PipeShape {
 
 PipeShape pipe_shape(int batch, int hq, int hkv, int d, int max_q, int max_kv, int mode, bool pages_ok, bool kv8) {
   PipeShape s{false, 1, 1, 1};
-  if ((mode != kDense && mode != kPacked) || kv8 || d > 128 || !pages_ok) return s;
+  if ((mode != kDense && mode != kPacked && mode != kCausal && mode != kPrefix) || kv8 || d > 128 || !pages_ok)
+    return s;
   const int group = hq / hkv;
   int gh = 1;
   for (int c = group; c >= 1; --c)
@@ -1449,7 +1467,8 @@ ma_status run_pipe(const VerifyArgs &a, VerifyParams prm, const PipeShape &ps) {
     prm.mode = kPacked;
   }
   const size_t lds = (size_t)kPipeStages * PipeStage<D>::BYTES;
-  auto kern = verify_pipe_kernel<D, OutT>;
+  const bool pos = prm.mode == kCausal || prm.mode == kPrefix;
+  auto kern = pos ? verify_pipe_kernel<D, OutT, true> : verify_pipe_kernel<D, OutT, false>;
   if (lds > 64 * 1024) {
     e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return set_error(MA_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));

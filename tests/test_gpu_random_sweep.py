@@ -158,6 +158,22 @@ def test_verify_random_sweep(seed):
     err = max_abs_err(outs["packed"][0], ref_o)
     assert err <= TOL_BF16, (desc, err)
     assert lse_err(outs["packed"][1], ref_l) <= 1e-2, desc
+    # the same rows under masks given by position (the tree-verify shapes take
+    # the balanced kernel with computed words)
+    prefix = np.array([int(x) for x in np.random.default_rng(4500 + seed).integers(0, np.asarray(w.kv_lens) + 1)],
+                      dtype=np.int32)
+    w.masks["causal"] = W.MaskInput("causal")
+    w.masks["prefix"] = W.MaskInput("prefix_lm", prefix_len=prefix)
+    for name in ("causal", "prefix"):
+        mi = w.masks[name]
+        pl = torch.from_numpy(prefix).cuda() if mi.kind == "prefix_lm" else None
+        o, l = ma.attn_decode(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], desc["max_q"],
+                              int(w.kv_lens.max()), w.scale, mask_kind=mi.kind, prefix_len=pl)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle(w, name)
+        err = max_abs_err(o, ref_o)
+        assert err <= TOL_BF16, (desc, name, err)
+        assert lse_err(l, ref_l) <= 1e-2, (desc, name)
 
 
 @pytest.mark.parametrize("seed", range(16))

@@ -11,7 +11,7 @@ import torch
 
 import masked_flash_attention_mask_amd as ma
 import workloads as W
-from helpers import TOL_BF16, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle, repage
+from helpers import OM, TOL_BF16, bf16_out_err, device_inputs, lse_err, max_abs_err, oracle, repage
 
 pytestmark = pytest.mark.gpu
 
@@ -25,11 +25,14 @@ def _workload(seed, q_lens, kv_lens, hq, hkv, d, p_visible=0.6):
     rows = []
     for ql, kl in zip(q_lens, kv_lens):
         m = np.zeros((ql, kl), dtype=bool)
-        ctx = kl - ql
-        m[:, :ctx] = True
-        if ql:
-            m[:, ctx:] = rng.random((ql, ql)) < p_visible
-            m[np.arange(ql), ctx + np.arange(ql)] = True
+        ctx = kl - ql          # negative: more queries than keys
+        lo = max(ctx, 0)
+        m[:, :lo] = True
+        if ql and kl:
+            m[:, lo:] = rng.random((ql, kl - lo)) < p_visible
+            t = np.arange(ql)
+            own = ctx + t >= 0
+            m[t[own], ctx + t[own]] = True
         rows.append(m)
     w.masks["dense"] = W.gen.MaskInput("dense", data=np.concatenate([r.astype(np.uint8).reshape(-1) for r in rows]))
     w.masks["packed"] = W.gen.MaskInput("packed", data=np.concatenate(
@@ -80,3 +83,43 @@ def test_balanced_verify_matches_oracle(case):
     ob, _ = _run(w, dev, "packed", max_q, out_dtype=torch.bfloat16)
     assert bf16_out_err(ob, ref_o) <= TOL_BF16
     assert (ob.float() - o_p).abs().max().item() <= 2 ** -7 * max(1.0, o_p.abs().max().item())
+
+
+POS_CASES = CASES + [
+    (5, [64, 64, 40], [30, 500, 40], 32, 8, 128, 16),               # more queries than keys: rows see nothing
+]
+
+
+@pytest.mark.parametrize("case", POS_CASES, ids=[f"seed{c[0]}" for c in POS_CASES])
+def test_balanced_positional_masks(case):
+    """Causal and PrefixLM rows take the balanced kernel with each row's word
+    computed from its position: bit-identical to the same masks given as
+    packed rows, and within the bf16 bound of the oracle."""
+    seed, q_lens, kv_lens, hq, hkv, d, page = case
+    if kv_lens is None:
+        kv_lens = list(W.rng_for(100 + seed).integers(40, 400, size=len(q_lens)))
+    print("[case] balanced positional", seed, hq, hkv, d, page, flush=True)
+    w = _workload(seed, q_lens, kv_lens, hq, hkv, d)
+    if page != w.page_size:
+        w = repage(w, page, 300 + seed)
+    dev = device_inputs(w)
+    max_q, max_kv = max(max(q_lens), 1), int(max(kv_lens))
+    prefix = np.array([int(W.rng_for(700 + seed).integers(0, k + 1)) for k in kv_lens], dtype=np.int32)
+    w.masks["causal"] = W.gen.MaskInput("causal")
+    w.masks["prefix"] = W.gen.MaskInput("prefix_lm", prefix_len=prefix)
+    for name, build in (("causal", lambda q, k, b: OM.causal(q, k)),
+                        ("prefix", lambda q, k, b: OM.prefix_lm(q, k, int(prefix[b])))):
+        mi = w.masks[name]
+        pl = torch.from_numpy(prefix).cuda() if mi.kind == "prefix_lm" else None
+        o_pos, l_pos = ma.attn_decode(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], max_q, max_kv,
+                                      w.scale, mask_kind=mi.kind, prefix_len=pl, out_dtype=torch.float32)
+        rows = [build(int(q), int(k), b) for b, (q, k) in enumerate(zip(q_lens, kv_lens))]
+        packed = np.concatenate([W.pack_rows(r).reshape(-1) for r in rows])
+        mask = torch.from_numpy(np.ascontiguousarray(packed.view(np.int64))).cuda()
+        o_pk, l_pk = ma.attn_verify_tree(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], mask, "packed",
+                                         max_q, max_kv, w.scale, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(o_pos, o_pk) and torch.equal(l_pos, l_pk), name
+        ref_o, ref_l = oracle(w, name)
+        assert max_abs_err(o_pos, ref_o) <= TOL_BF16, name
+        assert lse_err(l_pos, ref_l) <= 1e-2, name
