@@ -11,17 +11,19 @@
 //    q-tile, lane l tile l of the chunk; a lane loads its tile's 32 words (a
 //    row's 64 words are one 512-byte load across the wave) and reduces them
 //    in registers; the four row groups combine through LDS flags.
-//  * dense rows (classify_kernel): lanes 2i and 2i + 1 read the two 32-byte
-//    halves of wave row i's 64 bytes of a tile, turn them into bits (SWAR),
-//    and two shuffles give row i's word to lane i (eight tiles in flight per
-//    wave); the words go through LDS, where each wave scans a quarter of the
-//    rows for "some bit set" and "every in-bounds row full".
+//  * dense rows (classify_kernel): a wave reads its rows one after another,
+//    each row's chunk (up to 4 KB) in 1 KB loads along the row, turns each
+//    lane's 16 bytes into bits (SWAR), and the four lanes of a tile put its
+//    word together (four rows in flight per wave); the words go through
+//    LDS, where each wave scans a quarter of the rows for "some bit set" and
+//    "every in-bounds row full".
 // Pass 2 (compact_kernel): one wave per q-tile row appends the row's non-SKIP
 // tiles, in ascending k order, to its entry list.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstring>
+#include <type_traits>
 
 #include "internal.h"
 #include "kernels_common.h"
@@ -31,7 +33,7 @@ namespace {
 
 constexpr int kTiles = 64;     // k-tiles per chunk
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kDenseBatch = 8; // dense tiles in flight per wave
+constexpr int kDenseRows = 4;  // dense rows in flight per wave (4 KB each)
 
 struct ClassifyParams {
   const SeqInfo *seqs;
@@ -63,30 +65,6 @@ __device__ __forceinline__ uint64_t band_bits(int row, int c, int q_len, int kv,
 __device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t x) {
   const uint32_t t = ((((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) >> 7) & 0x01010101u;
   return ((t * 0x00204081u) >> 21) & 0xFu;
-}
-
-// 32 bits for the bytes [base, base + nb) of a dense mask (nb <= 32).  A
-// short run (a row's last) reads the same 32 bytes when they lie inside the
-// mask and masks off those past the row; only at the end of the mask are
-// bytes read one by one.
-__device__ __forceinline__ uint32_t dense_half(const uint8_t *m8, int64_t base, int nb, int64_t numel) {
-  uint32_t bits = 0;
-  if (nb <= 0) return 0;
-  if (base + 32 <= numel) {
-    dev::u32x4 v0, v1;
-    __builtin_memcpy(&v0, m8 + base, 16);
-    __builtin_memcpy(&v1, m8 + base + 16, 16);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      bits |= nonzero_bytes4(v0[c]) << (4 * c);
-      bits |= nonzero_bytes4(v1[c]) << (16 + 4 * c);
-    }
-    if (nb < 32) bits &= (1u << nb) - 1u;
-  } else {
-    for (int j = 0; j < nb; ++j)
-      if (base + j < numel && m8[base + j] != 0) bits |= 1u << j;
-  }
-  return bits;
 }
 
 // The sequence holding q-tile row r (aux row bases ascend): binary search.
@@ -147,56 +125,75 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p, ui
           wl[lane * ws + rg * 32 + i] = w[i] & inb & band_bits(row0 + i, c, sq.q_len, kv, p.window);
       }
     } else {
-      const int i = lane >> 1, half = lane & 1;
-      const int row = row0 + i;
-      const bool rv = row < sq.q_len;
-      const int64_t rbase = ax.moff + (int64_t)row * kv + 32 * half;
-      for (int ci0 = 0; ci0 < cn; ci0 += kDenseBatch) {
-        // Interior halves: two 16-byte loads each, all issued before any is
-        // used (other lanes load the mask's last 32 bytes and discard them).
-        // Halves cut by kv_len, and masks under 32 bytes, go through
-        // dense_half.
-        dev::u32x4 v0[kDenseBatch], v1[kDenseBatch];
-        bool fast[kDenseBatch];
-        const bool can_fast = p.mask_numel >= 32;
-        const uint8_t *dummy = m8 + (can_fast ? p.mask_numel - 32 : 0);
+      // One row at a time, read along the row: lane l of load k takes the
+      // row's bytes [64 c0 + 1024 k + 16 l, + 16), keys 16 (l % 4) .. + 15
+      // of tile c0 + 16 k + l / 4; the four lanes of a quad hold one tile,
+      // whose word their first lane assembles (quad permutes) and stores.
+      // Every load is issued (lanes past the row or the mask read the mask's
+      // last 16 bytes and discard them), so the compiler's waits cover whole
+      // batches.  Bytes past kv_len belong to the next row and are masked.
+      const int nbytes = min(64 * cn, kv - 64 * c0);   // the row's bytes in this chunk
+      const int lofs = 16 * lane;
+      // FAST: the mask holds at least 16 bytes, so its last 16 are a valid
+      // stand-in address for lanes that read nothing
+      auto rows = [&](auto fast_tag) {
+        constexpr bool FAST = decltype(fast_tag)::value;
+        const uint8_t *dummy = m8 + (FAST ? p.mask_numel - 16 : 0);
+        for (int i0 = 0; i0 < 32; i0 += kDenseRows) {
+          dev::u32x4 v[kDenseRows][4];
+          bool ok[kDenseRows][4];
 #pragma unroll
-        for (int u = 0; u < kDenseBatch; ++u) {
-          const int c = c0 + ci0 + u;
-          const int64_t base = rbase + 64 * c;
-          fast[u] = can_fast && rv && ci0 + u < cn && kv - 64 * c - 32 * half >= 32 && base + 32 <= p.mask_numel;
-          if (can_fast) {
-            const uint8_t *src = fast[u] ? m8 + base : dummy;
-            __builtin_memcpy(&v0[u], src, 16);
-            __builtin_memcpy(&v1[u], src + 16, 16);
-          } else {
-            v0[u] = dev::u32x4{0, 0, 0, 0};
-            v1[u] = dev::u32x4{0, 0, 0, 0};
+          for (int ii = 0; ii < kDenseRows; ++ii)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int row = row0 + i0 + ii;
+              const int off = 1024 * k + lofs;
+              const int64_t base = ax.moff + (int64_t)row * kv + 64 * c0 + off;
+              ok[ii][k] = FAST && row < sq.q_len && off < nbytes && base + 16 <= p.mask_numel;
+              if constexpr (FAST) __builtin_memcpy(&v[ii][k], ok[ii][k] ? m8 + base : dummy, 16);
+            }
+#pragma unroll
+          for (int ii = 0; ii < kDenseRows; ++ii) {
+            const int row = row0 + i0 + ii;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int off = 1024 * k + lofs;
+              uint32_t bits = 0;
+              if (ok[ii][k]) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bits |= nonzero_bytes4(v[ii][k][c]) << (4 * c);
+              }
+              // a lane whose 16 bytes run past the end of the mask reads its
+              // row's bytes one by one (only at the mask's end), in a branch
+              // the wave skips when no lane needs it
+              const bool slow = row < sq.q_len && off < nbytes && !ok[ii][k];
+              if (__any(slow)) {
+                if (slow) {
+                  const int64_t base = ax.moff + (int64_t)row * kv + 64 * c0 + off;
+                  for (int j = 0; j < 16; ++j)
+                    if (base + j < p.mask_numel && m8[base + j] != 0) bits |= 1u << j;
+                }
+              }
+              const int nb = nbytes - off;   // bytes of this lane inside the row
+              if (nb < 16) bits &= nb <= 0 ? 0u : (1u << nb) - 1u;
+              // the quad's other three lanes (quad permutes: lane j of a
+              // quad reads lane j + 1, j + 2, j + 3 modulo 4)
+              const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bits, 0x39, 0xF, 0xF, false);
+              const uint32_t b2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bits, 0x4E, 0xF, 0xF, false);
+              const uint32_t b3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bits, 0x93, 0xF, 0xF, false);
+              const int t = 16 * k + (lane >> 2);
+              if ((lane & 3) == 0 && t < cn)
+                wl[t * ws + rg * 32 + i0 + ii] =
+                    (((uint64_t)(b2 | (b3 << 16)) << 32) | (bits | (b1 << 16))) &
+                    band_bits(row, c0 + t, sq.q_len, kv, p.window);
+            }
           }
         }
-        uint32_t bits[kDenseBatch];
-#pragma unroll
-        for (int u = 0; u < kDenseBatch; ++u) {
-          uint32_t x = 0;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            x |= nonzero_bytes4(v0[u][c]) << (4 * c);
-            x |= nonzero_bytes4(v1[u][c]) << (16 + 4 * c);
-          }
-          bits[u] = fast[u] ? x : 0u;
-          const int c = c0 + ci0 + u;
-          const int nb = min(32, kv - 64 * c - 32 * half);
-          if (!fast[u] && rv && ci0 + u < cn && nb > 0) bits[u] = dense_half(m8, rbase + 64 * c, nb, p.mask_numel);
-        }
-#pragma unroll
-        for (int u = 0; u < kDenseBatch; ++u) {
-          const int src = 2 * (lane & 31);
-          const uint32_t lo = __shfl(bits[u], src, 64), hi = __shfl(bits[u], src + 1, 64);
-          if (lane < 32 && ci0 + u < cn)
-            wl[(ci0 + u) * ws + rg * 32 + lane] =
-                (((uint64_t)hi << 32) | lo) & band_bits(row0 + lane, c0 + ci0 + u, sq.q_len, kv, p.window);
-        }
-      }
+      };
+      if (p.mask_numel >= 16)
+        rows(std::true_type{});
+      else
+        rows(std::false_type{});
     }
   }
   __syncthreads();

@@ -74,6 +74,28 @@ def test_device_classify_matches_host_compile(tile_q):
         assert np.array_equal(dw, hw), kind
 
 
+@pytest.mark.parametrize("tile_q", [64, 128])
+@pytest.mark.parametrize("shape", [([3, 2], [4, 1]),                  # the whole mask under 16 bytes
+                                   ([5, 17, 40], [15, 33, 16]),        # rows shorter than a tile
+                                   ([1, 70], [1030, 2049])])           # rows ending 6 and 1 bytes into a load
+def test_device_classify_short_masks(tile_q, shape):
+    """Dense rows shorter than a 16-byte load, a mask shorter than one load,
+    and rows whose last bytes start a new 1 KB load: the device classes and
+    words equal the host compiler's."""
+    q_lens, kv_lens = shape
+    rng = np.random.default_rng(950 + tile_q + len(q_lens))
+    dense = [rng.random((q, k)) < 0.5 for q, k in zip(q_lens, kv_lens)]
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    kv = np.asarray(kv_lens, np.int32)
+    flat = np.concatenate([m.astype(np.uint8).reshape(-1) for m in dense])
+    host = ma.mask_compile_host("dense", cu, kv, mask=flat, tile_q=tile_q)
+    hc, hw = host.export()
+    _say("device classify short", shape, tile_q, flat.size)
+    p = ma.mask_compile("dense", cu, kv, mask=torch.from_numpy(flat).cuda(), tile_q=tile_q)
+    dc, dw = p.export()
+    assert np.array_equal(dc, hc) and np.array_equal(dw, hw)
+
+
 # ------------------------------------------- small ragged bf16 shapes, all d --
 def _ragged(seed, d, hq, hkv, q_lens, kv_lens, permute=True):
     rng = W.rng_for(seed)
