@@ -3,16 +3,18 @@
 // trip for the mask itself.  An HBM scan: the mask is read once, coalesced,
 // and only PARTIAL tiles' words are written.
 //
-// Pass 1: one workgroup (4 waves) per (q-tile row, chunk of 64 k-tiles), all
-// chunks of all rows at once, gives each tile position its class byte and
+// Pass 1: one workgroup (4 waves) per (q-tile row, chunk of 64 k-tiles for
+// packed rows, 48 for dense ones), all chunks of all rows at once, gives
+// each tile position its class byte and
 // writes the PARTIAL tiles' word blocks (tile_q words each, one block per
 // tile position):
 //  * packed rows (classify_packed_kernel): wave w takes 32 rows of the
 //    q-tile, lane l tile l of the chunk; a lane loads its tile's 32 words (a
 //    row's 64 words are one 512-byte load across the wave) and reduces them
 //    in registers; the four row groups combine through LDS flags.
-//  * dense rows (classify_kernel): a wave reads its rows one after another,
-//    each row's chunk (up to 4 KB) in 1 KB loads along the row, turns each
+//  * dense rows (classify_kernel): wave w takes a quarter of the q-tile's
+//    rows and reads them one after another,
+//    each row's chunk (up to 3 KB) in 1 KB loads along the row, turns each
 //    lane's 16 bytes into bits (SWAR), and the four lanes of a tile put its
 //    word together (four rows in flight per wave); the words go through
 //    LDS, where each wave scans a quarter of the rows for "some bit set" and
@@ -31,9 +33,12 @@
 namespace maskattn {
 namespace {
 
-constexpr int kTiles = 64;     // k-tiles per chunk
+constexpr int kTiles = 64;     // k-tiles per chunk (packed rows)
+constexpr int kDenseTiles = 48;                   // k-tiles per chunk (dense rows): 49.5 KB of LDS
+constexpr int kDenseLoads = kDenseTiles * 64 / 1024;   // 1 KB loads per row and chunk
+static_assert(kDenseTiles % 16 == 0 && kDenseTiles <= 64, "a chunk is whole 1 KB loads, one tile per lane at most");
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kDenseRows = 4;  // dense rows in flight per wave (4 KB each)
+constexpr int kDenseRows = 4;  // dense rows in flight per wave (3 KB each)
 
 struct ClassifyParams {
   const SeqInfo *seqs;
@@ -78,14 +83,16 @@ __device__ __forceinline__ int seq_of_row(const ClassifyParams &p, int r) {
   return lo;
 }
 
-// Pass 1 (dense masks): workgroup (q-tile row r, chunk ch) classifies k-tiles [64 ch,
-// 64 ch + 64) of row r: their classes go to cls (one byte per tile position)
-// and the PARTIAL tiles' word blocks to their tile positions.  Every chunk of
-// every row runs at once, so the whole mask is in flight.
+// Pass 1 (dense masks): workgroup (q-tile row r, chunk ch) classifies k-tiles
+// [48 ch, 48 ch + 48) of row r: their classes go to cls (one byte per tile
+// position) and the PARTIAL tiles' word blocks to their tile positions.
+// Every chunk of every row runs at once, so the whole mask is in flight; the
+// chunk's words (49.5 KB at tile_q 128) leave room for three workgroups per
+// CU.
 __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p, uint8_t *cls) {
-  extern __shared__ uint64_t wl[];                 // [kTiles][tile_q + 1] words of the chunk
-  __shared__ uint32_t any_q[4][kTiles], full_q[4][kTiles];
-  __shared__ uint8_t cls_s[kTiles];
+  extern __shared__ uint64_t wl[];                 // [kDenseTiles][tile_q + 1] words of the chunk
+  __shared__ uint32_t any_q[4][kDenseTiles], full_q[4][kDenseTiles];
+  __shared__ uint8_t cls_s[kDenseTiles];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.x;
   const int b = seq_of_row(p, r);
@@ -93,38 +100,18 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p, ui
   const SeqAux ax = p.aux[b];
   const int a = r - ax.row_base;
   const int nkt = sq.nkt, kv = sq.kv_len;
-  const int c0 = blockIdx.y * kTiles;
+  const int c0 = blockIdx.y * kDenseTiles;
   if (c0 >= nkt) return;
   const int tq = p.tile_q, ws = p.tile_q + 1;      // LDS row stride (words), padded
-  const int ngroups = tq / 32;
   const int rows_in = min(tq, sq.q_len - a * tq);  // in-bounds rows of this q-tile
   const int64_t ebase = ax.tile_base + (int64_t)a * nkt;  // tile positions of this row
-  const int64_t nw = (kv + 63) / 64;
   const uint8_t *m8 = (const uint8_t *)p.mask;
-  const uint64_t *m64 = (const uint64_t *)p.mask;
-  const int cn = min(kTiles, nkt - c0);
-  // ---- 1. words of the chunk -> LDS
-  for (int rg = wave; rg < ngroups; rg += 4) {
-    const int row0 = a * tq + rg * 32;
-    if (p.packed) {
-      // lane l: tile c0 + l of row row0 + i, for the wave's 32 rows
-      const int c = c0 + lane;
-      const int keys = kv - 64 * c;
-      const uint64_t inb = keys >= 64 ? ~0ull : (keys <= 0 ? 0ull : ((1ull << keys) - 1ull));
-      // all 32 loads in flight before the first LDS store
-      uint64_t w[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int row = row0 + i;
-        const int64_t idx = ax.moff + (int64_t)row * nw + c;
-        w[i] = (lane < cn && row < sq.q_len && idx < p.mask_numel) ? m64[idx] : 0ull;
-      }
-      if (lane < cn) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-          wl[lane * ws + rg * 32 + i] = w[i] & inb & band_bits(row0 + i, c, sq.q_len, kv, p.window);
-      }
-    } else {
+  const int cn = min(kDenseTiles, nkt - c0);
+  // ---- 1. words of the chunk -> LDS: wave w takes rows [w tq / 4, (w + 1) tq / 4)
+  {
+    const int rpw = tq / 4, q0w = wave * rpw;
+    const int row0 = a * tq + q0w;
+    {
       // One row at a time, read along the row: lane l of load k takes the
       // row's bytes [64 c0 + 1024 k + 16 l, + 16), keys 16 (l % 4) .. + 15
       // of tile c0 + 16 k + l / 4; the four lanes of a quad hold one tile,
@@ -139,13 +126,13 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p, ui
       auto rows = [&](auto fast_tag) {
         constexpr bool FAST = decltype(fast_tag)::value;
         const uint8_t *dummy = m8 + (FAST ? p.mask_numel - 16 : 0);
-        for (int i0 = 0; i0 < 32; i0 += kDenseRows) {
-          dev::u32x4 v[kDenseRows][4];
-          bool ok[kDenseRows][4];
+        for (int i0 = 0; i0 < rpw; i0 += kDenseRows) {
+          dev::u32x4 v[kDenseRows][kDenseLoads];
+          bool ok[kDenseRows][kDenseLoads];
 #pragma unroll
           for (int ii = 0; ii < kDenseRows; ++ii)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < kDenseLoads; ++k) {
               const int row = row0 + i0 + ii;
               const int off = 1024 * k + lofs;
               const int64_t base = ax.moff + (int64_t)row * kv + 64 * c0 + off;
@@ -156,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p, ui
           for (int ii = 0; ii < kDenseRows; ++ii) {
             const int row = row0 + i0 + ii;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < kDenseLoads; ++k) {
               const int off = 1024 * k + lofs;
               uint32_t bits = 0;
               if (ok[ii][k]) {
@@ -183,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p, ui
               const uint32_t b3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)bits, 0x93, 0xF, 0xF, false);
               const int t = 16 * k + (lane >> 2);
               if ((lane & 3) == 0 && t < cn)
-                wl[t * ws + rg * 32 + i0 + ii] =
+                wl[t * ws + q0w + i0 + ii] =
                     (((uint64_t)(b2 | (b3 << 16)) << 32) | (bits | (b1 << 16))) &
                     band_bits(row, c0 + t, sq.q_len, kv, p.window);
             }
@@ -211,8 +198,10 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p, ui
         full &= w == inb ? 1u : 0u;
       }
     }
-    any_q[wave][t] = any;
-    full_q[wave][t] = full;
+    if (t < kDenseTiles) {   // a chunk has fewer tiles than a wave has lanes
+      any_q[wave][t] = any;
+      full_q[wave][t] = full;
+    }
   }
   __syncthreads();
   if (wave == 0) {
@@ -223,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(ClassifyParams p, ui
       c = !any ? MA_TILE_SKIP : (full ? MA_TILE_FULL : MA_TILE_PARTIAL);
       cls[ebase + c0 + lane] = (uint8_t)c;
     }
-    cls_s[lane] = (uint8_t)c;
+    if (lane < kDenseTiles) cls_s[lane] = (uint8_t)c;
   }
   __syncthreads();
   // ---- 3. word blocks of the PARTIAL tiles
@@ -371,11 +360,12 @@ ma_status launch_classify(ma_plan *p, const void *mask, int32_t kind, int64_t ma
   uint8_t *cls = (uint8_t *)(base + p->off_extra);
   int32_t max_nkt = 1;
   for (int b = 0; b < p->batch; ++b) max_nkt = std::max(max_nkt, p->nkt[b]);
-  const dim3 grid(p->num_rows, (max_nkt + kTiles - 1) / kTiles);
   if (prm.packed) {
+    const dim3 grid(p->num_rows, (max_nkt + kTiles - 1) / kTiles);
     hipLaunchKernelGGL(classify_packed_kernel, grid, dim3(kThreads), 0, s, prm, cls);
   } else {
-    const size_t lds = (size_t)kTiles * (p->tile_q + 1) * sizeof(uint64_t);
+    const dim3 grid(p->num_rows, (max_nkt + kDenseTiles - 1) / kDenseTiles);
+    const size_t lds = (size_t)kDenseTiles * (p->tile_q + 1) * sizeof(uint64_t);
     e = hipSuccess;
     if (lds > 64 * 1024)
       e = hipFuncSetAttribute((const void *)classify_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
