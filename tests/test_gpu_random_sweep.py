@@ -164,11 +164,12 @@ def test_verify_random_sweep(seed):
                       dtype=np.int32)
     w.masks["causal"] = W.MaskInput("causal")
     w.masks["prefix"] = W.MaskInput("prefix_lm", prefix_len=prefix)
-    for name in ("causal", "prefix"):
+    w.masks["window"] = W.MaskInput("window", window=int(np.random.default_rng(4600 + seed).integers(1, 1500)))
+    for name in ("causal", "prefix", "window"):
         mi = w.masks[name]
         pl = torch.from_numpy(prefix).cuda() if mi.kind == "prefix_lm" else None
         o, l = ma.attn_decode(dev["q"], dev["k"], dev["v"], dev["pt"], dev["cu"], dev["kv"], desc["max_q"],
-                              int(w.kv_lens.max()), w.scale, mask_kind=mi.kind, prefix_len=pl)
+                              int(w.kv_lens.max()), w.scale, mask_kind=mi.kind, window=mi.window, prefix_len=pl)
         torch.cuda.synchronize()
         ref_o, ref_l = oracle(w, name)
         err = max_abs_err(o, ref_o)
