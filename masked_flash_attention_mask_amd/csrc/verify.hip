@@ -983,7 +983,7 @@ struct UnitRec {
 // Workgroups are dispatched to the 8 XCDs round-robin.  When the grid is a
 // multiple of 8, dispatch slot x runs logical workgroup (x % 8) * (G / 8) +
 // x / 8, so consecutive workgroups - the pieces of one unit, which read the
-// same query rows, and later the merge of those pieces - share one XCD's L2.
+// same query rows - share one XCD's L2.
 __device__ __forceinline__ int pipe_logical(int x, int g) {
   return (g & 7) == 0 ? (x & 7) * (g >> 3) + (x >> 3) : x;
 }
